@@ -1,0 +1,389 @@
+"""The three codecs, the decompress-reduce(-requantize) step and the decode.
+
+Test infrastructure only (see the package docstring). All arithmetic is
+float32 with one rounding per operation, in the order written; integer steps
+are exact.
+
+Layout of the input: a row-major [rows, cols] tensor of bf16 bit patterns.
+Quantization blocks are B contiguous elements along ``cols`` (B divides
+cols), so the tensor is simply a sequence of n / B blocks.
+"""
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+from .formats import (
+    E4M3_MAX,
+    bf16_bits_to_f32,
+    decode_e4m3,
+    encode_e4m3,
+    f32_to_bf16_bits,
+    pack_int4,
+    unpack_int4,
+)
+from .hadamard import fwht
+
+F32 = np.float32
+
+FP8_DUAL = 1    # TACO: Hadamard blocks + tensor scale g + per-block power-of-two exponent
+INT8_SYM = 2    # EQuARX: symmetric abs-max int8, one float32 scale per 64 entries
+INT4_ASYM = 3   # FlashComm: asymmetric min/max, group 128, 4-bit codes packed two per byte
+INT8_ASYM = 4   # FlashComm: the same scheme at 8 bits, used for the gather stage
+
+# Reading: the tensor scale g is kept within [2^-60, 2^60] so that g * 2^-k and
+# (1/g) * 2^k stay normal float32 numbers for every block exponent k.
+G_MIN = F32(2.0 ** -60)
+G_MAX = F32(2.0 ** 60)
+K_MIN, K_MAX = -64, 63          # block exponent stored as int8
+# Reading: a block whose abs-max (symmetric) or range (asymmetric) is below
+# 2^-100 is stored as all-zero codes with a zero scale, so 127/A and
+# qmax/r never overflow float32.
+TINY = F32(2.0 ** -100)
+
+
+@dataclass(frozen=True)
+class Codec:
+    format: int
+    block: int
+    hadamard: bool = False
+
+    @property
+    def bits(self):
+        return 4 if self.format == INT4_ASYM else 8
+
+    @staticmethod
+    def fp8(block=128, hadamard=True):
+        return Codec(FP8_DUAL, block, bool(hadamard))
+
+    @staticmethod
+    def int8_sym(block=64):
+        return Codec(INT8_SYM, block, False)
+
+    @staticmethod
+    def int4_asym(block=128):
+        return Codec(INT4_ASYM, block, False)
+
+    @staticmethod
+    def int8_asym(block=128):
+        return Codec(INT8_ASYM, block, False)
+
+
+@dataclass
+class Compressed:
+    """One compressed shard, as separate arrays.
+
+    codes: uint8 [n] (INT4: packed, [n / 2]); for INT8_SYM the bytes are int8.
+    scale: FP8_DUAL -> int8 block exponents k [n / B]; otherwise float32 s [n / B].
+    zero:  asymmetric formats -> uint8 zero points z [n / B]; else None.
+    tensor_scale: FP8_DUAL -> float32 g; else None.
+    """
+    codec: Codec
+    rows: int
+    cols: int
+    codes: np.ndarray
+    scale: np.ndarray
+    zero: Optional[np.ndarray] = None
+    tensor_scale: Optional[np.float32] = None
+    prequant: Optional[np.ndarray] = None   # the float32 fed to the rounding step
+
+
+# ---------------------------------------------------------------- TACO FP8 --
+
+def block_exponent(m):
+    """Per-block power-of-two exponent k of the dual-scale reading.
+
+    Reading of [TACO]'s Dual-Scale Quantization (named in the abstract and
+    Fig. 7, never defined): the second scale of a block is 2^k with k the
+    largest integer such that m * 2^k <= 448, where m is the block's largest
+    magnitude after the tensor scale; k is clamped to the int8 range
+    [-64, 63]; k = 0 for an all-zero block; an infinite m has no such k and
+    gets the lower clamp. With m = f * 2^E (f in [0.5, 1)) the largest k is
+    9 - E if f <= 0.875 (448 = 0.875 * 2^9) and 8 - E otherwise, which puts
+    the block maximum in (224, 448].
+    """
+    m = np.asarray(m, dtype=np.float32).astype(np.float64)
+    fin = np.isfinite(m) & (m > 0)
+    f, E = np.frexp(np.where(fin, m, 1.0))
+    k = np.where(f <= 0.875, 9, 8) - E.astype(np.int64)
+    k = np.clip(k, K_MIN, K_MAX)
+    k = np.where(m == 0, 0, k)
+    k = np.where(np.isinf(m), K_MIN, k)
+    return k.astype(np.int64)
+
+
+def auto_tensor_scale(y):
+    """Tensor scale g from the data (reading of [TACO] Fig. 7 "adaptive rescaling").
+
+    g = RN(A / 448) with A = max |y| over the whole tensor in the transformed
+    domain, so the tensor maximum maps onto the largest E4M3 value; g = 1 for
+    an all-zero tensor; g is clamped to [2^-60, 2^60].
+    """
+    y = np.asarray(y, dtype=np.float32)
+    A = np.max(np.abs(y)) if y.size else F32(0)
+    if A == 0:
+        return F32(1.0)
+    g = F32(A) / F32(E4M3_MAX)
+    return F32(min(max(g, G_MIN), G_MAX))
+
+
+def sum_tensor_scales(gs):
+    """Tensor scale of a sum of shards: g' = g_0 + g_1 + ... in order, clamped.
+
+    Reading: the pages do not say how the gather-stage FP8 tensor is scaled.
+    Since every |dequantized value| <= 448 * 2^-k * g_r, the sum of the g_r
+    bounds the sum without a second pass over it.
+    """
+    acc = F32(0)
+    for g in gs:
+        acc = F32(acc + F32(g))
+    return F32(min(max(acc, G_MIN), G_MAX))
+
+
+def _quantize_fp8_dual(y, g, B):
+    """Dual-scale E4M3 quantization of transformed values y (float32, flat).
+
+    w = RN(y * RN(1/g)); a w that is exactly zero is +0 (reading: the sign of
+    an exact zero carries nothing); m = max |w| per block; k from
+    ``block_exponent``; v = w * 2^k; q = E4M3 code of v.
+    """
+    g = F32(g)
+    inv_g = F32(F32(1.0) / g)
+    yb = y.reshape(-1, B)
+    w = yb * inv_g
+    w = np.where(yb == 0, F32(0.0), w).astype(np.float32)
+    m = np.max(np.abs(w), axis=1) if w.size else np.zeros(0, np.float32)
+    k = block_exponent(m)
+    v = np.ldexp(w, k[:, None]).astype(np.float32)
+    q = encode_e4m3(v)
+    return q.reshape(-1), k.astype(np.int8), v.reshape(-1)
+
+
+def _dequantize_fp8_dual(codes, k, g, B):
+    """x' = RN(dec(q) * 2^-k * g): dec(q) * 2^-k is exact, one rounding for g."""
+    d = decode_e4m3(codes).reshape(-1, B)
+    t = np.ldexp(d, -k.astype(np.int64)[:, None]).astype(np.float32)
+    return (t * F32(g)).astype(np.float32).reshape(-1)
+
+
+# ------------------------------------------------------------- EQuARX INT8 --
+
+def _quantize_int8_sym(u, B):
+    """Block-wise symmetric int8 ([EQuARX], "What carries the argument").
+
+    Per block: A = max |u| (abs-max reduction); s = RN(A / 127) is the FP32
+    scale that travels with the block; q = clamp(round(RN(u * RN(127 / A))),
+    -127, 127), rounding to nearest even. Readings: the code range is the
+    symmetric [-127, 127]; the codes come from multiplying by the rounded
+    reciprocal; a block with A < 2^-100 stores s = 0 and zero codes.
+    """
+    ub = u.reshape(-1, B)
+    A = np.max(np.abs(ub), axis=1) if ub.size else np.zeros(0, np.float32)
+    live = A >= TINY
+    Asafe = np.where(live, A, F32(1.0)).astype(np.float32)
+    s = np.where(live, Asafe / F32(127.0), F32(0.0)).astype(np.float32)
+    inv = (F32(127.0) / Asafe).astype(np.float32)
+    t = (ub * inv[:, None]).astype(np.float32)
+    q = np.clip(np.rint(t), -127, 127)
+    q = np.where(live[:, None], q, 0).astype(np.int8)
+    t = np.where(live[:, None], t, F32(0.0)).astype(np.float32)
+    return q.reshape(-1), s, t.reshape(-1)
+
+
+def _dequantize_int8_sym(q, s, B):
+    """Dequantize to FP32 before any addition ([EQuARX]): RN(q * s)."""
+    qf = q.astype(np.int8).astype(np.float32).reshape(-1, B)
+    return (qf * s[:, None]).astype(np.float32).reshape(-1)
+
+
+# --------------------------------------------------------- FlashComm asym --
+
+def _quantize_asym(u, B, bits):
+    """Asymmetric min/max quantization per group ([FlashComm], "What carries
+    the argument"; Algorithm 1 dequantizes from codes, zero point and scale).
+
+    The formulas (the page's Eq. (1)-(4)) are not printed; reading, with
+    qmax = 2^bits - 1: lo = min(min u, 0), hi = max(max u, 0) (the range always
+    holds zero, so zero is exact); r = RN(hi - lo); s = RN(r / qmax);
+    inv = RN(qmax / r); zero point z = clamp(round(RN(-lo * inv)), 0, qmax);
+    q = clamp(round(RN(u * inv)) + z, 0, qmax); rounding to nearest even.
+    A group with r < 2^-100 stores s = 0, z = 0 and zero codes.
+    """
+    qmax = F32((1 << bits) - 1)
+    ub = u.reshape(-1, B)
+    if ub.size:
+        lo = np.minimum(np.min(ub, axis=1), F32(0.0)).astype(np.float32)
+        hi = np.maximum(np.max(ub, axis=1), F32(0.0)).astype(np.float32)
+    else:
+        lo = hi = np.zeros(0, np.float32)
+    r = (hi - lo).astype(np.float32)
+    live = r >= TINY
+    rsafe = np.where(live, r, F32(1.0)).astype(np.float32)
+    s = np.where(live, rsafe / qmax, F32(0.0)).astype(np.float32)
+    inv = (qmax / rsafe).astype(np.float32)
+    z = np.clip(np.rint((-lo * inv).astype(np.float32)), 0, qmax)
+    t = (ub * inv[:, None]).astype(np.float32)
+    q = np.clip(np.rint(t) + z[:, None], 0, qmax)
+    q = np.where(live[:, None], q, 0).astype(np.uint8)
+    z = np.where(live, z, 0).astype(np.uint8)
+    t = np.where(live[:, None], t, F32(0.0)).astype(np.float32)
+    return q.reshape(-1), s, z, t.reshape(-1)
+
+
+def _dequantize_asym(q, s, z, B):
+    """RN(float(q - z) * s); q - z is an exact small integer."""
+    d = (q.reshape(-1, B).astype(np.int64) - z.astype(np.int64)[:, None]).astype(np.float32)
+    return (d * s[:, None]).astype(np.float32).reshape(-1)
+
+
+# ------------------------------------------------------------ public API ---
+
+def _check(codec, cols):
+    B = codec.block
+    if codec.format == FP8_DUAL:
+        assert B in (16, 32, 64, 128), "FP8 block must be 16, 32, 64 or 128"
+    elif codec.format == INT8_SYM:
+        assert B == 64, "INT8_SYM block is 64"
+    elif codec.format in (INT4_ASYM, INT8_ASYM):
+        assert B == 128, "asymmetric group is 128"
+    else:
+        raise ValueError("unknown format")
+    assert cols % B == 0, "cols must be a multiple of the block"
+
+
+def _pack(codec, rows, cols, q, s, z=None, g=None, pre=None):
+    codes = pack_int4(q) if codec.format == INT4_ASYM else q.view(np.uint8).copy()
+    return Compressed(codec, rows, cols, codes, s, z, g, pre)
+
+
+def quantize_values(codec, y, rows, cols, tensor_scale=None):
+    """Quantize float32 values that are already in the codec's domain.
+
+    For FP8_DUAL, ``y`` is taken to be in the transformed (Hadamard) domain and
+    no transform is applied; ``tensor_scale`` None means the data-driven g.
+    """
+    _check(codec, cols)
+    y = np.ascontiguousarray(y, dtype=np.float32).reshape(-1)
+    B = codec.block
+    if codec.format == FP8_DUAL:
+        g = auto_tensor_scale(y) if tensor_scale is None else F32(tensor_scale)
+        q, k, v = _quantize_fp8_dual(y, g, B)
+        return _pack(codec, rows, cols, q, k, None, g, v)
+    if codec.format == INT8_SYM:
+        q, s, t = _quantize_int8_sym(y, B)
+        return _pack(codec, rows, cols, q, s, None, None, t)
+    q, s, z, t = _quantize_asym(y, B, codec.bits)
+    return _pack(codec, rows, cols, q, s, z, None, t)
+
+
+def transform(codec, x_bits):
+    """Widen bf16 to float32 and, for FP8_DUAL with hadamard, apply the block FWHT.
+
+    Reading of [TACO]'s "data-driven reshaping": the [rows, cols] tensor is
+    viewed as [n / B, B] blocks along the hidden dimension (no data movement).
+    """
+    u = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16)).reshape(-1)
+    if codec.format == FP8_DUAL and codec.hadamard:
+        return fwht(u, codec.block)
+    return u
+
+
+def compress(codec, x_bits, tensor_scale=None):
+    """Compress one bf16 shard of shape [rows, cols] (uint16 bit patterns).
+
+    FP8_DUAL ([TACO] Fig. 7): widen, block FWHT (if enabled), tensor scale g
+    (given, or from this tensor when None), per-block exponent, E4M3 codes.
+    INT8_SYM ([EQuARX]) and INT4_ASYM / INT8_ASYM ([FlashComm]) quantize the
+    widened values directly.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    y = transform(codec, x_bits)
+    return quantize_values(codec, y, rows, cols, tensor_scale)
+
+
+def dequantize(c: Compressed):
+    """Dequantize one shard to float32 (FP8_DUAL: still in the transformed domain)."""
+    B = c.codec.block
+    if c.codec.format == FP8_DUAL:
+        return _dequantize_fp8_dual(c.codes, c.scale, c.tensor_scale, B)
+    if c.codec.format == INT8_SYM:
+        return _dequantize_int8_sym(c.codes.view(np.int8), c.scale, B)
+    q = unpack_int4(c.codes) if c.codec.format == INT4_ASYM else c.codes
+    return _dequantize_asym(q, c.scale, c.zero, B)
+
+
+ALLOWED_PAIRS = {
+    (FP8_DUAL, FP8_DUAL),
+    (INT8_SYM, INT8_SYM),
+    (INT4_ASYM, INT8_ASYM),
+    (INT8_ASYM, INT8_ASYM),
+}
+
+
+def check_pair(cin: Codec, cout: Codec):
+    assert (cin.format, cout.format) in ALLOWED_PAIRS, "unsupported format pair"
+    if cin.format == FP8_DUAL:
+        assert cin.block == cout.block and cin.hadamard == cout.hadamard
+    else:
+        assert cin.block == cout.block
+
+
+def decompress_reduce(shards: List[Compressed], out_codec: Optional[Codec] = None):
+    """Sum N compressed shards in FP32 and optionally re-quantize the sum.
+
+    Each shard is dequantized to FP32 before it is added ([EQuARX]); the sum
+    is acc = ((0 + x_0) + x_1) + ... + x_{N-1}, one float32 rounding per add
+    (reading: a fixed shard order stands in for the ring order). The partial
+    sum is then re-quantized for the gather stage ([FlashComm] re-quantizes to
+    INT8 for the All-Gather; [EQuARX] quantizes both stages): FP8_DUAL with
+    g' = sum of the shard tensor scales and no second transform (the FWHT is
+    linear and shared, so the sum of transformed shards is the transform of
+    the sum), INT8_SYM, or INT8_ASYM.
+
+    Returns (acc float32 [rows, cols], Compressed or None).
+    """
+    assert len(shards) >= 1
+    c0 = shards[0]
+    for s in shards:
+        assert s.codec == c0.codec and (s.rows, s.cols) == (c0.rows, c0.cols)
+    acc = np.zeros(c0.rows * c0.cols, dtype=np.float32)
+    for s in shards:
+        acc = (acc + dequantize(s)).astype(np.float32)
+    rq = None
+    if out_codec is not None:
+        check_pair(c0.codec, out_codec)
+        g = None
+        if out_codec.format == FP8_DUAL:
+            g = sum_tensor_scales([s.tensor_scale for s in shards])
+        rq = quantize_values(out_codec, acc, c0.rows, c0.cols, g)
+    return acc.reshape(c0.rows, c0.cols), rq
+
+
+def requantize(codec, x_f32, tensor_scale=None):
+    """Quantize a caller-supplied float32 tensor (FP8: taken as transformed values)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    rows, cols = x.shape
+    return quantize_values(codec, x, rows, cols, tensor_scale)
+
+
+def decode(c: Compressed, out_dtype="f32"):
+    """Consumer-side decode: dequantize and undo the transform.
+
+    FP8_DUAL with hadamard: x = FWHT(y') * 2^-log2(B) (the Sylvester matrix is
+    its own inverse up to 1/B); an exactly-zero result is +0.
+    Returns float32 [rows, cols], or bf16 bit patterns if out_dtype == "bf16".
+    """
+    y = dequantize(c)
+    if c.codec.format == FP8_DUAL and c.codec.hadamard:
+        B = c.codec.block
+        t = fwht(y, B)
+        x = np.ldexp(t, -int(np.log2(B))).astype(np.float32)
+        x = np.where(t == 0, F32(0.0), x).astype(np.float32)
+    else:
+        x = y
+    x = x.reshape(c.rows, c.cols)
+    if out_dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x

@@ -1,0 +1,121 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one. A pin set that lets a dropped term, a wrong sign, a wrong index
+or a wrong constant through would not be worth trusting."""
+
+import numpy as np
+import pytest
+
+from oracle import codecs as cd
+from oracle import formats as fm
+from oracle import hadamard as hd
+import tests.test_oracle_codecs as TC
+import tests.test_oracle_formats as TF
+import tests.test_oracle_hadamard as TH
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_encoder_ties_away_from_zero_is_caught(monkeypatch):
+    real = fm.encode_e4m3
+
+    def bad(v):
+        v = np.asarray(v, np.float32)
+        # nudge exact ties upward: rounds half away from zero
+        return real(np.where(np.isfinite(v), v * np.float32(1 + 2 ** -22), v))
+    monkeypatch.setattr(fm, "encode_e4m3", bad)
+    assert _fails(TF.test_e4m3_rounding_golden)
+
+
+def test_encoder_without_saturation_is_caught(monkeypatch):
+    real = fm.encode_e4m3
+
+    def bad(v):
+        c = real(v)
+        big = np.abs(np.asarray(v, np.float32)) > 464
+        return np.where(big, np.uint8(0x7F) | (c & 0x80), c).astype(np.uint8)
+    monkeypatch.setattr(fm, "encode_e4m3", bad)
+    assert _fails(TF.test_e4m3_rounding_golden)
+
+
+def test_swapped_butterfly_is_caught(monkeypatch):
+    def bad(y, B):
+        h = 1
+        while h < B:
+            v = y.reshape(-1, B // (2 * h), 2, h)
+            a, b = v[:, :, 0, :], v[:, :, 1, :]
+            y = np.stack([a - b, a + b], axis=2).reshape(-1, B)
+            h *= 2
+        return y
+    monkeypatch.setattr(hd, "_butterflies", bad)
+    assert _fails(TH.test_fwht_golden_examples)
+    assert _fails(TH.test_fwht_equals_dense_sylvester_matrix, 8)
+
+
+def test_skipped_butterfly_stage_is_caught(monkeypatch):
+    def bad(y, B):
+        h = 2
+        while h < B:
+            v = y.reshape(-1, B // (2 * h), 2, h)
+            a, b = v[:, :, 0, :], v[:, :, 1, :]
+            y = np.stack([a + b, a - b], axis=2).reshape(-1, B)
+            h *= 2
+        return y
+    monkeypatch.setattr(hd, "_butterflies", bad)
+    assert _fails(TH.test_fwht_equals_dense_sylvester_matrix, 16)
+
+
+def test_exponent_threshold_and_offset_errors_are_caught(monkeypatch):
+    real = cd.block_exponent
+    monkeypatch.setattr(cd, "block_exponent", lambda m: real(m) + 1)
+    assert _fails(TC.test_block_exponent_bruteforce)
+    monkeypatch.setattr(cd, "block_exponent", lambda m: np.where(np.asarray(m) > 0, real(np.asarray(m) * np.float32(0.99)), 0))
+    assert _fails(TC.test_block_exponent_bruteforce)
+
+
+def test_int8_scale_over_128_is_caught(monkeypatch):
+    real = cd._quantize_int8_sym
+
+    def bad(u, B):
+        q, s, t = real(u, B)
+        return q, (s * np.float32(127.0 / 128.0)).astype(np.float32), t
+    monkeypatch.setattr(cd, "_quantize_int8_sym", bad)
+    assert _fails(TC.test_int8_sym_extremes_and_error_bound)
+
+
+def test_asym_zero_point_sign_error_is_caught(monkeypatch):
+    real = cd._quantize_asym
+
+    def bad(u, B, bits):
+        q, s, z, t = real(u, B, bits)
+        qmax = (1 << bits) - 1
+        return q, s, (qmax - z).astype(np.uint8), t
+    monkeypatch.setattr(cd, "_quantize_asym", bad)
+    assert _fails(TC.test_int_codecs_golden)
+
+
+def test_dequant_dropping_tensor_scale_is_caught(monkeypatch):
+    def bad(codes, k, g, B):
+        d = fm.decode_e4m3(codes).reshape(-1, B)
+        return np.ldexp(d, -k.astype(np.int64)[:, None]).astype(np.float32).reshape(-1)
+    monkeypatch.setattr(cd, "_dequantize_fp8_dual", bad)
+    assert _fails(TC.test_fp8_dual_error_within_eq3_bound)
+
+
+def test_requant_with_max_scale_instead_of_sum_is_caught(monkeypatch):
+    monkeypatch.setattr(cd, "sum_tensor_scales", lambda gs: np.float32(max(gs)))
+    assert _fails(TC.test_taco_reduce_is_linear_through_the_transform) or \
+        _fails(TC.test_taco_requant_never_saturates_with_summed_scale)
+
+
+def test_int4_nibble_order_swap_is_caught(monkeypatch):
+    def bad(q):
+        q = np.asarray(q, np.uint8)
+        return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+    monkeypatch.setattr(fm, "pack_int4", bad)
+    assert _fails(TF.test_int4_pack_roundtrip_exhaustive)
