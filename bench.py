@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of the tensor-parallel activation compression hot path on one MI355X.
+
+One step = every rank's compress of its shard (N bf16 shards already resident
+in HBM, one compress launch each) followed by the decompress-reduce of the N
+compressed shards with re-quantization for the gather stage -- all of the hot
+path. Shards rotate over several input sets so that the working set exceeds
+the 256 MB Infinity Cache. The step is captured once per input set as two HIP
+graphs (the N compress launches, then the reduce); HIP events around each
+graph on the launch stream give the per-kernel durations.
+
+value = N * rows * cols * 2 bytes of bf16 input / step time (GB/s).
+
+Prints one JSON line. --gpus above 1 is refused: this build measures one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt-tp")
+    ap.add_argument("--scale-mode", choices=["delayed", "auto"], default="delayed",
+                    help="FP8 tensor scale: delayed (abs-max of the previous step, one pass) "
+                         "or auto (abs-max pre-pass of this tensor)")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Bytes each kernel must move, from the formats' definitions."""
+    n = w.n
+    if w.in_format == 1:
+        cbytes, meta_in = n, n // w.in_block          # E4M3 codes + int8 exponent per block
+        hdr = 16
+    elif w.in_format == 2:
+        cbytes, meta_in, hdr = n, 4 * (n // 64), 0
+    else:
+        cbytes = n // 2 if w.in_format == 3 else n
+        meta_in, hdr = 5 * (n // 128), 0              # float scale + uint8 zero point
+    compress = 2 * n + cbytes + meta_in + hdr
+    shard = cbytes + meta_in + hdr
+    if w.out_format is None:
+        out = 4 * n
+    elif w.out_format == 1:
+        out = n + n // w.out_block + 16
+    elif w.out_format == 2:
+        out = n + 4 * (n // 64)
+    else:
+        out = n + 5 * (n // 128)
+    reduce = w.shards * shard + out
+    return compress, reduce
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_compression_tensor_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, workload, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, as written, on a bounded sample of the same workload: row
+    chunks of every shard, compressed and reduced (+ requantized), spread over
+    a thread pool (NumPy releases the GIL inside its loops)."""
+    import numpy as np
+    import oracle
+    from oracle import codecs as cd
+    import workloads as W
+
+    cin = cd.Codec(w.in_format, w.in_block, w.hadamard)
+    cout = cd.Codec(w.out_format, w.out_block, w.hadamard) if w.out_format else None
+    nchunks = (w.rows + W.ROW_CHUNK - 1) // W.ROW_CHUNK
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    inputs = {}
+
+    def one(chunk):
+        shards = [oracle.compress(cin, inputs[(chunk, r)]) for r in range(w.shards)]
+        oracle.decompress_reduce(shards, cout)
+        return chunk
+
+    # calibrate on one chunk, then size the sample to the time budget
+    for r in range(w.shards):
+        inputs[(0, r)] = W.make_shard(w, r, chunks=[0])
+    t = time.perf_counter()
+    one(0)
+    per_chunk = time.perf_counter() - t
+    want = max(1, int(seconds * threads / max(per_chunk, 1e-6)))
+    chunks = list(range(min(nchunks, max(threads, want))))
+    for c in chunks:
+        for r in range(w.shards):
+            if (c, r) not in inputs:
+                inputs[(c, r)] = W.make_shard(w, r, chunks=[c])
+    t = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, chunks))
+    dt = time.perf_counter() - t
+    rows = sum(min(W.ROW_CHUNK, w.rows - c * W.ROW_CHUNK) for c in chunks)
+    bytes_in = w.shards * rows * w.cols * 2
+    return {"value": round(bytes_in / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {w.rows} rows of each of the {w.shards} shards ({len(chunks)} chunks of "
+                      f"{W.ROW_CHUNK} rows): compress + decompress-reduce"
+                      + (" + requantize" if cout else "") + f", {dt:.1f} s"}
+
+
+def quality(w, bufs, sets_bits, c_in):
+    """rel-MSE of the compress round trip of shard 0 (set 0) on a seeded sample of
+    row chunks: the GPU's (decoded on the GPU) next to the oracle's own."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import codecs as cd
+    from oracle.formats import bf16_bits_to_f32
+    import quantized_compression_tensor_amd as T
+    import workloads as W
+
+    ch = W.sample_chunks(w, 3, seed=7)
+    rows_idx = W.chunk_rows(ch, w.rows)
+    d = torch.empty(w.n, dtype=torch.float32, device="cuda")
+    T.taco_decompress(c_in, bufs[0][0], w.rows, w.cols, d, 0)
+    torch.cuda.synchronize()
+    x = sets_bits[0][0][rows_idx]
+    got = d.view(w.rows, w.cols)[torch.from_numpy(rows_idx).cuda()].cpu().numpy()
+    xf = bf16_bits_to_f32(x)
+    oc = cd.Codec(w.in_format, w.in_block, w.hadamard)
+    ref = oracle.decode(oracle.compress(oc, x))
+    return {"rel_mse_gpu": oracle.rel_mse(got, xf), "rel_mse_oracle": oracle.rel_mse(ref, xf),
+            "sample_rows": int(len(rows_idx))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_compression_tensor_amd as T
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    c_in = T.codec(w.in_format, w.in_block, 1 if w.hadamard else 0)
+    c_out = T.codec(w.out_format, w.out_block, 1 if w.hadamard else 0) if w.out_format else None
+    fp8 = w.in_format == T.TACO_FMT_FP8_DUAL
+    scale = (T.TACO_SCALE_DELAYED if args.scale_mode == "delayed" else T.TACO_SCALE_AUTO) if fp8 else 1.0
+
+    in_bytes = w.shards * w.n * 2
+    nsets = max(2, min(4, -(-2 * MALL_BYTES // in_bytes) + 1))
+    sets_bits, xs, bufs, outs = [], [], [], []
+    for s in range(nsets):
+        bits = [W.make_shard(w, r + 100 * s) for r in range(w.shards)]
+        sets_bits.append(bits if s == 0 else None)
+        xs.append([torch.from_numpy(b.view(np.int16)).to(dev) for b in bits])
+        bufs.append([T.empty_compressed(c_in, w.rows, w.cols, dev) for _ in range(w.shards)])
+        if c_out is not None:
+            outs.append(T.empty_compressed(c_out, w.rows, w.cols, dev))
+        else:
+            outs.append(torch.empty(w.n, dtype=torch.float32, device=dev))
+    wss = [torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(w.shards)]
+    torch.cuda.synchronize()
+
+    def compress(s):
+        for r in range(w.shards):
+            T.taco_compress(c_in, xs[s][r], w.rows, w.cols, scale, bufs[s][r],
+                            workspace=wss[r] if fp8 else None)
+
+    def reduce(s):
+        if c_out is not None:
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, None, c_out, outs[s])
+        else:
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, outs[s])
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        # first calls seed the delayed-scale history with this data
+        for s in range(nsets):
+            compress(s)
+            reduce(s)
+        torch.cuda.synchronize()
+        if args.launch == "graph":
+            g_comp, g_red = [], []
+            for s in range(nsets):
+                gc = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gc, stream=stream):
+                    compress(s)
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    reduce(s)
+                g_comp.append(gc)
+                g_red.append(gr)
+            run_c = lambda s: g_comp[s].replay()
+            run_r = lambda s: g_red[s].replay()
+        else:
+            run_c, run_r = compress, reduce
+
+        for i in range(args.warmup):
+            run_c(i % nsets)
+            run_r(i % nsets)
+        torch.cuda.synchronize()
+
+        K = args.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            s = i % nsets
+            ev[i][0].record(stream)
+            run_c(s)
+            ev[i][1].record(stream)
+            run_r(s)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    t_comp = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / w.shards   # ms per compress launch
+    t_red = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))                 # ms per reduce launch
+    ms_step = wall * 1e3 / K
+    value = in_bytes / (ms_step * 1e-3) / 1e9
+
+    b_comp, b_red = algorithmic_bytes(w)
+    comp_gbs = b_comp / (t_comp * 1e-3) / 1e9
+    red_gbs = b_red / (t_red * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    dominant = "compress" if w.shards * t_comp >= t_red else "reduce"
+    if dominant == "compress":
+        ach, bytes_launch, kname = comp_gbs, b_comp, "compress"
+    else:
+        ach, bytes_launch, kname = red_gbs, b_red, "reduce"
+    traffic = read_traffic(kname, w.name, src_hash)
+
+    q = quality(w, bufs, sets_bits, c_in)
+    cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": "compress+reduce GB/s of bf16 input (fraction of HBM peak); quant rel-MSE",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.shards} bf16 shards of {w.rows}x{w.cols}; "
+                        f"compress {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym'][w.in_format]} "
+                        f"block {w.in_block}{' + Hadamard' if w.hadamard else ''}; decompress-reduce "
+                        + (f"-> {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym'][w.out_format]}"
+                           if w.out_format else "-> FP32 sum"),
+            "shards": w.shards, "rows": w.rows, "cols": w.cols,
+            "tensor_scale": args.scale_mode if fp8 else "n/a",
+            "launch": args.launch, "input_sets": nsets,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_launch,
+        },
+        "kernels": {
+            "compress_ms": round(t_comp, 5), "compress_GBs": round(comp_gbs, 1),
+            "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
+            "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "quality": q,
+        "cpu_baseline": cpu,
+        "source_hash": src_hash,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

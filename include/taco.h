@@ -1,0 +1,181 @@
+/*
+ * taco.h -- C ABI of the MI355X (gfx950) library that compresses and
+ * decompresses tensor-parallel activations.
+ *
+ * What it computes, by source (Pith review pages, cited by title and the
+ * section or figure on them):
+ *
+ *  [TACO]      "TACO: Efficient Communication Compression of Intermediate
+ *              Tensors for Scalable Tensor-Parallel LLM Training": Fig. 7
+ *              (adaptive rescaling -> ASH transform -> dual-scale FP8
+ *              quantization), Fig. 9 (one fused compression operator), Fig. 3
+ *              (E4M3), Fig. 6 / Eq. (3) (FP8 rounding error bound).
+ *  [EQuARX]    "EQuARX: Efficient Quantized AllReduce in XLA for Distributed
+ *              Machine Learning Acceleration": "What carries the argument"
+ *              (dynamic block-wise symmetric int8, one FP32 scale per 64
+ *              entries, dequantize to FP32 before adding).
+ *  [FlashComm] "Flash Communication: Reducing Tensor Parallelization
+ *              Bottleneck for Fast Large Language Model Inference": "What
+ *              carries the argument" (asymmetric group-128 INT4/INT8, local sum
+ *              of all chunks, INT8 re-quantization for the gather), Algorithm 1
+ *              (dequantize from codes, zero point and scale).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are row-major [rows, cols]; blocks (groups) are `block`
+ *    contiguous elements along cols, so cols must be a multiple of block. The
+ *    tensor is treated as n / block independent blocks (n = rows * cols).
+ *  - Device pointers are HIP device memory owned by the caller, 16-byte
+ *    aligned; the library allocates nothing and keeps no pointer after a
+ *    call returns. Inputs are never written; outputs must not overlap inputs.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    the caller synchronizes. All validation happens before anything is
+ *    enqueued; a call that returns an error has enqueued nothing.
+ *  - rows == 0 is valid and enqueues nothing.
+ *  - Return value: TACO_OK or a negative TACO_ERR_* code
+ *    (taco_status_string names it).
+ *  - Values are finite: for blocks whose inputs or intermediate results are
+ *    not finite the codes of that block are unspecified (no crash, other
+ *    blocks unaffected; with the data-driven FP8 tensor scale the whole
+ *    tensor is affected).
+ */
+#ifndef TACO_H_
+#define TACO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define TACO_OK 0
+#define TACO_ERR_INVALID_ARG (-1) /* null pointer, bad size, n out of [1,16], bad tensor_scale */
+#define TACO_ERR_SHAPE (-2)       /* cols not a multiple of block, or block not allowed for the format */
+#define TACO_ERR_FORMAT (-3)      /* unknown format, hadamard on a non-FP8 format, pair not allowed */
+#define TACO_ERR_ALIGN (-4)       /* a device pointer not 16-byte aligned */
+#define TACO_ERR_WORKSPACE (-5)   /* workspace missing or too small where one is required */
+#define TACO_ERR_HIP (-6)         /* a kernel launch failed (hipGetLastError) */
+
+/* ---- formats ------------------------------------------------------------
+ * TACO_FMT_FP8_DUAL  [TACO] E4M3 codes with a float32 tensor scale g and a
+ *                    per-block power-of-two exponent k (value = dec(q) * 2^-k * g);
+ *                    block 16, 32, 64 or 128; hadamard = 1 applies the
+ *                    unnormalised Sylvester Walsh-Hadamard transform to every
+ *                    block before quantizing (the ASH transform).
+ * TACO_FMT_INT8_SYM  [EQuARX] int8 in [-127, 127], float32 scale s = absmax / 127
+ *                    per block of 64 (value = q * s).
+ * TACO_FMT_INT4_ASYM [FlashComm] 4-bit codes, two per byte (element 2j in the
+ *                    low nibble), float32 scale s and uint8 zero point z per
+ *                    group of 128 (value = (q - z) * s).
+ * TACO_FMT_INT8_ASYM [FlashComm] the same at 8 bits (gather stage).
+ */
+#define TACO_FMT_FP8_DUAL 1
+#define TACO_FMT_INT8_SYM 2
+#define TACO_FMT_INT4_ASYM 3
+#define TACO_FMT_INT8_ASYM 4
+
+typedef struct taco_codec {
+  int32_t format;   /* TACO_FMT_* */
+  int32_t block;    /* elements per block / group along cols */
+  int32_t hadamard; /* FP8 only: 1 = block Walsh-Hadamard transform */
+  int32_t reserved; /* must be 0 */
+} taco_codec;
+
+/* Byte layout of one compressed tensor: one caller-allocated buffer of
+ * total_bytes, regions at 256-byte aligned offsets:
+ *   codes   n bytes (INT4: n / 2)
+ *   scale   FP8: int8 k[n / block]; others: float32 s[n / block]
+ *   aux     asymmetric formats: uint8 z[n / block]; others: empty
+ *   tensor  FP8: float32 g (16 bytes reserved); others: empty           */
+typedef struct taco_layout_t {
+  int64_t codes_off, codes_bytes;
+  int64_t scale_off, scale_bytes;
+  int64_t aux_off, aux_bytes;
+  int64_t tensor_off, tensor_bytes;
+  int64_t total_bytes;
+} taco_layout_t;
+
+/* tensor_scale values for taco_compress / taco_requantize (FP8 only):
+ *   > 0   use this g; it must lie in [2^-60, 2^60]
+ *   AUTO  g from this tensor: an abs-max pass over the transformed values
+ *         first, g = absmax / 448 (1 for an all-zero tensor), clamped to
+ *         [2^-60, 2^60]. Needs a workspace.
+ *   DELAYED  g from the abs-max the workspace recorded in its previous call
+ *         (1 if none): one pass; the history lives in the caller's workspace.
+ * Every FP8 call given a workspace records its own abs-max there.          */
+#define TACO_SCALE_AUTO 0.0f
+#define TACO_SCALE_DELAYED (-1.0f)
+#define TACO_MAX_SHARDS 16
+#define TACO_WORKSPACE_BYTES 256
+
+/* Layout of a compressed [rows, cols] tensor. Host only. */
+int taco_layout(taco_codec c, int64_t rows, int64_t cols, taco_layout_t* out);
+
+/* total_bytes of taco_layout, or a negative status. Host only. */
+int64_t taco_compressed_bytes(taco_codec c, int64_t rows, int64_t cols);
+
+/* Workspace size the FP8 scale modes need (TACO_WORKSPACE_BYTES; 0 for the
+ * other formats). The workspace is caller-owned device memory, zero-filled
+ * once before its first use; every call leaves it in a reusable state and
+ * carries the abs-max history for TACO_SCALE_DELAYED. Calls sharing one
+ * workspace must be ordered (same stream). Host only. */
+size_t taco_workspace_bytes(taco_codec c, int64_t rows, int64_t cols);
+
+/* Compress one bf16 shard: [TACO] Fig. 7 / Fig. 9 (transform, tensor scale,
+ * block exponent and E4M3 codes in one pass), [EQuARX] block-wise INT8,
+ * [FlashComm] group-128 asymmetric INT4/INT8.
+ *   x_bf16   device, bf16 [rows, cols]
+ *   out      device, taco_compressed_bytes(c, rows, cols) bytes (see layout)
+ *   tensor_scale, workspace, ws_bytes: FP8 only (see above); ignored otherwise */
+int taco_compress(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                  void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* taco_compress that also writes, for every element, the float32 value handed
+ * to the final rounding step (FP8: the scaled value encoded to E4M3; INT:
+ * value * (1/scale) before rounding) to `prequant` (device, n floats). */
+int taco_compress_debug(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                        void* workspace, size_t ws_bytes, float* prequant, hipStream_t stream);
+
+/* Decompress-reduce: dequantize each of n shards to float32 and add them in
+ * shard order, acc = ((0 + x_0) + x_1) + ..., one float32 rounding per add
+ * ([EQuARX]: dequantize to FP32 before adding; [FlashComm]: local sum of the
+ * chunks). Then, optionally,
+ *   sum_fp32     device float32 [rows, cols] receives acc (nullable)
+ *   requant_out  device buffer in c_out's layout receives acc re-quantized for
+ *                the gather stage (nullable): FP8 -> FP8 with tensor scale
+ *                g' = g_0 + ... + g_{n-1} and no second transform (the
+ *                transform is linear and shared by all shards); INT8_SYM ->
+ *                INT8_SYM; INT4_ASYM -> INT8_ASYM; INT8_ASYM -> INT8_ASYM. FP8
+ *                pairs need equal block and hadamard.
+ * At least one output must be given.
+ *   shards   host array of n device pointers, each a buffer in c_in's layout
+ *   n        1 .. TACO_MAX_SHARDS                                            */
+int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n, int64_t rows, int64_t cols,
+                           float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream);
+
+/* Quantize a caller-supplied float32 tensor with c_out (the gather-stage
+ * re-quantization on its own). FP8 takes the values as already transformed
+ * (no transform is applied); tensor_scale / workspace as for taco_compress. */
+int taco_requantize(taco_codec c_out, const float* x_fp32, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Consumer-side decode of one compressed tensor to float32 (out_dtype 0) or
+ * bf16 (out_dtype 1, nearest-even): dequantize and, for FP8 with hadamard,
+ * undo the transform (x = H y * 2^-log2(block), since H H = block * I). */
+int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                    hipStream_t stream);
+
+/* Test hook: the device's E4M3 encoder (the one every FP8 kernel uses) on n
+ * float32 values; codes are 1 byte each. Same argument rules as above. */
+int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
+
+/* Name of a status code. Host only; never returns NULL. */
+const char* taco_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TACO_H_ */

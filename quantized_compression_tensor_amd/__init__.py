@@ -1,0 +1,206 @@
+"""Python binding of the C ABI declared in include/taco.h.
+
+Argument marshalling only: every function below forwards to the function of
+the same name in libtaco.so (hand-written gfx950 HIP kernels). Tensors may be
+passed as torch tensors (their data_ptr is used) or as raw integer addresses;
+the stream defaults to torch's current HIP stream. A nonzero status raises
+TacoError. There is no fallback path: if the library cannot be built or
+loaded, importing this package fails.
+"""
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libtaco.so")
+
+TACO_OK = 0
+TACO_ERR_INVALID_ARG = -1
+TACO_ERR_SHAPE = -2
+TACO_ERR_FORMAT = -3
+TACO_ERR_ALIGN = -4
+TACO_ERR_WORKSPACE = -5
+TACO_ERR_HIP = -6
+
+TACO_FMT_FP8_DUAL = 1
+TACO_FMT_INT8_SYM = 2
+TACO_FMT_INT4_ASYM = 3
+TACO_FMT_INT8_ASYM = 4
+
+TACO_SCALE_AUTO = 0.0
+TACO_SCALE_DELAYED = -1.0
+TACO_MAX_SHARDS = 16
+TACO_WORKSPACE_BYTES = 256
+
+# Entry points declared in include/taco.h (checked by the ABI tests).
+EXPORTS = (
+    "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
+    "taco_compress_debug", "taco_decompress_reduce", "taco_requantize", "taco_decompress",
+    "taco_e4m3_encode", "taco_status_string",
+)
+
+
+class taco_codec(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("hadamard", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"taco_codec(format={self.format}, block={self.block}, hadamard={self.hadamard})"
+
+
+class taco_layout_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "codes_off", "codes_bytes", "scale_off", "scale_bytes", "aux_off", "aux_bytes",
+        "tensor_off", "tensor_bytes", "total_bytes")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+def codec(fmt, block, hadamard=0):
+    return taco_codec(int(fmt), int(block), int(hadamard), 0)
+
+
+class TacoError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {taco_status_string(status)} ({status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    C = taco_codec
+    sig = {
+        "taco_layout": (ctypes.c_int, [C, I64, I64, ctypes.POINTER(taco_layout_t)]),
+        "taco_compressed_bytes": (I64, [C, I64, I64]),
+        "taco_workspace_bytes": (SZ, [C, I64, I64]),
+        "taco_compress": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
+        "taco_compress_debug": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P, P]),
+        "taco_decompress_reduce": (ctypes.c_int, [C, ctypes.POINTER(P), I32, I64, I64, P, C, P, P]),
+        "taco_requantize": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
+        "taco_decompress": (ctypes.c_int, [C, P, I64, I64, P, I32, P]),
+        "taco_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
+        "taco_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    if torch.cuda.is_available() and torch.cuda.is_initialized():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(status, where):
+    if status != TACO_OK:
+        raise TacoError(status, where)
+    return status
+
+
+# ------------------------------------------------------------- host only --
+
+def taco_status_string(status):
+    return _lib.taco_status_string(int(status)).decode()
+
+
+def taco_layout(c, rows, cols):
+    L = taco_layout_t()
+    _check(_lib.taco_layout(c, rows, cols, ctypes.byref(L)), "taco_layout")
+    return L
+
+
+def taco_compressed_bytes(c, rows, cols):
+    n = _lib.taco_compressed_bytes(c, rows, cols)
+    if n < 0:
+        raise TacoError(int(n), "taco_compressed_bytes")
+    return n
+
+
+def taco_workspace_bytes(c, rows, cols):
+    return _lib.taco_workspace_bytes(c, rows, cols)
+
+
+# ------------------------------------------------------------ device ops --
+
+def taco_compress(c, x_bf16, rows, cols, tensor_scale, out, workspace=None, ws_bytes=None, stream=None):
+    wsb = ws_bytes if ws_bytes is not None else (TACO_WORKSPACE_BYTES if workspace is not None else 0)
+    return _check(_lib.taco_compress(c, _ptr(x_bf16), rows, cols, float(tensor_scale), _ptr(out),
+                                     _ptr(workspace), wsb, _stream(stream)), "taco_compress")
+
+
+def taco_compress_debug(c, x_bf16, rows, cols, tensor_scale, out, prequant, workspace=None, ws_bytes=None,
+                        stream=None):
+    wsb = ws_bytes if ws_bytes is not None else (TACO_WORKSPACE_BYTES if workspace is not None else 0)
+    return _check(_lib.taco_compress_debug(c, _ptr(x_bf16), rows, cols, float(tensor_scale), _ptr(out),
+                                           _ptr(workspace), wsb, _ptr(prequant), _stream(stream)),
+                  "taco_compress_debug")
+
+
+def taco_decompress_reduce(c_in, shards, rows, cols, sum_fp32=None, c_out=None, requant_out=None, stream=None):
+    arr = (ctypes.c_void_p * max(1, len(shards)))(*[_ptr(s) for s in shards])
+    co = c_out if c_out is not None else taco_codec(0, 0, 0, 0)
+    return _check(_lib.taco_decompress_reduce(c_in, arr, len(shards), rows, cols, _ptr(sum_fp32), co,
+                                              _ptr(requant_out), _stream(stream)), "taco_decompress_reduce")
+
+
+def taco_requantize(c_out, x_fp32, rows, cols, tensor_scale, out, workspace=None, ws_bytes=None, stream=None):
+    wsb = ws_bytes if ws_bytes is not None else (TACO_WORKSPACE_BYTES if workspace is not None else 0)
+    return _check(_lib.taco_requantize(c_out, _ptr(x_fp32), rows, cols, float(tensor_scale), _ptr(out),
+                                       _ptr(workspace), wsb, _stream(stream)), "taco_requantize")
+
+
+def taco_decompress(c, inp, rows, cols, out, out_dtype=0, stream=None):
+    return _check(_lib.taco_decompress(c, _ptr(inp), rows, cols, _ptr(out), int(out_dtype), _stream(stream)),
+                  "taco_decompress")
+
+
+def taco_e4m3_encode(x, codes, n, stream=None):
+    return _check(_lib.taco_e4m3_encode(_ptr(x), _ptr(codes), n, _stream(stream)), "taco_e4m3_encode")
+
+
+# ------------------------------------------------- buffer plumbing (torch) --
+
+def empty_compressed(c, rows, cols, device="cuda"):
+    """A uint8 device tensor sized for one compressed [rows, cols] tensor."""
+    import torch
+    return torch.empty(max(1, taco_compressed_bytes(c, rows, cols)), dtype=torch.uint8, device=device)
+
+
+def regions(buf, c, rows, cols):
+    """Views of a compressed buffer's regions (codes, scale, aux, tensor), as laid
+    out by taco_layout: codes uint8; scale int8 (FP8) or float32; aux uint8;
+    tensor float32[4] (FP8) -- for tests and inspection."""
+    import torch
+    L = taco_layout(c, rows, cols)
+    codes = buf[L.codes_off:L.codes_off + L.codes_bytes]
+    sc = buf[L.scale_off:L.scale_off + L.scale_bytes]
+    sc = sc.view(torch.int8) if c.format == TACO_FMT_FP8_DUAL else sc.view(torch.float32)
+    aux = buf[L.aux_off:L.aux_off + L.aux_bytes]
+    ten = buf[L.tensor_off:L.tensor_off + L.tensor_bytes].view(torch.float32)
+    return codes, sc, aux, ten

@@ -1,0 +1,183 @@
+// Device helpers shared by the gfx950 kernels of the compression library.
+//
+// Every floating-point step is written so that it performs exactly the float32
+// operations (one round-to-nearest-even each) that the codec definitions call
+// for; files are compiled with contraction off, IEEE mode and float32
+// denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "taco_internal.h"
+
+#define TACO_DEV __device__ __forceinline__
+
+namespace taco {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;
+
+constexpr float kE4M3Max = 448.0f;
+// Blocks whose abs-max (symmetric) or range (asymmetric) is below this are
+// stored as zero codes with a zero scale, so 127/A and qmax/r stay finite.
+constexpr float kTiny = 0x1p-100f;
+
+// ---------------------------------------------------------------- loads --
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is read once).
+TACO_DEV uint4 ld16_nt(const void* p) {
+  u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------------ bf16 --
+TACO_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+TACO_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bf16, nearest-even; NaN -> 0x7FC0.
+TACO_DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (f != f) ? 0x7FC0u : r;
+}
+
+// ------------------------------------------------------------------- E4M3 --
+// Hardware OCP E4M3 conversions of gfx950 (nearest-even). Four floats ->
+// one dword, element i in byte i.
+TACO_DEV uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+TACO_DEV void e4m3_unpack4(uint32_t w, float* o) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+
+// Saturate to +-448 keeping NaN (only reached when a block exponent is
+// clamped, i.e. the block maximum cannot be brought down to 448).
+TACO_DEV float sat448(float v) {
+  return (fabsf(v) > kE4M3Max) ? copysignf(kE4M3Max, v) : v;
+}
+
+// ------------------------------------------------------- scales, exponents --
+// 2^k as a float for k in [-126, 127].
+TACO_DEV float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// Block exponent: largest k in [-64, 63] with m * 2^k <= 448 (m >= 0), 0 for
+// m == 0. From the float bits: with m = 1.f * 2^(e-127), the frexp fraction
+// is <= 0.875 exactly when the stored mantissa is <= 0x600000, giving
+// k = 135 - e or 134 - e; subnormal m clamps to 63 and infinity to -64.
+TACO_DEV int block_exponent(float m) {
+  uint32_t b = __float_as_uint(m);
+  int k = ((b & 0x7FFFFFu) <= 0x600000u ? 135 : 134) - (int)(b >> 23);
+  k = k < -64 ? -64 : (k > 63 ? 63 : k);
+  return b == 0 ? 0 : k;
+}
+
+// Data-driven tensor scale from an abs-max A (FP8 dual-scale).
+TACO_DEV float tensor_scale_from_amax(float A) {
+  if (A == 0.0f) return 1.0f;
+  float g = A / kE4M3Max;
+  return fminf(fmaxf(g, kGMin), kGMax);
+}
+
+// Round to the nearest integer, ties to even, for |t| < 2^22: adding
+// 1.5 * 2^23 lands in the binade whose spacing is 1, so the float add does
+// the rounding; the result is read back from the bits.
+TACO_DEV int rne_int(float t) {
+  return (int)(__float_as_uint(t + 12582912.0f) - 0x4B400000u);
+}
+
+// ----------------------------------------------------------- lane exchange --
+// DPP patterns inside a 16-lane row. Each is one hardware lane permutation:
+//   X1 = lane ^ 1, X2 = lane ^ 2 (quad permutes), X7 = lane ^ 7 (half-row
+//   mirror), X8 = lane ^ 8 (row rotate by 8).
+#define TACO_DPP_X1 "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+#define TACO_DPP_X2 "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+#define TACO_DPP_X7 "row_half_mirror row_mask:0xf bank_mask:0xf"
+#define TACO_DPP_X8 "row_ror:8 row_mask:0xf bank_mask:0xf"
+
+// max / min over groups of G lanes (G = 1, 2, 4, 8, 16; groups aligned to G),
+// one DPP op per step. The leading s_nop covers the hazards between a VALU or
+// EXEC write and a DPP read; between chained steps one s_nop 1 suffices.
+template <int G>
+TACO_DEV float group_max(float a) {
+  if constexpr (G >= 2) asm volatile("s_nop 4\n\tv_max_f32_dpp %0, %0, %0 " TACO_DPP_X1 : "+v"(a));
+  if constexpr (G >= 4) asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " TACO_DPP_X2 : "+v"(a));
+  if constexpr (G >= 8) asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " TACO_DPP_X7 : "+v"(a));
+  if constexpr (G >= 16) asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " TACO_DPP_X8 : "+v"(a));
+  return a;
+}
+
+template <int G>
+TACO_DEV float group_min(float a) {
+  if constexpr (G >= 2) asm volatile("s_nop 4\n\tv_min_f32_dpp %0, %0, %0 " TACO_DPP_X1 : "+v"(a));
+  if constexpr (G >= 4) asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %0, %0 " TACO_DPP_X2 : "+v"(a));
+  if constexpr (G >= 8) asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %0, %0 " TACO_DPP_X7 : "+v"(a));
+  if constexpr (G >= 16) asm volatile("s_nop 1\n\tv_min_f32_dpp %0, %0, %0 " TACO_DPP_X8 : "+v"(a));
+  return a;
+}
+
+// Max of 8 magnitudes (non-negative result).
+TACO_DEV float absmax8(const float* v) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  float b = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  float c = fmaxf(fabsf(v[6]), fabsf(v[7]));
+  return fmaxf(fmaxf(a, b), c);
+}
+
+// Whole-wave max of a non-negative float (result valid in every lane).
+TACO_DEV float wave_max(float a) {
+  a = group_max<16>(a);
+  a = fmaxf(a, __shfl_xor(a, 16));
+  a = fmaxf(a, __shfl_xor(a, 32));
+  return a;
+}
+
+// ------------------------------------------------------------- workspace --
+// Caller-owned, zero-initialised once; every kernel that uses it leaves
+// `arrivals` and `amax_acc` at zero again. `amax_last` holds the abs-max of
+// the transformed tensor seen by the most recent call.
+struct Workspace {
+  uint32_t arrivals;
+  uint32_t amax_acc;    // float bits of a non-negative max
+  uint32_t amax_last;   // float bits
+  uint32_t calls;
+};
+
+TACO_DEV float ws_load_amax_last(Workspace* ws) {
+  return __uint_as_float(__hip_atomic_load(&ws->amax_last, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Fold one workgroup's non-negative max into the workspace; the last
+// workgroup to arrive publishes the tensor max and resets the accumulators.
+// Must be called by every workgroup of the grid, by thread 0 only.
+TACO_DEV void ws_publish_amax(Workspace* ws, float wg_max, uint32_t num_groups) {
+  __hip_atomic_fetch_max(&ws->amax_acc, __float_as_uint(wg_max), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t prev = __hip_atomic_fetch_add(&ws->arrivals, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev == num_groups - 1) {
+    uint32_t a = __hip_atomic_exchange(&ws->amax_acc, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws->amax_last, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&ws->calls, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws->arrivals, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Workgroup max of a non-negative float through LDS (all threads call it).
+TACO_DEV float block_max(float a, float* lds4) {
+  a = wave_max(a);
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds4[wave] = a;
+  __syncthreads();
+  float r = fmaxf(fmaxf(lds4[0], lds4[1]), fmaxf(lds4[2], lds4[3]));
+  return r;
+}
+
+}  // namespace taco

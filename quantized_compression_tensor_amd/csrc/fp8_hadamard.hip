@@ -1,0 +1,367 @@
+// TACO FP8 path with the block Hadamard transform: fused compress, the
+// abs-max pre-pass for the data-driven tensor scale, and the consumer-side
+// decode.
+//
+// Source: "TACO: Efficient Communication Compression of Intermediate Tensors
+// for Scalable Tensor-Parallel LLM Training" (Pith review page) -- Fig. 7
+// (adaptive rescaling, ASH transform, dual-scale quantization), Fig. 9 (one
+// fused operator instead of a chain of kernels), abstract (the fused operator
+// cuts memory traffic and launches). The transform is the unnormalised
+// Sylvester Walsh-Hadamard matrix on B contiguous elements along the hidden
+// dimension, butterflies of half-width 1, 2, ..., B/2 in that order; the
+// dual scale is a float32 tensor scale g times a per-block power of two 2^-k.
+//
+// Wave layout. A wave holds 512 consecutive elements, 8 per lane (one 16-byte
+// bf16 load). A block of B elements sits in G = B/8 consecutive lanes. Inside
+// a lane the 8 elements differ in index bits 0-2, so the first three
+// butterfly stages are plain register arithmetic. Index bits 3-6 select the
+// lane's 8-element chunk; lane j of a group holds chunk
+//     c(j) = j ^ (bit2(j) ? 3 : 0),
+// which makes flipping chunk bit 0, 1, 2, 3 the lane permutations j^1, j^2,
+// j^7, j^8 -- each a single DPP pattern (quad permute, quad permute, half-row
+// mirror, row rotate by 8). The memory access stays one contiguous 1 KiB
+// span per wave.
+//
+// Sign tracking. A cross-lane butterfly needs a+b in one lane and a-b in its
+// partner. Each lane instead computes own + s * partner with one DPP-fed
+// fused multiply-add (s = +-1, so the product is exact and the single
+// rounding equals that of a+b or a-b); the upper lane then holds -(a-b). The
+// sign a lane carries after all stages is the parity of its chunk index, and
+// is folded into the scale that follows. Nonzero results are bit-identical
+// to the plain butterflies; an exact zero may carry either sign and is
+// normalised to +0 by the final fused multiply-add with a +0 addend.
+#include "device_common.h"
+#include "taco_internal.h"
+
+namespace taco {
+
+constexpr int kTileElems = 512;   // per wave
+
+template <int LOGB>
+struct HadGeom {
+  static constexpr int B = 1 << LOGB;
+  static constexpr int G = B / 8;            // lanes per block
+  static constexpr int BPT = kTileElems / B; // blocks per wave tile
+  static constexpr int STAGES = LOGB - 3;    // cross-lane stages
+};
+
+// Chunk index of this lane inside its block.
+template <int G>
+TACO_DEV int lane_chunk(int lane) {
+  int j = lane & (G - 1);
+  if constexpr (G >= 8) j ^= ((j >> 2) & 1) * 3;
+  return j;
+}
+
+TACO_DEV float sgn_bit(int c, int bit) { return ((c >> bit) & 1) ? -1.0f : 1.0f; }
+
+// Butterflies of half-width 1, 2, 4 on the lane's 8 registers.
+TACO_DEV void fwht_in_lane(float* v) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+#define TACO_FMAC8(S, DPP)                                   \
+  "v_fmac_f32_dpp %0, %0, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %1, %1, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %2, %2, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %3, %3, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %4, %4, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %5, %5, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %6, %6, " S " " DPP "\n\t"                 \
+  "v_fmac_f32_dpp %7, %7, " S " " DPP "\n\t"
+
+// Cross-lane butterfly stages (chunk bits 0 .. STAGES-1). Eight independent
+// registers per stage keep every DPP read at least seven instructions after
+// the write it depends on; the leading s_nop covers the code before.
+template <int STAGES>
+TACO_DEV void fwht_cross_lane(float* v, float s0, float s1, float s2, float s3) {
+  if constexpr (STAGES == 1) {
+    asm volatile("s_nop 4\n\t" TACO_FMAC8("%8", TACO_DPP_X1)
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "v"(s0));
+  } else if constexpr (STAGES == 2) {
+    asm volatile("s_nop 4\n\t" TACO_FMAC8("%8", TACO_DPP_X1) TACO_FMAC8("%9", TACO_DPP_X2)
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "v"(s0), "v"(s1));
+  } else if constexpr (STAGES == 3) {
+    asm volatile("s_nop 4\n\t" TACO_FMAC8("%8", TACO_DPP_X1) TACO_FMAC8("%9", TACO_DPP_X2)
+                     TACO_FMAC8("%10", TACO_DPP_X7)
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "v"(s0), "v"(s1), "v"(s2));
+  } else {
+    static_assert(STAGES == 4, "block of 16 to 128");
+    asm volatile("s_nop 4\n\t" TACO_FMAC8("%8", TACO_DPP_X1) TACO_FMAC8("%9", TACO_DPP_X2)
+                     TACO_FMAC8("%10", TACO_DPP_X7) TACO_FMAC8("%11", TACO_DPP_X8)
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "v"(s0), "v"(s1), "v"(s2), "v"(s3));
+  }
+}
+
+// Lane constants of the transform: per-stage signs and the final parity sign.
+template <int LOGB>
+struct LaneSigns {
+  float s0, s1, s2, s3, parity;
+  int elem_off;  // element offset of this lane's chunk inside the wave tile
+  TACO_DEV explicit LaneSigns(int lane) {
+    using Gm = HadGeom<LOGB>;
+    const int c = lane_chunk<Gm::G>(lane);
+    s0 = sgn_bit(c, 0); s1 = sgn_bit(c, 1); s2 = sgn_bit(c, 2); s3 = sgn_bit(c, 3);
+    parity = (__builtin_popcount(c) & 1) ? -1.0f : 1.0f;
+    elem_off = ((lane & ~(Gm::G - 1)) | c) * 8;
+  }
+};
+
+TACO_DEV void widen8(uint4 w, float* v) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// ------------------------------------------------------------ compress --
+//
+// One pass: load bf16, transform, block abs-max, exponent, scale, E4M3
+// encode, store codes and exponents. With GFROM_WS the tensor scale comes from
+// the abs-max the workspace recorded (the pre-pass of this call, or the
+// previous call: delayed scaling); otherwise from the argument. With a
+// workspace the kernel also records this tensor's abs-max for the next call.
+template <int LOGB, bool GFROM_WS, bool DEBUG, int T>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
+    const uint4* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
+    float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
+    float* __restrict__ dbg) {
+  using Gm = HadGeom<LOGB>;
+  __shared__ float lds4[4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const LaneSigns<LOGB> ls(lane);
+  const int row = lane / Gm::G;
+
+  float g = GFROM_WS ? tensor_scale_from_amax(ws_load_amax_last(ws)) : g_arg;
+  const float inv_g = 1.0f / g;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
+
+  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
+  uint4 raw[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int64_t blk = (tile0 + i) * Gm::BPT + row;
+    raw[i] = make_uint4(0, 0, 0, 0);
+    if (blk < nblocks) raw[i] = ld16_nt(x + ((tile0 + i) * kTileElems + ls.elem_off) / 8);
+  }
+
+  float run_max = 0.0f;
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int64_t blk = (tile0 + i) * Gm::BPT + row;
+    float v[8];
+    widen8(raw[i], v);
+    fwht_in_lane(v);
+    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+    const float M = group_max<Gm::G>(absmax8(v));
+    run_max = fmaxf(run_max, M);
+    const float m = M * inv_g;
+    const int k = block_exponent(m);
+    const float c = inv_g * pow2f(k) * ls.parity;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], c, 0.0f);
+    if (__builtin_expect(m * pow2f(k) > kE4M3Max, 0)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sat448(v[e]);
+    }
+    if (blk < nblocks) {
+      const int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
+      uint2 q;
+      q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
+      q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
+      *reinterpret_cast<uint2*>(codes + eoff) = q;
+      if ((lane & (Gm::G - 1)) == 0) kexp[blk] = (int8_t)k;
+      if constexpr (DEBUG) {
+        float4* d = reinterpret_cast<float4*>(dbg + eoff);
+        d[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+  if (ws != nullptr) {
+    const float wg = block_max(run_max, lds4);
+    if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
+  }
+}
+
+// Abs-max of the transformed tensor, published into the workspace.
+template <int LOGB, int T>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint4* __restrict__ x, int64_t nblocks,
+                                                                Workspace* __restrict__ ws) {
+  using Gm = HadGeom<LOGB>;
+  __shared__ float lds4[4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const LaneSigns<LOGB> ls(lane);
+  const int row = lane / Gm::G;
+  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
+  uint4 raw[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int64_t blk = (tile0 + i) * Gm::BPT + row;
+    raw[i] = make_uint4(0, 0, 0, 0);
+    if (blk < nblocks) raw[i] = ld16_nt(x + ((tile0 + i) * kTileElems + ls.elem_off) / 8);
+  }
+  float run_max = 0.0f;
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    float v[8];
+    widen8(raw[i], v);
+    fwht_in_lane(v);
+    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+    run_max = fmaxf(run_max, absmax8(v));
+  }
+  const float wg = block_max(run_max, lds4);
+  if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
+}
+
+// --------------------------------------------------------------- decode --
+//
+// Consumer side: dequantize (dec(q) * g * 2^-k, the combined scale is exact),
+// inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
+// factor, then float32 or bf16 output.
+template <int LOGB, bool BF16OUT, int T>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
+    const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
+    int64_t nblocks, void* __restrict__ out) {
+  using Gm = HadGeom<LOGB>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const LaneSigns<LOGB> ls(lane);
+  const int row = lane / Gm::G;
+  const float g = *g_hdr;
+  const float outscale = pow2f(-LOGB) * ls.parity;
+  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
+  uint2 raw[T];
+  int kk[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int64_t blk = (tile0 + i) * Gm::BPT + row;
+    raw[i] = make_uint2(0, 0);
+    kk[i] = 0;
+    if (blk < nblocks) {
+      raw[i] = *reinterpret_cast<const uint2*>(codes + (tile0 + i) * kTileElems + ls.elem_off);
+      kk[i] = kexp[blk];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int64_t blk = (tile0 + i) * Gm::BPT + row;
+    const float d = g * pow2f(-kk[i]);
+    float v[8];
+    e4m3_unpack4(raw[i].x, v);
+    e4m3_unpack4(raw[i].y, v + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * d;
+    fwht_in_lane(v);
+    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], outscale, 0.0f);
+    if (blk < nblocks) {
+      const int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
+      if constexpr (BF16OUT) {
+        uint4 o;
+        o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+        o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+        o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+        o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + eoff) = o;
+      } else {
+        float4* d4 = reinterpret_cast<float4*>(static_cast<float*>(out) + eoff);
+        d4[0] = make_float4(v[0], v[1], v[2], v[3]);
+        d4[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers --
+
+constexpr int kCompressTiles = 4;
+
+static int64_t had_groups(int logb, int64_t nblocks, int T) {
+  const int64_t elems = nblocks << logb;
+  const int64_t tiles = (elems + kTileElems - 1) / kTileElems;
+  return (tiles + 4 * T - 1) / (4 * T);
+}
+
+template <int LOGB>
+static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
+  constexpr int T = kCompressTiles;
+  const int64_t groups = had_groups(LOGB, a.nblocks, T);
+  if (groups == 0) return hipSuccess;
+  dim3 grid((unsigned)groups), block(kBlockThreads);
+  auto* x = static_cast<const uint4*>(a.x);
+  auto* ws = static_cast<Workspace*>(a.ws);
+  if (a.auto_prepass) {
+    hipLaunchKernelGGL((k_fp8_had_amax<LOGB, T>), grid, block, 0, s, x, a.nblocks, ws);
+  }
+  if (a.g_from_ws) {
+    if (a.dbg)
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, true, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                         a.nblocks, a.g, ws, a.dbg);
+    else
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, false, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                         a.nblocks, a.g, ws, a.dbg);
+  } else {
+    if (a.dbg)
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, true, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                         a.nblocks, a.g, ws, a.dbg);
+    else
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, false, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                         a.nblocks, a.g, ws, a.dbg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s) {
+  switch (a.logb) {
+    case 4: return launch_compress_logb<4>(a, s);
+    case 5: return launch_compress_logb<5>(a, s);
+    case 6: return launch_compress_logb<6>(a, s);
+    case 7: return launch_compress_logb<7>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int LOGB>
+static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
+  constexpr int T = 2;
+  const int64_t groups = had_groups(LOGB, a.nblocks, T);
+  if (groups == 0) return hipSuccess;
+  dim3 grid((unsigned)groups), block(kBlockThreads);
+  if (a.bf16_out)
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, true, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
+                       a.out);
+  else
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, false, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
+                       a.out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_had_decode(const FP8HadDecodeArgs& a, hipStream_t s) {
+  switch (a.logb) {
+    case 4: return launch_decode_logb<4>(a, s);
+    case 5: return launch_decode_logb<5>(a, s);
+    case 6: return launch_decode_logb<6>(a, s);
+    case 7: return launch_decode_logb<7>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace taco

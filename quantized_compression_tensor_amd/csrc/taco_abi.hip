@@ -1,0 +1,270 @@
+// The C ABI: validation, buffer layout and kernel dispatch. Everything here is
+// host code; all checks run before any work is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "taco.h"
+#include "taco_internal.h"
+
+namespace {
+
+using namespace taco;
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+int check_codec(const taco_codec& c) {
+  if (c.reserved != 0) return TACO_ERR_INVALID_ARG;
+  switch (c.format) {
+    case TACO_FMT_FP8_DUAL:
+      if (c.hadamard != 0 && c.hadamard != 1) return TACO_ERR_FORMAT;
+      if (c.block != 16 && c.block != 32 && c.block != 64 && c.block != 128) return TACO_ERR_SHAPE;
+      return TACO_OK;
+    case TACO_FMT_INT8_SYM:
+      if (c.hadamard != 0) return TACO_ERR_FORMAT;
+      return c.block == 64 ? TACO_OK : TACO_ERR_SHAPE;
+    case TACO_FMT_INT4_ASYM:
+    case TACO_FMT_INT8_ASYM:
+      if (c.hadamard != 0) return TACO_ERR_FORMAT;
+      return c.block == 128 ? TACO_OK : TACO_ERR_SHAPE;
+    default:
+      return TACO_ERR_FORMAT;
+  }
+}
+
+int check_shape(const taco_codec& c, int64_t rows, int64_t cols) {
+  int st = check_codec(c);
+  if (st != TACO_OK) return st;
+  if (rows < 0 || cols <= 0) return TACO_ERR_INVALID_ARG;
+  if (cols % c.block != 0) return TACO_ERR_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return TACO_ERR_INVALID_ARG;
+  return TACO_OK;
+}
+
+void layout_of(const taco_codec& c, int64_t n, taco_layout_t* L) {
+  const int64_t nb = n / c.block;
+  L->codes_off = 0;
+  L->codes_bytes = c.format == TACO_FMT_INT4_ASYM ? n / 2 : n;
+  L->scale_off = align256(L->codes_bytes);
+  L->scale_bytes = c.format == TACO_FMT_FP8_DUAL ? nb : 4 * nb;
+  L->aux_off = align256(L->scale_off + L->scale_bytes);
+  L->aux_bytes = (c.format == TACO_FMT_INT4_ASYM || c.format == TACO_FMT_INT8_ASYM) ? nb : 0;
+  L->tensor_off = align256(L->aux_off + L->aux_bytes);
+  L->tensor_bytes = c.format == TACO_FMT_FP8_DUAL ? 16 : 0;
+  L->total_bytes = align256(L->tensor_off + L->tensor_bytes);
+}
+
+int log2_block(int b) { return b == 16 ? 4 : b == 32 ? 5 : b == 64 ? 6 : 7; }
+
+// FP8 tensor-scale mode: 0 = given g, 1 = auto (pre-pass), 2 = delayed.
+int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, int* mode) {
+  *mode = 0;
+  if (c.format != TACO_FMT_FP8_DUAL) return TACO_OK;
+  if (isnan(ts) || isinf(ts)) return TACO_ERR_INVALID_ARG;
+  if (ts > 0.0f) {
+    if (ts < kGMin || ts > kGMax) return TACO_ERR_INVALID_ARG;
+  } else {
+    *mode = (ts == 0.0f) ? 1 : 2;
+    if (ws == nullptr || ws_bytes < TACO_WORKSPACE_BYTES) return TACO_ERR_WORKSPACE;
+  }
+  if (ws != nullptr && (ws_bytes < TACO_WORKSPACE_BYTES || !aligned16(ws))) return TACO_ERR_WORKSPACE;
+  return TACO_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
+
+struct Regions {
+  uint8_t* codes;
+  void* scale;
+  uint8_t* aux;
+  float* tensor;
+};
+
+Regions regions_of(void* buf, const taco_layout_t& L) {
+  uint8_t* b = static_cast<uint8_t*>(buf);
+  return Regions{b + L.codes_off, b + L.scale_off, b + L.aux_off, reinterpret_cast<float*>(b + L.tensor_off)};
+}
+
+int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int64_t cols, float ts, void* out,
+                    void* ws, size_t ws_bytes, float* dbg, hipStream_t stream) {
+  int st = check_shape(c, rows, cols);
+  if (st != TACO_OK) return st;
+  int mode = 0;
+  st = scale_mode(c, ts, ws, ws_bytes, &mode);
+  if (st != TACO_OK) return st;
+  const int64_t n = rows * cols;
+  if (n == 0) return TACO_OK;
+  if (x == nullptr || out == nullptr) return TACO_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out) || (dbg && !aligned16(dbg))) return TACO_ERR_ALIGN;
+  taco_layout_t L;
+  layout_of(c, n, &L);
+  const int64_t in_bytes = n * (f32_in ? 4 : 2);
+  if (overlaps(x, in_bytes, out, L.total_bytes)) return TACO_ERR_INVALID_ARG;
+  if (dbg && (overlaps(dbg, 4 * n, x, in_bytes) || overlaps(dbg, 4 * n, out, L.total_bytes)))
+    return TACO_ERR_INVALID_ARG;
+  Regions R = regions_of(out, L);
+  if (c.format == TACO_FMT_FP8_DUAL && c.hadamard == 1 && !f32_in) {
+    FP8HadArgs a;
+    a.x = x; a.codes = R.codes; a.kexp = static_cast<int8_t*>(R.scale); a.g_hdr = R.tensor;
+    a.nblocks = n / c.block; a.logb = log2_block(c.block);
+    a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
+    a.ws = ws; a.dbg = dbg;
+    return hip_status(launch_fp8_had_compress(a, stream));
+  }
+  QuantArgs a;
+  a.fmt = c.format; a.block = c.block; a.f32_in = f32_in; a.x = x; a.n = n;
+  a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
+  a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
+  a.ws = c.format == TACO_FMT_FP8_DUAL ? ws : nullptr; a.dbg = dbg;
+  return hip_status(launch_quantize(a, stream));
+}
+
+bool pair_allowed(const taco_codec& i, const taco_codec& o) {
+  if (i.format == TACO_FMT_FP8_DUAL)
+    return o.format == TACO_FMT_FP8_DUAL && o.block == i.block && o.hadamard == i.hadamard;
+  if (i.format == TACO_FMT_INT8_SYM) return o.format == TACO_FMT_INT8_SYM;
+  if (i.format == TACO_FMT_INT4_ASYM) return o.format == TACO_FMT_INT8_ASYM;
+  if (i.format == TACO_FMT_INT8_ASYM) return o.format == TACO_FMT_INT8_ASYM;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int taco_layout(taco_codec c, int64_t rows, int64_t cols, taco_layout_t* out) {
+  if (out == nullptr) return TACO_ERR_INVALID_ARG;
+  int st = check_shape(c, rows, cols);
+  if (st != TACO_OK) return st;
+  layout_of(c, rows * cols, out);
+  return TACO_OK;
+}
+
+int64_t taco_compressed_bytes(taco_codec c, int64_t rows, int64_t cols) {
+  taco_layout_t L;
+  int st = taco_layout(c, rows, cols, &L);
+  return st == TACO_OK ? L.total_bytes : (int64_t)st;
+}
+
+size_t taco_workspace_bytes(taco_codec c, int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return c.format == TACO_FMT_FP8_DUAL ? TACO_WORKSPACE_BYTES : 0;
+}
+
+int taco_compress(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return quantize_common(c, x_bf16, false, rows, cols, tensor_scale, out, workspace, ws_bytes, nullptr, stream);
+}
+
+int taco_compress_debug(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                        void* workspace, size_t ws_bytes, float* prequant, hipStream_t stream) {
+  if (prequant == nullptr) return TACO_ERR_INVALID_ARG;
+  return quantize_common(c, x_bf16, false, rows, cols, tensor_scale, out, workspace, ws_bytes, prequant, stream);
+}
+
+int taco_requantize(taco_codec c_out, const float* x_fp32, int64_t rows, int64_t cols, float tensor_scale, void* out,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return quantize_common(c_out, x_fp32, true, rows, cols, tensor_scale, out, workspace, ws_bytes, nullptr, stream);
+}
+
+int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n, int64_t rows, int64_t cols,
+                           float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream) {
+  int st = check_shape(c_in, rows, cols);
+  if (st != TACO_OK) return st;
+  if (requant_out != nullptr) {
+    st = check_shape(c_out, rows, cols);
+    if (st != TACO_OK) return st;
+    if (!pair_allowed(c_in, c_out)) return TACO_ERR_FORMAT;
+  }
+  if (shards == nullptr || n < 1 || n > TACO_MAX_SHARDS) return TACO_ERR_INVALID_ARG;
+  if (sum_fp32 == nullptr && requant_out == nullptr) return TACO_ERR_INVALID_ARG;
+  const int64_t elems = rows * cols;
+  taco_layout_t Li, Lo;
+  layout_of(c_in, elems, &Li);
+  layout_of(requant_out ? c_out : c_in, elems, &Lo);
+  for (int r = 0; r < n; ++r) {
+    if (shards[r] == nullptr) return TACO_ERR_INVALID_ARG;
+    if (!aligned16(shards[r])) return TACO_ERR_ALIGN;
+  }
+  if ((sum_fp32 && !aligned16(sum_fp32)) || (requant_out && !aligned16(requant_out))) return TACO_ERR_ALIGN;
+  for (int r = 0; r < n; ++r) {
+    if (sum_fp32 && overlaps(shards[r], Li.total_bytes, sum_fp32, 4 * elems)) return TACO_ERR_INVALID_ARG;
+    if (requant_out && overlaps(shards[r], Li.total_bytes, requant_out, Lo.total_bytes)) return TACO_ERR_INVALID_ARG;
+  }
+  if (sum_fp32 && requant_out && overlaps(sum_fp32, 4 * elems, requant_out, Lo.total_bytes))
+    return TACO_ERR_INVALID_ARG;
+  if (elems == 0) return TACO_OK;
+  ReduceArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fin = c_in.format; a.bin = c_in.block;
+  a.fout = requant_out ? c_out.format : c_in.format; a.bout = requant_out ? c_out.block : c_in.block;
+  a.nshards = n; a.n = elems;
+  for (int r = 0; r < n; ++r) {
+    Regions R = regions_of(const_cast<void*>(shards[r]), Li);
+    a.in.codes[r] = R.codes; a.in.scale[r] = R.scale; a.in.zero[r] = R.aux; a.in.g[r] = R.tensor;
+  }
+  a.sum = sum_fp32;
+  if (requant_out) {
+    Regions O = regions_of(requant_out, Lo);
+    a.rq_codes = O.codes; a.rq_scale = O.scale; a.rq_zero = O.aux; a.rq_g_hdr = O.tensor;
+  }
+  return hip_status(launch_reduce(a, stream));
+}
+
+int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                    hipStream_t stream) {
+  int st = check_shape(c, rows, cols);
+  if (st != TACO_OK) return st;
+  if (out_dtype != 0 && out_dtype != 1) return TACO_ERR_INVALID_ARG;
+  const int64_t n = rows * cols;
+  if (n == 0) return TACO_OK;
+  if (in == nullptr || out == nullptr) return TACO_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out)) return TACO_ERR_ALIGN;
+  taco_layout_t L;
+  layout_of(c, n, &L);
+  if (overlaps(in, L.total_bytes, out, n * (out_dtype ? 2 : 4))) return TACO_ERR_INVALID_ARG;
+  Regions R = regions_of(const_cast<void*>(in), L);
+  if (c.format == TACO_FMT_FP8_DUAL && c.hadamard == 1) {
+    FP8HadDecodeArgs a;
+    a.codes = R.codes; a.kexp = static_cast<const int8_t*>(R.scale); a.g_hdr = R.tensor;
+    a.nblocks = n / c.block; a.logb = log2_block(c.block); a.bf16_out = out_dtype == 1; a.out = out;
+    return hip_status(launch_fp8_had_decode(a, stream));
+  }
+  DequantArgs a;
+  a.fmt = c.format; a.block = c.block; a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
+  a.n = n; a.bf16_out = out_dtype == 1; a.out = out;
+  return hip_status(launch_dequantize(a, stream));
+}
+
+int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+  if (n < 0 || n > kMaxElems) return TACO_ERR_INVALID_ARG;
+  if (n == 0) return TACO_OK;
+  if (x == nullptr || codes == nullptr) return TACO_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return TACO_ERR_ALIGN;
+  if (overlaps(x, 4 * n, codes, n)) return TACO_ERR_INVALID_ARG;
+  return hip_status(launch_e4m3_encode(x, codes, n, stream));
+}
+
+const char* taco_status_string(int status) {
+  switch (status) {
+    case TACO_OK: return "TACO_OK";
+    case TACO_ERR_INVALID_ARG: return "TACO_ERR_INVALID_ARG";
+    case TACO_ERR_SHAPE: return "TACO_ERR_SHAPE";
+    case TACO_ERR_FORMAT: return "TACO_ERR_FORMAT";
+    case TACO_ERR_ALIGN: return "TACO_ERR_ALIGN";
+    case TACO_ERR_WORKSPACE: return "TACO_ERR_WORKSPACE";
+    case TACO_ERR_HIP: return "TACO_ERR_HIP";
+    default: return "TACO_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

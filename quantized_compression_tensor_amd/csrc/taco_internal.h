@@ -1,0 +1,104 @@
+// Host-side interface between the C ABI (taco_abi.hip) and the kernel files.
+// Argument structs carry plain device pointers and sizes that the ABI layer
+// has already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace taco {
+
+enum Format : int { kFP8 = 1, kINT8S = 2, kINT4A = 3, kINT8A = 4 };
+
+// Range of the per-tensor scale g (FP8 dual-scale): both g * 2^-k and
+// (1/g) * 2^k stay normal float32 numbers for every block exponent k in
+// [-64, 63], so the combined per-block scales are exact.
+constexpr float kGMin = 0x1p-60f;
+constexpr float kGMax = 0x1p60f;
+
+// FP8 dual-scale with the Hadamard transform, bf16 input.
+struct FP8HadArgs {
+  const void* x;        // bf16 [nblocks << logb]
+  uint8_t* codes;
+  int8_t* kexp;
+  float* g_hdr;
+  int64_t nblocks;
+  int logb;
+  float g;              // used when !g_from_ws
+  bool g_from_ws;       // tensor scale from the workspace's recorded abs-max
+  bool auto_prepass;    // run the abs-max pass first (data-driven g of this tensor)
+  void* ws;             // Workspace* or null
+  float* dbg;           // pre-rounding values or null
+};
+
+struct FP8HadDecodeArgs {
+  const uint8_t* codes;
+  const int8_t* kexp;
+  const float* g_hdr;
+  int64_t nblocks;
+  int logb;
+  bool bf16_out;
+  void* out;
+};
+
+// Quantization without a transform (INT8 symmetric, asymmetric INT4/INT8,
+// and FP8 dual-scale with hadamard off or on already-transformed float32).
+struct QuantArgs {
+  int fmt;
+  int block;
+  bool f32_in;          // input float32 (else bf16)
+  const void* x;
+  int64_t n;            // elements, a multiple of block
+  uint8_t* codes;
+  void* scale;          // FP8: int8 k; others: float s
+  uint8_t* zero;        // asymmetric only
+  float* g_hdr;         // FP8 only
+  float g;
+  bool g_from_ws;
+  bool auto_prepass;
+  void* ws;
+  float* dbg;
+};
+
+struct DequantArgs {
+  int fmt;
+  int block;
+  const uint8_t* codes;
+  const void* scale;
+  const uint8_t* zero;
+  const float* g_hdr;
+  int64_t n;
+  bool bf16_out;
+  void* out;
+};
+
+constexpr int kMaxShards = 16;
+
+struct ShardPtrs {
+  const uint8_t* codes[kMaxShards];
+  const void* scale[kMaxShards];
+  const uint8_t* zero[kMaxShards];
+  const float* g[kMaxShards];
+};
+
+struct ReduceArgs {
+  int fin, fout;
+  int bin, bout;        // block sizes
+  int nshards;
+  int64_t n;
+  ShardPtrs in;
+  float* sum;           // nullable
+  uint8_t* rq_codes;    // nullable (no requantization)
+  void* rq_scale;
+  uint8_t* rq_zero;
+  float* rq_g_hdr;
+};
+
+hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s);
+hipError_t launch_fp8_had_decode(const FP8HadDecodeArgs& a, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s);
+
+}  // namespace taco

@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: run the C ABI through the binding and turn
+its output buffers into the oracle's representation for comparison."""
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import codecs as cd
+import quantized_compression_tensor_amd as T
+
+DEV = "cuda"
+
+
+def ccodec(oc: cd.Codec):
+    return T.codec(oc.format, oc.block, 1 if oc.hadamard else 0)
+
+
+def upload_bits(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+
+
+def upload_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def new_workspace():
+    return torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=DEV)
+
+
+def gpu_compress(oc, bits, scale=1.0, ws=None, debug=False, xdev=None):
+    """Compress with the GPU; scale is the tensor_scale argument (FP8)."""
+    rows, cols = bits.shape
+    c = ccodec(oc)
+    x = upload_bits(bits) if xdev is None else xdev
+    buf = T.empty_compressed(c, rows, cols)
+    pre = None
+    if debug:
+        pre = torch.empty(max(1, rows * cols), dtype=torch.float32, device=DEV)
+        T.taco_compress_debug(c, x, rows, cols, scale, buf, pre, workspace=ws)
+    else:
+        T.taco_compress(c, x, rows, cols, scale, buf, workspace=ws)
+    torch.cuda.synchronize()
+    return buf, pre
+
+
+def parse(buf, oc, rows, cols):
+    """GPU buffer -> dict(codes, scale, zero, g) as numpy arrays."""
+    codes, sc, aux, ten = T.regions(buf, ccodec(oc), rows, cols)
+    out = dict(codes=codes.cpu().numpy(), scale=sc.cpu().numpy(),
+               zero=aux.cpu().numpy() if aux.numel() else None,
+               g=np.float32(ten.cpu().numpy()[0]) if ten.numel() else None)
+    return out
+
+
+def assert_same(gpu, ref: oracle.Compressed, where=""):
+    """Codes and every scale bit-exact. NaN codes compare as a class."""
+    gc, rc = gpu["codes"], ref.codes
+    assert gc.shape == rc.shape, where
+    bad = gc != rc
+    if ref.codec.format == cd.FP8_DUAL:
+        bad &= ~(((gc & 0x7F) == 0x7F) & ((rc & 0x7F) == 0x7F))
+    nbad = int(bad.sum())
+    assert nbad == 0, f"{where}: {nbad} of {gc.size} codes differ; first at {np.flatnonzero(bad)[:8]}"
+    if ref.codec.format == cd.FP8_DUAL:
+        assert (gpu["scale"].astype(np.int8) == ref.scale.astype(np.int8)).all(), f"{where}: block exponents differ"
+        assert gpu["g"].view(np.uint32) == np.float32(ref.tensor_scale).view(np.uint32), \
+            f"{where}: g {gpu['g']!r} vs {ref.tensor_scale!r}"
+    else:
+        s_bad = gpu["scale"].view(np.uint32) != ref.scale.astype(np.float32).view(np.uint32)
+        assert not s_bad.any(), f"{where}: {int(s_bad.sum())} scales differ"
+    if ref.zero is not None:
+        assert (gpu["zero"] == ref.zero).all(), f"{where}: zero points differ"
+
+
+def same_f32_bits(a, b):
+    a = np.ascontiguousarray(a, np.float32).reshape(-1)
+    b = np.ascontiguousarray(b, np.float32).reshape(-1)
+    return (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))

@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every entry point its
+header declares, computes layouts, names status codes, and rejects bad
+arguments before anything is enqueued (none of these calls touches HIP)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_compression_tensor_amd as T
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "taco.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(taco_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(T.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(T.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in [(0, "TACO_OK"), (-1, "TACO_ERR_INVALID_ARG"), (-2, "TACO_ERR_SHAPE"),
+                       (-3, "TACO_ERR_FORMAT"), (-4, "TACO_ERR_ALIGN"), (-5, "TACO_ERR_WORKSPACE"),
+                       (-6, "TACO_ERR_HIP"), (-99, "TACO_ERR_UNKNOWN")]:
+        assert T.taco_status_string(code) == name
+
+
+FP8 = T.codec(T.TACO_FMT_FP8_DUAL, 128, 1)
+I8S = T.codec(T.TACO_FMT_INT8_SYM, 64)
+I4A = T.codec(T.TACO_FMT_INT4_ASYM, 128)
+I8A = T.codec(T.TACO_FMT_INT8_ASYM, 128)
+
+
+def test_layouts_by_hand():
+    L = T.taco_layout(FP8, 4096, 4096).as_dict()
+    n = 4096 * 4096
+    assert L == dict(codes_off=0, codes_bytes=n, scale_off=n, scale_bytes=n // 128,
+                     aux_off=n + n // 128, aux_bytes=0, tensor_off=n + n // 128, tensor_bytes=16,
+                     total_bytes=n + n // 128 + 256)
+    L = T.taco_layout(I4A, 3, 384).as_dict()          # n = 1152: 576 code bytes, 9 groups
+    assert L["codes_bytes"] == 576 and L["scale_off"] == 768 and L["scale_bytes"] == 36
+    assert L["aux_off"] == 1024 and L["aux_bytes"] == 9 and L["tensor_off"] == 1280
+    assert L["tensor_bytes"] == 0 and L["total_bytes"] == 1280
+    L = T.taco_layout(I8S, 1, 64).as_dict()
+    assert L["codes_bytes"] == 64 and L["scale_off"] == 256 and L["scale_bytes"] == 4
+    assert L["total_bytes"] == 512
+    assert T.taco_compressed_bytes(I8A, 0, 128) == 0
+    assert T.taco_workspace_bytes(FP8, 1, 128) == T.TACO_WORKSPACE_BYTES
+    assert T.taco_workspace_bytes(I8S, 1, 64) == 0
+
+
+@pytest.mark.parametrize("c,cols,err", [
+    (T.codec(T.TACO_FMT_FP8_DUAL, 128, 1), 100, T.TACO_ERR_SHAPE),
+    (T.codec(T.TACO_FMT_FP8_DUAL, 96, 1), 96, T.TACO_ERR_SHAPE),
+    (T.codec(T.TACO_FMT_FP8_DUAL, 128, 2), 128, T.TACO_ERR_FORMAT),
+    (T.codec(T.TACO_FMT_INT8_SYM, 128), 128, T.TACO_ERR_SHAPE),
+    (T.codec(T.TACO_FMT_INT8_SYM, 64, 1), 64, T.TACO_ERR_FORMAT),
+    (T.codec(T.TACO_FMT_INT4_ASYM, 64), 128, T.TACO_ERR_SHAPE),
+    (T.codec(9, 128), 128, T.TACO_ERR_FORMAT),
+    (T.codec(T.TACO_FMT_FP8_DUAL, 128, 1), 0, T.TACO_ERR_INVALID_ARG),
+])
+def test_layout_rejects(c, cols, err):
+    with pytest.raises(T.TacoError) as e:
+        T.taco_layout(c, 4, cols)
+    assert e.value.status == err
+    assert T.lib().taco_compressed_bytes(c, 4, cols) == err
+
+
+def _st(fn, *a):
+    try:
+        fn(*a)
+    except T.TacoError as e:
+        return e.status
+    return 0
+
+
+A = 4096          # a fake, 16-byte aligned "device" address: never dereferenced,
+B_ = 1 << 20      # every call below fails validation before any launch
+
+
+def test_compress_validation():
+    comp = T.taco_compress
+    assert _st(comp, FP8, None, 2, 128, 1.0, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 1.0, None) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A + 2, 2, 128, 1.0, B_) == T.TACO_ERR_ALIGN
+    assert _st(comp, FP8, A, 2, 128, 1.0, B_ + 8) == T.TACO_ERR_ALIGN
+    assert _st(comp, FP8, A, -1, 128, 1.0, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 100, 1.0, B_) == T.TACO_ERR_SHAPE
+    assert _st(comp, FP8, A, 2, 128, 0.0, B_) == T.TACO_ERR_WORKSPACE          # auto needs a workspace
+    assert _st(comp, FP8, A, 2, 128, -1.0, B_) == T.TACO_ERR_WORKSPACE         # delayed needs one too
+    assert _st(comp, FP8, A, 2, 128, 0.0, B_, 3 * B_, 16) == T.TACO_ERR_WORKSPACE  # too small
+    assert _st(comp, FP8, A, 2, 128, float("nan"), B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 2.0 ** 61, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 2.0 ** -61, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 1.0, A) == T.TACO_ERR_INVALID_ARG         # output overlaps input
+    assert _st(comp, FP8, A, 0, 128, 1.0, B_) == 0                             # empty: nothing to do
+    assert _st(comp, I8S, A, 2, 96, 1.0, B_) == T.TACO_ERR_SHAPE
+    assert _st(T.taco_compress_debug, FP8, A, 2, 128, 1.0, B_, None) == T.TACO_ERR_INVALID_ARG
+
+
+def test_reduce_validation():
+    red = T.taco_decompress_reduce
+    shards = [A, A + (1 << 16)]
+    assert _st(red, I8S, [], 4, 64, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(red, I8S, [A] * 17, 4, 64, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(red, I8S, shards, 4, 64, None, None, None) == T.TACO_ERR_INVALID_ARG   # no output
+    assert _st(red, I8S, [A, None], 4, 64, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(red, I8S, [A, A + 4], 4, 64, B_) == T.TACO_ERR_ALIGN
+    assert _st(red, I8S, shards, 4, 128, None, I8A, B_) == T.TACO_ERR_FORMAT
+    assert _st(red, I8S, shards, 4, 64, None, I8A, B_) == T.TACO_ERR_SHAPE          # 64 cols: no 128 group
+    assert _st(red, I4A, shards, 4, 128, None, I4A, B_) == T.TACO_ERR_FORMAT
+    assert _st(red, FP8, shards, 4, 128, None, T.codec(T.TACO_FMT_FP8_DUAL, 64, 1), B_) == T.TACO_ERR_FORMAT
+    assert _st(red, FP8, shards, 4, 128, None, T.codec(T.TACO_FMT_FP8_DUAL, 128, 0), B_) == T.TACO_ERR_FORMAT
+    assert _st(red, I8S, shards, 4, 64, A) == T.TACO_ERR_INVALID_ARG               # sum overlaps a shard
+    assert _st(red, I8S, shards, 0, 64, B_) == 0
+
+
+def test_other_entry_points_validation():
+    assert _st(T.taco_decompress, I8S, A, 4, 64, B_, 2) == T.TACO_ERR_INVALID_ARG
+    assert _st(T.taco_decompress, I8S, A, 4, 64, None, 0) == T.TACO_ERR_INVALID_ARG
+    assert _st(T.taco_decompress, I8S, A + 1, 4, 64, B_, 0) == T.TACO_ERR_ALIGN
+    assert _st(T.taco_requantize, I8S, A, 4, 96, 1.0, B_) == T.TACO_ERR_SHAPE
+    assert _st(T.taco_requantize, FP8, A, 4, 128, 0.0, B_) == T.TACO_ERR_WORKSPACE
+    assert _st(T.taco_e4m3_encode, A, None, 16) == T.TACO_ERR_INVALID_ARG
+    assert _st(T.taco_e4m3_encode, A, B_, -1) == T.TACO_ERR_INVALID_ARG
+    assert _st(T.taco_e4m3_encode, A, A + 16, 64) == T.TACO_ERR_INVALID_ARG       # overlap
+    assert _st(T.taco_e4m3_encode, A, B_, 0) == 0

@@ -1,0 +1,316 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the same
+seeded inputs, at sizes the oracle finishes quickly that still span several
+wave tiles and a ragged tail. Codes, block exponents, scales, zero points and
+tensor scales must be bit-exact; float32 sums and decodes too (the GPU performs
+the same float32 operations in the same order)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import codecs as cd
+from oracle import formats as fm
+import quantized_compression_tensor_amd as T
+import workloads as W
+from tests.gpu_util import (DEV, assert_same, ccodec, gpu_compress, new_workspace, parse, same_f32_bits,
+                            upload_bits, upload_f32)
+
+pytestmark = pytest.mark.gpu
+
+FP8_CODECS = [cd.Codec.fp8(b, h) for b in (16, 32, 64, 128) for h in (True, False)]
+INT_CODECS = [cd.Codec.int8_sym(), cd.Codec.int4_asym(), cd.Codec.int8_asym()]
+ALL = FP8_CODECS + INT_CODECS
+SHAPES = [(1, 128), (3, 384), (37, 1024), (5, 2560), (64, 4096)]
+
+
+def cid(c):
+    return f"f{c.format}b{c.block}h{int(c.hadamard)}"
+
+
+def bits_for(shape, seed, body="normal", sigma=0.02):
+    return W.random_bits(shape, seed=seed, sigma=sigma, body=body)
+
+
+# ------------------------------------------------------------ encoder ----
+
+def test_e4m3_encoder_matches_oracle():
+    x = fm.bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    x = x[np.isfinite(x)]
+    parts = []
+    for s in (0, -4, 4, -10, 8):
+        with np.errstate(over="ignore"):
+            y = (x * np.float32(2.0 ** s)).astype(np.float32)
+        parts.append(y[np.abs(y) <= 448])
+    vals = fm.decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    parts += [mids, np.nextafter(mids, np.float32(1e9)), np.nextafter(mids, np.float32(-1e9)), -mids,
+              np.array([0.0, -0.0, 448.0, -448.0, 1e-45, -1e-45], np.float32)]
+    v = np.concatenate(parts).astype(np.float32)
+    n = v.size
+    out = torch.empty(n + 16, dtype=torch.uint8, device=DEV)
+    T.taco_e4m3_encode(upload_f32(v), out, n)
+    torch.cuda.synchronize()
+    got = out[:n].cpu().numpy()
+    want = fm.encode_e4m3(v)
+    bad = got != want
+    assert not bad.any(), list(zip(v[bad][:10], got[bad][:10], want[bad][:10]))
+    assert (out[n:].cpu().numpy() == out[n:].cpu().numpy()).all()
+
+
+def test_e4m3_encoder_nan_is_a_nan_code():
+    v = np.array([np.nan, -np.nan, 1.0, np.nan], np.float32)
+    out = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    T.taco_e4m3_encode(upload_f32(v), out, 4)
+    torch.cuda.synchronize()
+    got = out[:4].cpu().numpy()
+    assert (got[[0, 1, 3]] & 0x7F == 0x7F).all() and got[2] == 0x38
+
+
+# ----------------------------------------------------------- compress ----
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("oc", ALL, ids=cid)
+def test_compress_given_scale(oc, shape):
+    if shape[1] % oc.block:
+        pytest.skip("cols not a multiple of block")
+    body = "t3" if oc.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    bits = bits_for(shape, seed=shape[0] * 7 + oc.block + oc.format, body=body)
+    g = np.float32(0.0123)
+    ref = oracle.compress(oc, bits, tensor_scale=g)
+    buf, _ = gpu_compress(oc, bits, scale=float(g))
+    assert_same(parse(buf, oc, *shape), ref, f"{cid(oc)} {shape}")
+
+
+@pytest.mark.parametrize("oc", FP8_CODECS, ids=cid)
+def test_compress_auto_scale_and_workspace(oc):
+    shape = (37, 1024)
+    bits = bits_for(shape, seed=41 + oc.block)
+    ws = new_workspace()
+    ref = oracle.compress(oc, bits)              # data-driven g
+    buf, _ = gpu_compress(oc, bits, scale=T.TACO_SCALE_AUTO, ws=ws)
+    assert_same(parse(buf, oc, *shape), ref, cid(oc))
+    w = ws.cpu().numpy()
+    y = cd.transform(oc, bits)
+    assert w[0] == 0 and w[1] == 0                        # accumulators reset
+    assert w[2].view(np.float32) == np.max(np.abs(y))      # recorded abs-max
+    assert w[3] == 2                                      # pre-pass and compress both recorded
+
+
+def test_compress_delayed_scale_uses_previous_call():
+    oc = cd.Codec.fp8()
+    shape = (64, 4096)
+    a = bits_for(shape, seed=5)
+    b = bits_for(shape, seed=6, sigma=0.05)
+    ws = new_workspace()
+    buf1, _ = gpu_compress(oc, a, scale=T.TACO_SCALE_DELAYED, ws=ws)
+    assert_same(parse(buf1, oc, *shape), oracle.compress(oc, a, tensor_scale=np.float32(1.0)), "first: g = 1")
+    buf2, _ = gpu_compress(oc, b, scale=T.TACO_SCALE_DELAYED, ws=ws)
+    g_prev = cd.auto_tensor_scale(cd.transform(oc, a))
+    assert_same(parse(buf2, oc, *shape), oracle.compress(oc, b, tensor_scale=g_prev), "second: g from a")
+    assert ws.cpu().numpy()[2].view(np.float32) == np.max(np.abs(cd.transform(oc, b)))
+
+
+@pytest.mark.parametrize("oc", ALL, ids=cid)
+def test_compress_debug_prequant(oc):
+    shape = (5, 2560) if oc.block != 128 or oc.format != cd.INT8_SYM else (5, 2560)
+    bits = bits_for(shape, seed=77 + oc.format, body="t3", sigma=0.05)
+    g = np.float32(0.05)
+    ref = oracle.compress(oc, bits, tensor_scale=g)
+    buf, pre = gpu_compress(oc, bits, scale=float(g), debug=True)
+    assert_same(parse(buf, oc, *shape), ref, cid(oc))
+    p = pre.cpu().numpy()
+    r = ref.prequant.astype(np.float32)
+    # below 2^-126 the oracle scales with a rounding ldexp, the GPU with one
+    # multiply; both encode to the same (zero) code, compare the rest bit for bit
+    live = np.abs(r) >= 2.0 ** -126
+    assert same_f32_bits(p[live], r[live]).all()
+
+
+def test_compress_is_deterministic():
+    oc = cd.Codec.fp8()
+    bits = bits_for((64, 4096), seed=9)
+    x = upload_bits(bits)
+    b1, _ = gpu_compress(oc, bits, scale=0.01, xdev=x)
+    b2, _ = gpu_compress(oc, bits, scale=0.01, xdev=x)
+    assert torch.equal(b1, b2)
+
+
+def test_compress_edge_values():
+    """All-zero blocks, tiny blocks, single-signed groups, subnormal inputs,
+    negative zeros, and a stale g that forces the exponent clamp (saturation)."""
+    rows, cols = 8, 1024
+    x = np.zeros((rows, cols), np.float32)
+    x[1, :] = -0.0
+    x[2, :128] = 1e-35
+    x[3, :] = np.abs(np.linspace(0.1, 2, cols))
+    x[4, :] = -np.abs(np.linspace(0.1, 2, cols))
+    x[5, :] = 1e-39 * np.arange(cols)
+    x[6, ::3] = 65504.0
+    x[7, :] = np.linspace(-3e4, 3e4, cols)
+    bits = W.f32_to_bf16_rne(x)
+    for oc in ALL:
+        for g in (1.0, 2.0 ** -60, 2.0 ** 60):
+            ref = oracle.compress(oc, bits, tensor_scale=np.float32(g))
+            buf, _ = gpu_compress(oc, bits, scale=g)
+            assert_same(parse(buf, oc, rows, cols), ref, f"{cid(oc)} g={g}")
+
+
+def test_compress_nonfinite_block_does_not_spill():
+    oc = cd.Codec.fp8()
+    x = W.random_bits((4, 1024), seed=3)
+    xf = fm.bf16_bits_to_f32(x)
+    xf[1, 130] = np.nan
+    xf[2, 900] = np.inf
+    bits = W.f32_to_bf16_rne(xf)
+    ref = oracle.compress(oc, bits, tensor_scale=np.float32(0.01))
+    buf, _ = gpu_compress(oc, bits, scale=0.01)
+    got = parse(buf, oc, 4, 1024)
+    finite_blocks = np.isfinite(xf.reshape(-1, 128)).all(axis=1)
+    gc = got["codes"].reshape(-1, 128)[finite_blocks]
+    rc = ref.codes.reshape(-1, 128)[finite_blocks]
+    assert (gc == rc).all()
+    assert (got["scale"][finite_blocks] == ref.scale[finite_blocks]).all()
+
+
+def test_empty_tensor_is_a_no_op():
+    oc = cd.Codec.fp8()
+    c = ccodec(oc)
+    x = torch.zeros(16, dtype=torch.int16, device=DEV)
+    out = torch.full((64,), 7, dtype=torch.uint8, device=DEV)
+    T.taco_compress(c, x, 0, 128, 1.0, out)
+    T.taco_decompress(c, out, 0, 128, x, 0)
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 7).all()
+
+
+# ------------------------------------------------------------- reduce ----
+
+PAIRS = [(cd.Codec.fp8(), cd.Codec.fp8()), (cd.Codec.fp8(64, True), cd.Codec.fp8(64, True)),
+         (cd.Codec.fp8(32, False), cd.Codec.fp8(32, False)),
+         (cd.Codec.int8_sym(), cd.Codec.int8_sym()), (cd.Codec.int4_asym(), cd.Codec.int8_asym()),
+         (cd.Codec.int8_asym(), cd.Codec.int8_asym())]
+
+
+def pid(p):
+    return f"{cid(p[0])}-{cid(p[1])}"
+
+
+@pytest.mark.parametrize("nshards", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("pair", PAIRS, ids=pid)
+def test_decompress_reduce(pair, nshards):
+    cin, cout = pair
+    rows, cols = 13, 1280
+    body = "t3" if cin.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    refs, bufs = [], []
+    for r in range(nshards):
+        bits = bits_for((rows, cols), seed=1000 + 17 * r + nshards, body=body, sigma=0.02 * (1 + r % 3))
+        g = np.float32(0.004 * (1 + r))
+        refs.append(oracle.compress(cin, bits, tensor_scale=g))
+        buf, _ = gpu_compress(cin, bits, scale=float(g))
+        assert_same(parse(buf, cin, rows, cols), refs[-1], f"shard {r}")
+        bufs.append(buf)
+    acc, rq = oracle.decompress_reduce(refs, cout)
+    s = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+    out = T.empty_compressed(ccodec(cout), rows, cols)
+    T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, s, ccodec(cout), out)
+    torch.cuda.synchronize()
+    assert same_f32_bits(s.cpu().numpy(), acc).all()
+    assert_same(parse(out, cout, rows, cols), rq, "requantized")
+    # sum only, and requantize only
+    s2 = torch.zeros_like(s)
+    T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, s2)
+    out2 = T.empty_compressed(ccodec(cout), rows, cols)
+    T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, None, ccodec(cout), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s2)
+    assert torch.equal(out, out2)
+
+
+def test_reduce_with_zero_shards_and_repeats():
+    cin = cout = cd.Codec.int8_sym()
+    rows, cols = 9, 640
+    a = bits_for((rows, cols), seed=1, sigma=1.0)
+    z = np.zeros((rows, cols), np.uint16)
+    ba, _ = gpu_compress(cin, a)
+    bz, _ = gpu_compress(cin, z)
+    ra, rz = oracle.compress(cin, a), oracle.compress(cin, z)
+    acc, rq = oracle.decompress_reduce([ra, rz, ra, rz, ra], cout)
+    s = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+    out = T.empty_compressed(ccodec(cout), rows, cols)
+    T.taco_decompress_reduce(ccodec(cin), [ba, bz, ba, bz, ba], rows, cols, s, ccodec(cout), out)
+    torch.cuda.synchronize()
+    assert same_f32_bits(s.cpu().numpy(), acc).all()
+    assert_same(parse(out, cout, rows, cols), rq)
+
+
+# ------------------------------------------------------------- decode ----
+
+@pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
+@pytest.mark.parametrize("oc", ALL, ids=cid)
+def test_decompress(oc, out_dtype):
+    rows, cols = 21, 1280
+    body = "t3" if oc.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    bits = bits_for((rows, cols), seed=321 + oc.block, body=body)
+    ref = oracle.compress(oc, bits, tensor_scale=np.float32(0.02))
+    buf, _ = gpu_compress(oc, bits, scale=0.02)
+    want = oracle.decode(ref, "bf16" if out_dtype else "f32")
+    out = torch.empty(rows * cols, dtype=torch.int16 if out_dtype else torch.float32, device=DEV)
+    T.taco_decompress(ccodec(oc), buf, rows, cols, out, out_dtype)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if out_dtype:
+        assert (got.view(np.uint16) == want.reshape(-1)).all()
+    else:
+        assert same_f32_bits(got, want).all()
+
+
+# ---------------------------------------------------------- requantize ---
+
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(128, True), cd.Codec.fp8(16, False)] + INT_CODECS, ids=cid)
+def test_requantize(oc):
+    rows, cols = 11, 2048
+    rng = np.random.default_rng(oc.format + oc.block)
+    x = (rng.standard_t(3, size=(rows, cols)) * 0.3).astype(np.float32)
+    x[0, :200] = 0.0
+    xd = upload_f32(x)
+    c = ccodec(oc)
+    out = T.empty_compressed(c, rows, cols)
+    T.taco_requantize(c, xd, rows, cols, 0.125, out)
+    torch.cuda.synchronize()
+    assert_same(parse(out, oc, rows, cols), oracle.requantize(oc, x, tensor_scale=np.float32(0.125)))
+    if oc.format == cd.FP8_DUAL:
+        ws = new_workspace()
+        out2 = T.empty_compressed(c, rows, cols)
+        T.taco_requantize(c, xd, rows, cols, T.TACO_SCALE_AUTO, out2, workspace=ws)
+        torch.cuda.synchronize()
+        assert_same(parse(out2, oc, rows, cols), oracle.requantize(oc, x))
+
+
+# ------------------------------------------------ the small bench workload --
+
+def test_taco_tiny_workload_end_to_end():
+    """The 2048 x 1024 FP8 workload: 2 shards, data-driven g, FP32 sum, decode."""
+    w = W.WORKLOADS["taco-tiny"]
+    oc = cd.Codec.fp8(w.in_block, w.hadamard)
+    refs, bufs = [], []
+    for r in range(w.shards):
+        bits = W.make_shard(w, r)
+        ws = new_workspace()
+        refs.append(oracle.compress(oc, bits))
+        buf, _ = gpu_compress(oc, bits, scale=T.TACO_SCALE_AUTO, ws=ws)
+        assert_same(parse(buf, oc, w.rows, w.cols), refs[-1], f"shard {r}")
+        bufs.append(buf)
+    acc, _ = oracle.decompress_reduce(refs)
+    s = torch.empty(w.n, dtype=torch.float32, device=DEV)
+    T.taco_decompress_reduce(ccodec(oc), bufs, w.rows, w.cols, s)
+    torch.cuda.synchronize()
+    assert same_f32_bits(s.cpu().numpy(), acc).all()
+    # quality is the oracle's, exactly
+    x0 = fm.bf16_bits_to_f32(W.make_shard(w, 0))
+    d = torch.empty(w.n, dtype=torch.float32, device=DEV)
+    T.taco_decompress(ccodec(oc), bufs[0], w.rows, w.cols, d, 0)
+    torch.cuda.synchronize()
+    r_gpu = oracle.rel_mse(d.cpu().numpy(), x0.reshape(-1))
+    r_ref = oracle.rel_mse(oracle.decode(refs[0]).reshape(-1), x0.reshape(-1))
+    assert abs(r_gpu - r_ref) <= 0.01 * r_ref
