@@ -35,9 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt-tp")
-    ap.add_argument("--scale-mode", choices=["delayed", "auto"], default="delayed",
-                    help="FP8 tensor scale: delayed (abs-max of the previous step, one pass) "
-                         "or auto (abs-max pre-pass of this tensor)")
+    ap.add_argument("--scale-mode", choices=["delayed", "auto", "given"], default="delayed",
+                    help="FP8 tensor scale: delayed (abs-max of the previous step, one pass), "
+                         "auto (abs-max pre-pass of this tensor) or given (a fixed g, no workspace)")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -185,7 +185,9 @@ def main():
     c_in = T.codec(w.in_format, w.in_block, 1 if w.hadamard else 0)
     c_out = T.codec(w.out_format, w.out_block, 1 if w.hadamard else 0) if w.out_format else None
     fp8 = w.in_format == T.TACO_FMT_FP8_DUAL
-    scale = (T.TACO_SCALE_DELAYED if args.scale_mode == "delayed" else T.TACO_SCALE_AUTO) if fp8 else 1.0
+    scale = {"delayed": T.TACO_SCALE_DELAYED, "auto": T.TACO_SCALE_AUTO, "given": 0.01}[args.scale_mode] \
+        if fp8 else 1.0
+    use_ws = fp8 and args.scale_mode != "given"
 
     in_bytes = w.shards * w.n * 2
     nsets = max(2, min(4, -(-2 * MALL_BYTES // in_bytes) + 1))
@@ -205,7 +207,7 @@ def main():
     def compress(s):
         for r in range(w.shards):
             T.taco_compress(c_in, xs[s][r], w.rows, w.cols, scale, bufs[s][r],
-                            workspace=wss[r] if fp8 else None)
+                            workspace=wss[r] if use_ws else None)
 
     def reduce(s):
         if c_out is not None:

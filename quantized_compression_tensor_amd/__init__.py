@@ -68,6 +68,10 @@ class TacoError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime (same soname as /opt/rocm's). Loading it
+    # first makes libtaco.so bind to that one runtime; loading libtaco.so first
+    # would map a second runtime that does not know torch's streams or memory.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         from . import build as _build
         _build.build()

@@ -159,14 +159,25 @@ TACO_DEV float ws_load_amax_last(Workspace* ws) {
 // Fold one workgroup's non-negative max into the workspace; the last
 // workgroup to arrive publishes the tensor max and resets the accumulators.
 // Must be called by every workgroup of the grid, by thread 0 only.
+//
+// Ordering without fences: device-scope read-modify-writes are performed at
+// the device's coherence point and each one here waits for its returned value
+// before the next is issued (s_waitcnt vmcnt(0)). A workgroup's max is
+// therefore performed before its arrival is counted, and the workgroup that
+// counts last performs its exchange after every max. Release/acquire fences
+// would instead write back and invalidate the L2 of the issuing XCD once per
+// workgroup.
 TACO_DEV void ws_publish_amax(Workspace* ws, float wg_max, uint32_t num_groups) {
   __hip_atomic_fetch_max(&ws->amax_acc, __float_as_uint(wg_max), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t prev = __hip_atomic_fetch_add(&ws->arrivals, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t prev = __hip_atomic_fetch_add(&ws->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (prev == num_groups - 1) {
-    uint32_t a = __hip_atomic_exchange(&ws->amax_acc, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t a = __hip_atomic_exchange(&ws->amax_acc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __hip_atomic_store(&ws->amax_last, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&ws->calls, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws->arrivals, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -81,6 +81,10 @@ int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, int* mo
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
 
+// A launch is judged by hipGetLastError afterwards, so drop any error an
+// earlier, unrelated runtime call on this thread left behind.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 struct Regions {
   uint8_t* codes;
   void* scale;
@@ -117,6 +121,7 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
     a.nblocks = n / c.block; a.logb = log2_block(c.block);
     a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
     a.ws = ws; a.dbg = dbg;
+    clear_stale_error();
     return hip_status(launch_fp8_had_compress(a, stream));
   }
   QuantArgs a;
@@ -124,6 +129,7 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
   a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
   a.ws = c.format == TACO_FMT_FP8_DUAL ? ws : nullptr; a.dbg = dbg;
+  clear_stale_error();
   return hip_status(launch_quantize(a, stream));
 }
 
@@ -217,7 +223,8 @@ int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n
     Regions O = regions_of(requant_out, Lo);
     a.rq_codes = O.codes; a.rq_scale = O.scale; a.rq_zero = O.aux; a.rq_g_hdr = O.tensor;
   }
-  return hip_status(launch_reduce(a, stream));
+  clear_stale_error();
+    return hip_status(launch_reduce(a, stream));
 }
 
 int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
@@ -237,12 +244,14 @@ int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, vo
     FP8HadDecodeArgs a;
     a.codes = R.codes; a.kexp = static_cast<const int8_t*>(R.scale); a.g_hdr = R.tensor;
     a.nblocks = n / c.block; a.logb = log2_block(c.block); a.bf16_out = out_dtype == 1; a.out = out;
+    clear_stale_error();
     return hip_status(launch_fp8_had_decode(a, stream));
   }
   DequantArgs a;
   a.fmt = c.format; a.block = c.block; a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
   a.n = n; a.bf16_out = out_dtype == 1; a.out = out;
-  return hip_status(launch_dequantize(a, stream));
+  clear_stale_error();
+    return hip_status(launch_dequantize(a, stream));
 }
 
 int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
@@ -251,7 +260,8 @@ int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stre
   if (x == nullptr || codes == nullptr) return TACO_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes)) return TACO_ERR_ALIGN;
   if (overlaps(x, 4 * n, codes, n)) return TACO_ERR_INVALID_ARG;
-  return hip_status(launch_e4m3_encode(x, codes, n, stream));
+  clear_stale_error();
+    return hip_status(launch_e4m3_encode(x, codes, n, stream));
 }
 
 const char* taco_status_string(int status) {

@@ -137,3 +137,15 @@ def test_other_entry_points_validation():
     assert _st(T.taco_e4m3_encode, A, B_, -1) == T.TACO_ERR_INVALID_ARG
     assert _st(T.taco_e4m3_encode, A, A + 16, 64) == T.TACO_ERR_INVALID_ARG       # overlap
     assert _st(T.taco_e4m3_encode, A, B_, 0) == 0
+
+
+def test_one_hip_runtime_in_the_process():
+    """The binding must leave exactly one HIP runtime mapped (torch's), whatever
+    was imported first: a second runtime cannot use torch's streams or memory."""
+    import subprocess
+    import sys
+    code = ("import quantized_compression_tensor_amd, torch\n"
+            "m = open('/proc/self/maps').read()\n"
+            "print(len(set(l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l)))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.stdout.strip() == "1", out.stdout + out.stderr

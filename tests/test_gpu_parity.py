@@ -13,8 +13,8 @@ from oracle import codecs as cd
 from oracle import formats as fm
 import quantized_compression_tensor_amd as T
 import workloads as W
-from tests.gpu_util import (DEV, assert_same, ccodec, gpu_compress, new_workspace, parse, same_f32_bits,
-                            upload_bits, upload_f32)
+from tests.gpu_util import (DEV, assert_same, ccodec, gpu_compress, new_workspace, parse, same_buffers,
+                            same_f32_bits, upload_bits, upload_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,6 @@ def test_e4m3_encoder_matches_oracle():
     want = fm.encode_e4m3(v)
     bad = got != want
     assert not bad.any(), list(zip(v[bad][:10], got[bad][:10], want[bad][:10]))
-    assert (out[n:].cpu().numpy() == out[n:].cpu().numpy()).all()
 
 
 def test_e4m3_encoder_nan_is_a_nan_code():
@@ -133,7 +132,7 @@ def test_compress_is_deterministic():
     x = upload_bits(bits)
     b1, _ = gpu_compress(oc, bits, scale=0.01, xdev=x)
     b2, _ = gpu_compress(oc, bits, scale=0.01, xdev=x)
-    assert torch.equal(b1, b2)
+    assert same_buffers(b1, b2, oc, 64, 4096)
 
 
 def test_compress_edge_values():
@@ -224,7 +223,7 @@ def test_decompress_reduce(pair, nshards):
     T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, None, ccodec(cout), out2)
     torch.cuda.synchronize()
     assert torch.equal(s, s2)
-    assert torch.equal(out, out2)
+    assert same_buffers(out, out2, cout, rows, cols)
 
 
 def test_reduce_with_zero_shards_and_repeats():
