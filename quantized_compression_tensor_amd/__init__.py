@@ -30,7 +30,7 @@ TACO_FMT_INT8_ASYM = 4
 TACO_SCALE_AUTO = 0.0
 TACO_SCALE_DELAYED = -1.0
 TACO_MAX_SHARDS = 16
-TACO_WORKSPACE_BYTES = 256
+TACO_WORKSPACE_BYTES = 8192
 
 # Entry points declared in include/taco.h (checked by the ABI tests).
 EXPORTS = (

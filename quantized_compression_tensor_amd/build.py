@@ -52,7 +52,7 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False, extra_flags=()):
+def build(verbose=False, extra_flags=(), out=None):
     cc = hipcc()
     os.makedirs(LIBDIR, exist_ok=True)
     with tempfile.TemporaryDirectory(dir=LIBDIR) as tmp:
@@ -64,10 +64,10 @@ def build(verbose=False, extra_flags=()):
             objs = list(ex.map(compile_one, SOURCES))
         tmp_lib = os.path.join(tmp, "libtaco.so")
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, out or LIB)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out or LIB)
+    return out or LIB
 
 
 if __name__ == "__main__":

@@ -372,54 +372,113 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
 
 // Decompress N shards, sum in float32 in shard order, then optionally store
 // the sum and/or re-quantize it (FP8: g' = g_0 + ... + g_{N-1}, clamped).
-template <int FIN, int BIN, int FOUT, int BOUT>
+//
+// Persistent grid over 1024-element wave tiles. All NMAX shard slots are read
+// through buffer resources; slots r >= N get an empty resource, load zeros and
+// add an exact +0 (acc is never -0), so the instruction stream is the same for
+// every N <= NMAX and the compiler can wait for exactly the loads it needs.
+// A launch covers at most kReducePiece elements (the host splits larger
+// tensors), so every byte offset fits 32 bits.
+template <int FMT, int B>
+struct ShardRsrc {
+  rsrc_t codes, scale, zero, g;
+};
+
+template <int FMT, int B>
+TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int64_t n) {
+  const bool live = r < a.nshards;
+  const int64_t nb = n / B;
+  ShardRsrc<FMT, B> s;
+  s.codes = make_rsrc(a.in.codes[r], live ? (FMT == kINT4A ? n / 2 : n) : 0);
+  s.scale = make_rsrc(a.in.scale[r], live ? (FMT == kFP8 ? nb : 4 * nb) : 0);
+  s.zero = make_rsrc(a.in.zero[r], live && (FMT == kINT4A || FMT == kINT8A) ? nb : 0);
+  s.g = make_rsrc(a.in.g[r], live && FMT == kFP8 ? 4 : 0);
+  return s;
+}
+
+template <int FMT, int B>
+TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0) {
+  LaneIn<FMT, B> r;
+  const int blk = e0 / B;
+  if constexpr (FMT == kINT4A) {
+    uint2 w = bload64<kNT>(s.codes, e0 / 2, 0);
+    r.q = make_uint4(w.x, w.y, 0, 0);
+  } else {
+    r.q = bload128<kNT>(s.codes, e0, 0);
+  }
+  if constexpr (FMT == kFP8) {
+    const int k = (int)(int8_t)bload8(s.scale, blk, 0);
+    r.s = __uint_as_float(bload32(s.g, 0, 0)) * pow2f(-k);
+    r.zf = 0.0f;
+  } else {
+    r.s = __uint_as_float(bload32(s.scale, blk * 4, 0));
+    r.zf = (FMT == kINT8S) ? 0.0f : (float)bload8(s.zero, blk, 0);
+  }
+  return r;
+}
+
+template <int FIN, int BIN, int FOUT, int BOUT, int NMAX>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t tile = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
-  const bool valid = e0 < a.n;
-  float acc[16];
+  const int64_t n = a.n;
+  const int ntiles = (int)((n + kWaveElems - 1) / kWaveElems);
+  const int stride = (int)gridDim.x * (kBlockThreads / kWave);
+  const bool rq = a.rq_codes != nullptr;
+  float inv_g = 0.0f;
+  if constexpr (FOUT == kFP8) {
+    if (rq) {
+      float gs = 0.0f;
+      for (int r = 0; r < a.nshards; ++r) gs = gs + *a.in.g[r];
+      gs = fminf(fmaxf(gs, kGMin), kGMax);
+      inv_g = 1.0f / gs;
+      if (blockIdx.x == 0 && threadIdx.x == 0 && a.write_g) *a.rq_g_hdr = gs;
+    }
+  }
+  const int64_t nb_out = n / BOUT;
+  const rsrc_t r_sum = make_rsrc(a.sum, a.sum ? 4 * n : 0);
+  const rsrc_t r_qc = make_rsrc(a.rq_codes, rq ? n : 0);
+  const rsrc_t r_qs = make_rsrc(a.rq_scale, rq ? (FOUT == kFP8 ? nb_out : 4 * nb_out) : 0);
+  const rsrc_t r_qz = make_rsrc(a.rq_zero, rq && FOUT == kINT8A ? nb_out : 0);
+
+  for (int t = (int)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
+    const int e0 = t * kWaveElems + lane * kLaneElems;
+    float acc[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  if (valid) {
-    int r = 0;
-    for (; r + 4 <= a.nshards; r += 4) {
-      LaneIn<FIN, BIN> in[4];
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    constexpr int GRP = NMAX < 8 ? NMAX : 8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        in[u] = load_in<FIN, BIN>(a.in.codes[r + u], a.in.scale[r + u], a.in.zero[r + u], a.in.g[r + u], e0);
+    for (int r0 = 0; r0 < NMAX; r0 += GRP) {
+      LaneIn<FIN, BIN> in[GRP];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < GRP; ++u) in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r0 + u, n), e0);
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
         float d[16];
         dequant_lane<FIN, BIN>(in[u], d);
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
       }
     }
-    for (; r < a.nshards; ++r) {
-      LaneIn<FIN, BIN> in = load_in<FIN, BIN>(a.in.codes[r], a.in.scale[r], a.in.zero[r], a.in.g[r], e0);
-      float d[16];
-      dequant_lane<FIN, BIN>(in, d);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
-    }
     if (a.sum != nullptr) {
-      float4* o = reinterpret_cast<float4*>(a.sum + e0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      for (int q = 0; q < 4; ++q)
+        bstore128(make_uint4(__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
+                             __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3])),
+                  r_sum, e0 * 4 + 16 * q, 0);
     }
-  }
-  if (a.rq_codes != nullptr) {
-    float inv_g = 0.0f;
-    if constexpr (FOUT == kFP8) {
-      float gs = 0.0f;
-      for (int r = 0; r < a.nshards; ++r) gs = gs + *a.in.g[r];
-      gs = fminf(fmaxf(gs, kGMin), kGMax);
-      inv_g = 1.0f / gs;
-      if (blockIdx.x == 0 && threadIdx.x == 0) *a.rq_g_hdr = gs;
+    if (rq) {
+      // lanes beyond the tensor quantize zeros; their stores fall outside the
+      // resources and are dropped
+      LaneCodes q = quant_lane<FOUT, BOUT>(acc, inv_g, nullptr);
+      const int blk = e0 / BOUT;
+      bstore128(q.q, r_qc, e0, 0);
+      if constexpr (FOUT == kFP8) {
+        bstore8((uint32_t)q.k, r_qs, blk, 0);
+      } else {
+        bstore32(__float_as_uint(q.s), r_qs, blk * 4, 0);
+        if constexpr (FOUT == kINT8A) bstore8((uint32_t)q.z, r_qz, blk, 0);
+      }
     }
-    LaneCodes rq = quant_lane<FOUT, BOUT>(acc, inv_g, nullptr);
-    if (valid) store_lane<FOUT, BOUT>(rq, e0, a.rq_codes, a.rq_scale, a.rq_zero);
   }
 }
 
@@ -502,32 +561,70 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FIN, int BIN, int FOUT, int BOUT>
+template <int FIN, int BIN, int FOUT, int BOUT, int NMAX>
 static void launch_r(const ReduceArgs& a, hipStream_t s) {
   dim3 grid = grid_for(a.n), block(kBlockThreads);
-  hipLaunchKernelGGL((k_reduce<FIN, BIN, FOUT, BOUT>), grid, block, 0, s, a);
+  const unsigned cap = (unsigned)(device_cu_count() * kReduceGroupsPerCU);
+  if (kReduceGroupsPerCU > 0 && grid.x > cap) grid.x = cap;
+  hipLaunchKernelGGL((k_reduce<FIN, BIN, FOUT, BOUT, NMAX>), grid, block, 0, s, a);
 }
 
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
+template <int FIN, int BIN, int FOUT, int BOUT>
+static void launch_rn(const ReduceArgs& a, hipStream_t s) {
+  if (a.nshards <= 2) launch_r<FIN, BIN, FOUT, BOUT, 2>(a, s);
+  else if (a.nshards <= 4) launch_r<FIN, BIN, FOUT, BOUT, 4>(a, s);
+  else if (a.nshards <= 8) launch_r<FIN, BIN, FOUT, BOUT, 8>(a, s);
+  else launch_r<FIN, BIN, FOUT, BOUT, 16>(a, s);
+}
+
+static hipError_t launch_reduce_piece(const ReduceArgs& a, hipStream_t s) {
   if (a.fin == kFP8) {
     switch (a.bin) {
-      case 16: launch_r<kFP8, 16, kFP8, 16>(a, s); break;
-      case 32: launch_r<kFP8, 32, kFP8, 32>(a, s); break;
-      case 64: launch_r<kFP8, 64, kFP8, 64>(a, s); break;
-      case 128: launch_r<kFP8, 128, kFP8, 128>(a, s); break;
+      case 16: launch_rn<kFP8, 16, kFP8, 16>(a, s); break;
+      case 32: launch_rn<kFP8, 32, kFP8, 32>(a, s); break;
+      case 64: launch_rn<kFP8, 64, kFP8, 64>(a, s); break;
+      case 128: launch_rn<kFP8, 128, kFP8, 128>(a, s); break;
       default: return hipErrorInvalidValue;
     }
   } else if (a.fin == kINT8S) {
-    launch_r<kINT8S, 64, kINT8S, 64>(a, s);
+    launch_rn<kINT8S, 64, kINT8S, 64>(a, s);
   } else if (a.fin == kINT4A) {
-    launch_r<kINT4A, 128, kINT8A, 128>(a, s);
+    launch_rn<kINT4A, 128, kINT8A, 128>(a, s);
   } else if (a.fin == kINT8A) {
-    launch_r<kINT8A, 128, kINT8A, 128>(a, s);
+    launch_rn<kINT8A, 128, kINT8A, 128>(a, s);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+static int64_t code_bytes(int fmt, int64_t elems) { return fmt == kINT4A ? elems / 2 : elems; }
+static int64_t scale_bytes(int fmt, int64_t blocks) { return fmt == kFP8 ? blocks : 4 * blocks; }
+
+// Split the tensor into pieces of at most kReducePiece elements; each piece is
+// one launch over offset pointers (blocks never straddle pieces).
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  for (int64_t e = 0; e < a.n; e += kReducePiece) {
+    ReduceArgs p = a;
+    p.n = (a.n - e < kReducePiece) ? a.n - e : kReducePiece;
+    p.write_g = (e == 0);
+    const int64_t bi = e / a.bin, bo = e / a.bout;
+    for (int r = 0; r < a.nshards; ++r) {
+      p.in.codes[r] = a.in.codes[r] + code_bytes(a.fin, e);
+      p.in.scale[r] = static_cast<const uint8_t*>(a.in.scale[r]) + scale_bytes(a.fin, bi);
+      p.in.zero[r] = a.in.zero[r] + bi;
+    }
+    if (a.sum) p.sum = a.sum + e;
+    if (a.rq_codes) {
+      p.rq_codes = a.rq_codes + e;
+      p.rq_scale = static_cast<uint8_t*>(a.rq_scale) + scale_bytes(a.fout, bo);
+      p.rq_zero = a.rq_zero + bo;
+    }
+    hipError_t err = launch_reduce_piece(p, s);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s) {

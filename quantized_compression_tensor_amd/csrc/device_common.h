@@ -18,6 +18,9 @@ namespace taco {
 constexpr int kWave = 64;
 constexpr int kBlockThreads = 256;
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value.
+TACO_DEV int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) / kWave; }
+
 constexpr float kE4M3Max = 448.0f;
 // Blocks whose abs-max (symmetric) or range (asymmetric) is below this are
 // stored as zero codes with a zero scale, so 127/A and qmax/r stay finite.
@@ -30,6 +33,45 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 TACO_DEV uint4 ld16_nt(const void* p) {
   u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ----------------------------------------------------------- buffer ops --
+// Raw buffer accesses through a 128-bit resource (base, byte size): a load
+// outside [0, size) returns zeros and a store there is dropped, so ragged
+// tails need no branches and every access is issued unconditionally (which
+// also lets the compiler wait for exactly the loads it needs).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;   // gfx9-family raw buffer, 32-bit data format
+constexpr int kNT = 2;                   // non-temporal cache policy (read once)
+
+TACO_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nr = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kRsrcFlags);
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int AUX = 0>
+TACO_DEV uint4 bload128(rsrc_t r, int voff, int soff) {
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int AUX = 0>
+TACO_DEV uint2 bload64(rsrc_t r, int voff, int soff) {
+  u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+  return make_uint2(v.x, v.y);
+}
+TACO_DEV uint32_t bload32(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0); }
+TACO_DEV uint32_t bload8(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0); }
+TACO_DEV void bstore128(uint4 v, rsrc_t r, int voff, int soff) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
+}
+TACO_DEV void bstore64(uint2 v, rsrc_t r, int voff, int soff) {
+  u32x2 w = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+}
+TACO_DEV void bstore32(uint32_t v, rsrc_t r, int voff, int soff) { __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0); }
+TACO_DEV void bstore8(uint32_t v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, voff, soff, 0);
 }
 
 // ------------------------------------------------------------------ bf16 --
@@ -142,43 +184,72 @@ TACO_DEV float wave_max(float a) {
 }
 
 // ------------------------------------------------------------- workspace --
-// Caller-owned, zero-initialised once; every kernel that uses it leaves
-// `arrivals` and `amax_acc` at zero again. `amax_last` holds the abs-max of
+// Caller-owned, zero-filled once; every kernel that uses it leaves all its
+// counters and accumulators at zero again. `amax_last` holds the abs-max of
 // the transformed tensor seen by the most recent call.
+//
+// Workgroups fold their maxima in two levels: into one of kPubGroups group
+// accumulators (each counter and each max on its own 128-byte line, so that
+// atomics to them proceed in parallel), then the last arrival of each group
+// into the top accumulator. A single shared address would serialize one
+// atomic per workgroup.
+constexpr int kPubGroups = 16;
+constexpr int kLineWords = 32;
+
 struct Workspace {
-  uint32_t arrivals;
-  uint32_t amax_acc;    // float bits of a non-negative max
   uint32_t amax_last;   // float bits
   uint32_t calls;
+  uint32_t top_arrivals;
+  uint32_t top_max;
+  uint32_t pad0[kLineWords - 4];
+  uint32_t grp_arrivals[kPubGroups][kLineWords];
+  uint32_t grp_max[kPubGroups][kLineWords];
 };
+static_assert(sizeof(Workspace) <= 8192, "workspace size");
 
 TACO_DEV float ws_load_amax_last(Workspace* ws) {
   return __uint_as_float(__hip_atomic_load(&ws->amax_last, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Fold one workgroup's non-negative max into the workspace; the last
-// workgroup to arrive publishes the tensor max and resets the accumulators.
-// Must be called by every workgroup of the grid, by thread 0 only.
+#define TACO_AT_MAX(p, v) __hip_atomic_fetch_max((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+#define TACO_AT_ADD(p, v) __hip_atomic_fetch_add((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+#define TACO_AT_XCHG(p, v) __hip_atomic_exchange((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+#define TACO_AT_STORE(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+#define TACO_WAIT_MEM() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+
+// Fold this workgroup's non-negative max into the workspace; the last
+// workgroup to arrive publishes the tensor max. Called once per workgroup of
+// the grid, by thread 0.
 //
 // Ordering without fences: device-scope read-modify-writes are performed at
-// the device's coherence point and each one here waits for its returned value
-// before the next is issued (s_waitcnt vmcnt(0)). A workgroup's max is
-// therefore performed before its arrival is counted, and the workgroup that
-// counts last performs its exchange after every max. Release/acquire fences
-// would instead write back and invalidate the L2 of the issuing XCD once per
-// workgroup.
+// the device's coherence point, and each one here waits for its returned
+// value before the next is issued. A workgroup's max is therefore performed
+// before its arrival is counted, and the arrival that completes a count reads
+// the accumulator after every max that count covers. (Release/acquire fences
+// would instead write back and invalidate the issuing XCD's L2 once per
+// workgroup.)
 TACO_DEV void ws_publish_amax(Workspace* ws, float wg_max, uint32_t num_groups) {
-  __hip_atomic_fetch_max(&ws->amax_acc, __float_as_uint(wg_max), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  uint32_t prev = __hip_atomic_fetch_add(&ws->arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (prev == num_groups - 1) {
-    uint32_t a = __hip_atomic_exchange(&ws->amax_acc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __hip_atomic_store(&ws->amax_last, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&ws->calls, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  const uint32_t G = num_groups < (uint32_t)kPubGroups ? num_groups : (uint32_t)kPubGroups;
+  const uint32_t g = blockIdx.x % G;
+  const uint32_t members = (num_groups - g + G - 1) / G;
+  TACO_AT_MAX(&ws->grp_max[g][0], __float_as_uint(wg_max));
+  TACO_WAIT_MEM();
+  const uint32_t prev = TACO_AT_ADD(&ws->grp_arrivals[g][0], 1u);
+  TACO_WAIT_MEM();
+  if (prev != members - 1) return;
+  const uint32_t gm = TACO_AT_XCHG(&ws->grp_max[g][0], 0u);
+  TACO_WAIT_MEM();
+  TACO_AT_STORE(&ws->grp_arrivals[g][0], 0u);
+  TACO_AT_MAX(&ws->top_max, gm);
+  TACO_WAIT_MEM();
+  const uint32_t prev2 = TACO_AT_ADD(&ws->top_arrivals, 1u);
+  TACO_WAIT_MEM();
+  if (prev2 != G - 1) return;
+  const uint32_t a = TACO_AT_XCHG(&ws->top_max, 0u);
+  TACO_WAIT_MEM();
+  TACO_AT_STORE(&ws->amax_last, a);
+  TACO_AT_ADD(&ws->calls, 1u);
+  TACO_AT_STORE(&ws->top_arrivals, 0u);
 }
 
 // Workgroup max of a non-negative float through LDS (all threads call it).

@@ -135,35 +135,41 @@ TACO_DEV void widen8(uint4 w, float* v) {
 // the abs-max the workspace recorded (the pre-pass of this call, or the
 // previous call: delayed scaling); otherwise from the argument. With a
 // workspace the kernel also records this tensor's abs-max for the next call.
-template <int LOGB, bool GFROM_WS, bool DEBUG, int T>
-__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
-    const uint4* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
-    float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
-    float* __restrict__ dbg) {
+//
+// Persistent grid: each wave walks chunks of T consecutive wave tiles
+// (T * 512 elements) with a stride of the whole grid, loading the next chunk
+// while it transforms the current one (two register sets, used alternately).
+// All accesses go through buffer resources rebased per chunk, so the ragged
+// last chunk reads zeros and drops its out-of-range stores.
+#ifndef TACO_CHUNK_TILES
+#define TACO_CHUNK_TILES 4
+#endif
+constexpr int kChunkTiles = TACO_CHUNK_TILES;
+
+template <int LOGB>
+struct HadChunk {
   using Gm = HadGeom<LOGB>;
-  __shared__ float lds4[4];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const LaneSigns<LOGB> ls(lane);
-  const int row = lane / Gm::G;
+  static constexpr int T = kChunkTiles;
+  static constexpr int64_t ELEMS = (int64_t)T * kTileElems;
 
-  float g = GFROM_WS ? tensor_scale_from_amax(ws_load_amax_last(ws)) : g_arg;
-  const float inv_g = 1.0f / g;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
-
-  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
-  uint4 raw[T];
+  static TACO_DEV void load(const uint16_t* x, int64_t c, int64_t elems, int elem_off, uint4* raw) {
+    const rsrc_t r = make_rsrc(x + c * ELEMS, (elems - c * ELEMS) * 2);
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int64_t blk = (tile0 + i) * Gm::BPT + row;
-    raw[i] = make_uint4(0, 0, 0, 0);
-    if (blk < nblocks) raw[i] = ld16_nt(x + ((tile0 + i) * kTileElems + ls.elem_off) / 8);
+    for (int i = 0; i < T; ++i) raw[i] = bload128<kNT>(r, elem_off * 2, i * kTileElems * 2);
   }
+};
 
-  float run_max = 0.0f;
+template <int LOGB, bool DEBUG>
+TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
+                                 float inv_g, uint8_t* codes, int8_t* kexp, float* dbg, float& run_max) {
+  using Gm = HadGeom<LOGB>;
+  constexpr int T = kChunkTiles;
+  constexpr int64_t E = HadChunk<LOGB>::ELEMS;
+  const int64_t rem = elems - c * E;
+  const rsrc_t rc = make_rsrc(codes + c * E, rem);
+  const rsrc_t rk = make_rsrc(kexp + (c * E >> LOGB), rem >> LOGB);
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const int64_t blk = (tile0 + i) * Gm::BPT + row;
     float v[8];
     widen8(raw[i], v);
     fwht_in_lane(v);
@@ -172,26 +178,61 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     run_max = fmaxf(run_max, M);
     const float m = M * inv_g;
     const int k = block_exponent(m);
-    const float c = inv_g * pow2f(k) * ls.parity;
+    const float cs = inv_g * pow2f(k) * ls.parity;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], c, 0.0f);
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], cs, 0.0f);
     if (__builtin_expect(m * pow2f(k) > kE4M3Max, 0)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = sat448(v[e]);
     }
-    if (blk < nblocks) {
-      const int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
-      uint2 q;
-      q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
-      q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
-      *reinterpret_cast<uint2*>(codes + eoff) = q;
-      if ((lane & (Gm::G - 1)) == 0) kexp[blk] = (int8_t)k;
-      if constexpr (DEBUG) {
-        float4* d = reinterpret_cast<float4*>(dbg + eoff);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
-      }
+    uint2 q;
+    q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
+    q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
+    bstore64(q, rc, ls.elem_off, i * kTileElems);
+    // every lane of the block writes the same exponent byte
+    bstore8((uint32_t)k, rk, row, i * Gm::BPT);
+    if constexpr (DEBUG) {
+      const rsrc_t rd = make_rsrc(dbg + c * E, rem * 4);
+      bstore128(make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                           __float_as_uint(v[3])), rd, ls.elem_off * 4, i * kTileElems * 4);
+      bstore128(make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                           __float_as_uint(v[7])), rd, ls.elem_off * 4 + 16, i * kTileElems * 4);
     }
+  }
+}
+
+template <int LOGB, bool GFROM_WS, bool DEBUG>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
+    float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
+    float* __restrict__ dbg) {
+  using Gm = HadGeom<LOGB>;
+  using CH = HadChunk<LOGB>;
+  __shared__ float lds4[4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const LaneSigns<LOGB> ls(lane);
+  const int row = lane / Gm::G;
+
+  const float g = GFROM_WS ? tensor_scale_from_amax(ws_load_amax_last(ws)) : g_arg;
+  const float inv_g = 1.0f / g;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
+
+  const int64_t elems = nblocks << LOGB;
+  const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
+
+  float run_max = 0.0f;
+  uint4 ra[CH::T], rb[CH::T];
+  CH::load(x, c, elems, ls.elem_off, ra);
+  while (c < nchunks) {
+    CH::load(x, c + stride, elems, ls.elem_off, rb);
+    had_compress_chunk<LOGB, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+    c += stride;
+    if (c >= nchunks) break;
+    CH::load(x, c + stride, elems, ls.elem_off, ra);
+    had_compress_chunk<LOGB, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+    c += stride;
   }
   if (ws != nullptr) {
     const float wg = block_max(run_max, lds4);
@@ -200,31 +241,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
 }
 
 // Abs-max of the transformed tensor, published into the workspace.
-template <int LOGB, int T>
-__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint4* __restrict__ x, int64_t nblocks,
+template <int LOGB>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* __restrict__ x, int64_t nblocks,
                                                                 Workspace* __restrict__ ws) {
   using Gm = HadGeom<LOGB>;
+  using CH = HadChunk<LOGB>;
   __shared__ float lds4[4];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
   const LaneSigns<LOGB> ls(lane);
   const int row = lane / Gm::G;
-  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
-  uint4 raw[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int64_t blk = (tile0 + i) * Gm::BPT + row;
-    raw[i] = make_uint4(0, 0, 0, 0);
-    if (blk < nblocks) raw[i] = ld16_nt(x + ((tile0 + i) * kTileElems + ls.elem_off) / 8);
-  }
+  const int64_t elems = nblocks << LOGB;
+  const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float run_max = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); c < nchunks; c += stride) {
+    uint4 raw[CH::T];
+    CH::load(x, c, elems, ls.elem_off, raw);
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    float v[8];
-    widen8(raw[i], v);
-    fwht_in_lane(v);
-    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
-    run_max = fmaxf(run_max, absmax8(v));
+    for (int i = 0; i < CH::T; ++i) {
+      float v[8];
+      widen8(raw[i], v);
+      fwht_in_lane(v);
+      fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+      run_max = fmaxf(run_max, absmax8(v));
+    }
   }
   const float wg = block_max(run_max, lds4);
   if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
@@ -292,38 +332,42 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
 
 // ------------------------------------------------------------ launchers --
 
-constexpr int kCompressTiles = 4;
-
 static int64_t had_groups(int logb, int64_t nblocks, int T) {
   const int64_t elems = nblocks << logb;
   const int64_t tiles = (elems + kTileElems - 1) / kTileElems;
   return (tiles + 4 * T - 1) / (4 * T);
 }
 
+// Persistent grid: enough workgroups to keep every CU busy, never more than
+// there are chunks.
+static unsigned persistent_groups(int logb, int64_t nblocks) {
+  const int64_t need = had_groups(logb, nblocks, kChunkTiles);
+  if (kPersistentGroupsPerCU == 0) return (unsigned)need;
+  const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
+  return (unsigned)(need < cap ? need : cap);
+}
+
 template <int LOGB>
 static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
-  constexpr int T = kCompressTiles;
-  const int64_t groups = had_groups(LOGB, a.nblocks, T);
+  const unsigned groups = persistent_groups(LOGB, a.nblocks);
   if (groups == 0) return hipSuccess;
-  dim3 grid((unsigned)groups), block(kBlockThreads);
-  auto* x = static_cast<const uint4*>(a.x);
+  dim3 grid(groups), block(kBlockThreads);
+  auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
-  if (a.auto_prepass) {
-    hipLaunchKernelGGL((k_fp8_had_amax<LOGB, T>), grid, block, 0, s, x, a.nblocks, ws);
-  }
+  if (a.auto_prepass) hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), grid, block, 0, s, x, a.nblocks, ws);
   if (a.g_from_ws) {
     if (a.dbg)
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, true, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, true>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
                          a.nblocks, a.g, ws, a.dbg);
     else
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, false, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
                          a.nblocks, a.g, ws, a.dbg);
   } else {
     if (a.dbg)
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, true, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, true>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
                          a.nblocks, a.g, ws, a.dbg);
     else
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, false, T>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
                          a.nblocks, a.g, ws, a.dbg);
   }
   return hipGetLastError();

@@ -133,6 +133,26 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   return hip_status(launch_quantize(a, stream));
 }
 
+}  // namespace
+
+namespace taco {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
+}  // namespace taco
+
+namespace {
+
 bool pair_allowed(const taco_codec& i, const taco_codec& o) {
   if (i.format == TACO_FMT_FP8_DUAL)
     return o.format == TACO_FMT_FP8_DUAL && o.block == i.block && o.hadamard == i.hadamard;

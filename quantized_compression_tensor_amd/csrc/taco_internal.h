@@ -92,7 +92,25 @@ struct ReduceArgs {
   void* rq_scale;
   uint8_t* rq_zero;
   float* rq_g_hdr;
+  bool write_g;         // this launch writes the requantized tensor scale
 };
+
+// Largest number of elements one reduce launch covers (keeps every buffer
+// offset, including the float32 sum's, below 2^31 bytes).
+constexpr int64_t kReducePiece = int64_t(1) << 28;
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+// Workgroups per CU for the persistent kernels (4 waves each); 0 = one
+// workgroup per four tiles of work (no grid-stride reuse).
+#ifndef TACO_GROUPS_PER_CU
+#define TACO_GROUPS_PER_CU 4
+#endif
+#ifndef TACO_REDUCE_GROUPS_PER_CU
+#define TACO_REDUCE_GROUPS_PER_CU 4
+#endif
+constexpr int kPersistentGroupsPerCU = TACO_GROUPS_PER_CU;
+constexpr int kReduceGroupsPerCU = TACO_REDUCE_GROUPS_PER_CU;
 
 hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s);
 hipError_t launch_fp8_had_decode(const FP8HadDecodeArgs& a, hipStream_t s);
