@@ -5,9 +5,10 @@ One step = every rank's compress of its shard (N bf16 shards already resident
 in HBM, one compress launch each) followed by the decompress-reduce of the N
 compressed shards with re-quantization for the gather stage -- all of the hot
 path. Shards rotate over several input sets so that the working set exceeds
-the 256 MB Infinity Cache. The step is captured once per input set as two HIP
-graphs (the N compress launches, then the reduce); HIP events around each
-graph on the launch stream give the per-kernel durations.
+the 256 MB Infinity Cache. Kernels are launched eagerly on one stream with a
+pair of HIP events around every launch on that stream, which gives each
+kernel's average launch duration; --launch graph replays the step from HIP
+graphs instead (slower here: the runtime leaves gaps between graph launches).
 
 value = N * rows * cols * 2 bytes of bf16 input / step time (GB/s).
 
@@ -38,9 +39,15 @@ def parse():
     ap.add_argument("--scale-mode", choices=["delayed", "auto", "given"], default="delayed",
                     help="FP8 tensor scale: delayed (abs-max of the previous step, one pass), "
                          "auto (abs-max pre-pass of this tensor) or given (a fixed g, no workspace)")
-    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="eager")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (known bytes) for counter calibration")
+    ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE / kernel-trace output into the "
+                         "profiles/ summaries and exit")
+    ap.add_argument("--command", default="", help="with --summarize: the profiled command, recorded")
     return ap.parse_args()
 
 
@@ -95,6 +102,83 @@ def read_traffic(name, workload, src_hash):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+COPY_BYTES = 256 << 20
+KERNEL_KEYS = {"compress": ("k_fp8_had_compress", "k_quantize"), "reduce": ("k_reduce",)}
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize(fetch_dir, write_dir, trace_dir, workload, command):
+    """Per-launch HBM bytes of the hot kernels from two counter passes, scaled by
+    what the same counters read for a plain copy of COPY_BYTES (read and write),
+    plus the kernel-trace averages; written to profiles/<kernel>_<workload>_*.txt."""
+    import numpy as np
+    src_hash = kernel_source_hash()
+    per = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for row in _csv_rows(d, "counter_collection.csv"):
+            if row.get("Counter_Name") != cname:
+                continue
+            name = row.get("Kernel_Name", "")
+            per.setdefault((cname, name), []).append(float(row["Counter_Value"]))
+    # the calibration copies are the three largest copy dispatches of the run
+    copy_f = sorted((v for (c, k), vs in per.items() if c == "FETCH_SIZE" and "copy" in k.lower() for v in vs),
+                    reverse=True)[:3]
+    copy_w = sorted((v for (c, k), vs in per.items() if c == "WRITE_SIZE" and "copy" in k.lower() for v in vs),
+                    reverse=True)[:3]
+    f_fetch = COPY_BYTES / (np.median(copy_f) * 1024) if copy_f else None
+    f_write = COPY_BYTES / (np.median(copy_w) * 1024) if copy_w else None
+    trace = {}
+    for row in _csv_rows(trace_dir, "kernel_stats.csv"):
+        trace[row["Name"]] = row
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    written = []
+    for key, subs in KERNEL_KEYS.items():
+        fk = [(k, vs) for (c, k), vs in per.items() if c == "FETCH_SIZE" and any(t in k for t in subs)]
+        wk = [(k, vs) for (c, k), vs in per.items() if c == "WRITE_SIZE" and any(t in k for t in subs)]
+        fk.sort(key=lambda kv: -len(kv[1]))
+        wk.sort(key=lambda kv: -len(kv[1]))
+        if not fk or not wk:
+            continue
+        kname = fk[0][0]
+        fetch_kib = float(np.median(fk[0][1]))
+        write_kib = float(np.median(wk[0][1]))
+        hbm = None
+        if f_fetch and f_write:
+            hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
+        tr = next((v for n, v in trace.items() if n == kname), None)
+        path = os.path.join(ROOT, "profiles", f"{key}_{workload}_counters.txt")
+        with open(path, "w") as fh:
+            fh.write(f"# rocprofv3 hardware counters for {kname}\n")
+            fh.write(f"# workload: {workload}\n# command: {command}\n")
+            fh.write("# FETCH_SIZE and WRITE_SIZE come from separate --pmc passes (KiB per dispatch,\n"
+                     "# median over dispatches); each is scaled by COPY_BYTES / counter of a plain\n"
+                     "# device-to-device copy of COPY_BYTES profiled in the same pass.\n")
+            fh.write(f"kernel: {kname}\n")
+            fh.write(f"source_hash: {src_hash}\n")
+            fh.write(f"fetch_kib_per_dispatch: {fetch_kib:.1f}\n")
+            fh.write(f"write_kib_per_dispatch: {write_kib:.1f}\n")
+            fh.write(f"copy_bytes: {COPY_BYTES}\n")
+            fh.write(f"copy_fetch_factor: {f_fetch}\n")
+            fh.write(f"copy_write_factor: {f_write}\n")
+            fh.write(f"hbm_bytes_per_launch: {hbm}\n")
+            if tr is not None:
+                fh.write(f"trace_calls: {tr.get('Calls')}\n")
+                fh.write(f"trace_average_ns: {tr.get('AverageNs')}\n")
+                fh.write(f"trace_min_ns: {tr.get('MinNs')}\n")
+                fh.write(f"trace_max_ns: {tr.get('MaxNs')}\n")
+        written.append(path)
+    print("\n".join(written))
 
 
 def cpu_baseline(w, seconds):
@@ -169,6 +253,9 @@ def quality(w, bufs, sets_bits, c_in):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize, args.workload, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU exchange is a design, not part of this build)", file=sys.stderr)
@@ -204,18 +291,23 @@ def main():
     wss = [torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(w.shards)]
     torch.cuda.synchronize()
 
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    def compress_one(s, r):
+        T.taco_compress(c_in, xs[s][r], w.rows, w.cols, scale, bufs[s][r],
+                        workspace=wss[r] if use_ws else None, stream=sh)
+
     def compress(s):
         for r in range(w.shards):
-            T.taco_compress(c_in, xs[s][r], w.rows, w.cols, scale, bufs[s][r],
-                            workspace=wss[r] if use_ws else None)
+            compress_one(s, r)
 
     def reduce(s):
         if c_out is not None:
-            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, None, c_out, outs[s])
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, None, c_out, outs[s], stream=sh)
         else:
-            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, outs[s])
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, outs[s], stream=sh)
 
-    stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         # first calls seed the delayed-scale history with this data
         for s in range(nsets):
@@ -223,43 +315,74 @@ def main():
             reduce(s)
         torch.cuda.synchronize()
         if args.launch == "graph":
-            g_comp, g_red = [], []
+            g_step = []
             for s in range(nsets):
-                gc = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gc, stream=stream):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
                     compress(s)
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr, stream=stream):
                     reduce(s)
-                g_comp.append(gc)
-                g_red.append(gr)
-            run_c = lambda s: g_comp[s].replay()
-            run_r = lambda s: g_red[s].replay()
-        else:
-            run_c, run_r = compress, reduce
+                g_step.append(g)
+
+        def step(s):
+            if args.launch == "graph":
+                g_step[s].replay()
+            else:
+                compress(s)
+                reduce(s)
 
         for i in range(args.warmup):
-            run_c(i % nsets)
-            run_r(i % nsets)
+            step(i % nsets)
         torch.cuda.synchronize()
 
         K = args.steps
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        ev_c, ev_r, ev_s = [], [], []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
             s = i % nsets
-            ev[i][0].record(stream)
-            run_c(s)
-            ev[i][1].record(stream)
-            run_r(s)
-            ev[i][2].record(stream)
+            if args.launch == "graph":
+                a, b = mk(), mk()
+                a.record(stream)
+                step(s)
+                b.record(stream)
+                ev_s.append((a, b))
+                continue
+            for r in range(w.shards):
+                a, b = mk(), mk()
+                a.record(stream)
+                compress_one(s, r)
+                b.record(stream)
+                ev_c.append((a, b))
+            a, b = mk(), mk()
+            a.record(stream)
+            reduce(s)
+            b.record(stream)
+            ev_r.append((a, b))
+        host = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
-    t_comp = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / w.shards   # ms per compress launch
-    t_red = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))                 # ms per reduce launch
+        if args.launch == "graph":
+            # per-kernel durations for the roofline: one more pass of eager
+            # launches with events, right after the timed graph replays
+            for i in range(K):
+                s = i % nsets
+                for r in range(w.shards):
+                    a, b = mk(), mk()
+                    a.record(stream)
+                    compress_one(s, r)
+                    b.record(stream)
+                    ev_c.append((a, b))
+                a, b = mk(), mk()
+                a.record(stream)
+                reduce(s)
+                b.record(stream)
+                ev_r.append((a, b))
+            torch.cuda.synchronize()
+
+    t_comp = float(np.mean([a.elapsed_time(b) for a, b in ev_c]))   # ms per compress launch
+    t_red = float(np.mean([a.elapsed_time(b) for a, b in ev_r]))    # ms per reduce launch
     ms_step = wall * 1e3 / K
     value = in_bytes / (ms_step * 1e-3) / 1e9
 
@@ -273,6 +396,13 @@ def main():
     else:
         ach, bytes_launch, kname = red_gbs, b_red, "reduce"
     traffic = read_traffic(kname, w.name, src_hash)
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     q = quality(w, bufs, sets_bits, c_in)
     cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
@@ -310,6 +440,7 @@ def main():
             "compress_ms": round(t_comp, 5), "compress_GBs": round(comp_gbs, 1),
             "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
             "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "host_ms_per_step": round(host * 1e3 / K, 5),
         },
         "quality": q,
         "cpu_baseline": cpu,
