@@ -5,10 +5,12 @@ One step = every rank's compress of its shard (N bf16 shards already resident
 in HBM, one compress launch each) followed by the decompress-reduce of the N
 compressed shards with re-quantization for the gather stage -- all of the hot
 path. Shards rotate over several input sets so that the working set exceeds
-the 256 MB Infinity Cache. Kernels are launched eagerly on one stream with a
-pair of HIP events around every launch on that stream, which gives each
-kernel's average launch duration; --launch graph replays the step from HIP
-graphs instead (slower here: the runtime leaves gaps between graph launches).
+the 256 MB Infinity Cache. Kernels are launched eagerly on one stream; the
+timed region has one pair of HIP events per step. Each kernel's average launch
+duration (for the roofline) comes from the same launches repeated right after,
+each between its own pair of events on the launch stream. --launch graph
+replays the step from HIP graphs instead (slower here: the runtime leaves gaps
+between graph launches).
 
 value = N * rows * cols * 2 bytes of bf16 input / step time (GB/s).
 
@@ -42,6 +44,9 @@ def parse():
     ap.add_argument("--launch", choices=["graph", "eager"], default="eager")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
+                         "next activation, on a second stream, and report the overlap")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (known bytes) for counter calibration")
     ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
@@ -178,6 +183,17 @@ def summarize(fetch_dir, write_dir, trace_dir, workload, command):
                 fh.write(f"trace_min_ns: {tr.get('MinNs')}\n")
                 fh.write(f"trace_max_ns: {tr.get('MaxNs')}\n")
         written.append(path)
+    if trace:
+        path = os.path.join(ROOT, "profiles", f"kernels_{workload}_trace.txt")
+        with open(path, "w") as fh:
+            fh.write(f"# rocprofv3 kernel-trace statistics, workload {workload}\n# command: {command}\n")
+            fh.write("# (kernel durations exclude dispatch gaps; the bench's step events include them)\n")
+            fh.write(f"source_hash: {src_hash}\n")
+            fh.write(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
+            for name, row in sorted(trace.items(), key=lambda kv: -float(kv[1]["TotalDurationNs"])):
+                fh.write(f"{int(row['Calls']):>6} {float(row['AverageNs']) / 1e3:>9.2f} "
+                         f"{float(row['MinNs']) / 1e3:>9.2f} {float(row['MaxNs']) / 1e3:>9.2f}  {name[:160]}\n")
+        written.append(path)
     print("\n".join(written))
 
 
@@ -249,6 +265,42 @@ def quality(w, bufs, sets_bits, c_in):
     ref = oracle.decode(oracle.compress(oc, x))
     return {"rel_mse_gpu": oracle.rel_mse(got, xf), "rel_mse_oracle": oracle.rel_mse(ref, xf),
             "sample_rows": int(len(rows_idx))}
+
+
+def measure_overlap(w, step_fn, nsets, stream, codec_ms, K):
+    """The bf16 GEMM [rows, cols] x [cols, cols] that produces the next activation,
+    alone and concurrently with the codec step on a second stream (default
+    priority). Reported: GEMM alone, codec alone (the timed step), both together,
+    and how much of the shorter one the overlap hid."""
+    import torch
+    g_stream = torch.cuda.Stream()
+    a = torch.randn(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(w.cols, w.cols, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(g_stream):
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(g_stream):
+        for _ in range(K):
+            torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    gemm_ms = (time.perf_counter() - t0) * 1e3 / K
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        with torch.cuda.stream(g_stream):
+            torch.matmul(a, b, out=c)
+        with torch.cuda.stream(stream):
+            step_fn(i % nsets)
+    torch.cuda.synchronize()
+    both_ms = (time.perf_counter() - t0) * 1e3 / K
+    flops = 2.0 * w.rows * w.cols * w.cols
+    serial = gemm_ms + codec_ms
+    return {"gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(flops / gemm_ms / 1e9, 1),
+            "codec_ms": round(codec_ms, 4), "both_ms": round(both_ms, 4), "serial_ms": round(serial, 4),
+            "hidden_frac": round((serial - both_ms) / min(gemm_ms, codec_ms), 3)}
 
 
 def main():
@@ -336,18 +388,24 @@ def main():
 
         K = args.steps
         mk = lambda: torch.cuda.Event(enable_timing=True)
-        ev_c, ev_r, ev_s = [], [], []
+        # timed region: K whole steps, one event pair per step (event records
+        # between kernels cost GPU time, so none inside a step)
+        ev_s = [(mk(), mk()) for _ in range(K)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
+            ev_s[i][0].record(stream)
+            step(i % nsets)
+            ev_s[i][1].record(stream)
+        host = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+        # per-kernel launch durations (roofline): the same launches again, each
+        # between its own pair of events on the launch stream
+        ev_c, ev_r = [], []
+        for i in range(K):
             s = i % nsets
-            if args.launch == "graph":
-                a, b = mk(), mk()
-                a.record(stream)
-                step(s)
-                b.record(stream)
-                ev_s.append((a, b))
-                continue
             for r in range(w.shards):
                 a, b = mk(), mk()
                 a.record(stream)
@@ -359,31 +417,12 @@ def main():
             reduce(s)
             b.record(stream)
             ev_r.append((a, b))
-        host = time.perf_counter() - t0
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-
-        if args.launch == "graph":
-            # per-kernel durations for the roofline: one more pass of eager
-            # launches with events, right after the timed graph replays
-            for i in range(K):
-                s = i % nsets
-                for r in range(w.shards):
-                    a, b = mk(), mk()
-                    a.record(stream)
-                    compress_one(s, r)
-                    b.record(stream)
-                    ev_c.append((a, b))
-                a, b = mk(), mk()
-                a.record(stream)
-                reduce(s)
-                b.record(stream)
-                ev_r.append((a, b))
-            torch.cuda.synchronize()
 
     t_comp = float(np.mean([a.elapsed_time(b) for a, b in ev_c]))   # ms per compress launch
     t_red = float(np.mean([a.elapsed_time(b) for a, b in ev_r]))    # ms per reduce launch
     ms_step = wall * 1e3 / K
+    gpu_ms_step = float(np.mean([a.elapsed_time(b) for a, b in ev_s]))
     value = in_bytes / (ms_step * 1e-3) / 1e9
 
     b_comp, b_red = algorithmic_bytes(w)
@@ -396,6 +435,11 @@ def main():
     else:
         ach, bytes_launch, kname = red_gbs, b_red, "reduce"
     traffic = read_traffic(kname, w.name, src_hash)
+
+    overlap = None
+    if args.overlap:
+        overlap = measure_overlap(w, step_fn=lambda s: (compress(s), reduce(s)), nsets=nsets, stream=stream,
+                                  codec_ms=ms_step, K=max(5, K // 5))
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -441,9 +485,11 @@ def main():
             "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
             "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "host_ms_per_step": round(host * 1e3 / K, 5),
+            "event_ms_per_step": round(gpu_ms_step, 5),
         },
         "quality": q,
         "cpu_baseline": cpu,
+        **({"overlap": overlap} if overlap else {}),
         "source_hash": src_hash,
     }
     print(json.dumps(out))

@@ -30,7 +30,7 @@ TACO_FMT_INT8_ASYM = 4
 TACO_SCALE_AUTO = 0.0
 TACO_SCALE_DELAYED = -1.0
 TACO_MAX_SHARDS = 16
-TACO_WORKSPACE_BYTES = 8192
+TACO_WORKSPACE_BYTES = 16384
 
 # Entry points declared in include/taco.h (checked by the ABI tests).
 EXPORTS = (
@@ -208,3 +208,22 @@ def regions(buf, c, rows, cols):
     aux = buf[L.aux_off:L.aux_off + L.aux_bytes]
     ten = buf[L.tensor_off:L.tensor_off + L.tensor_bytes].view(torch.float32)
     return codes, sc, aux, ten
+
+
+def workspace_history(ws):
+    """Read an FP8 tensor-scale workspace (a device tensor, 16 KiB): returns
+    (calls recorded, abs-max recorded by the most recent call, that call's slot
+    index). Layout (uint32 words): [0] grid P of the last call; words 32 + 32 g:
+    ticket counter of group g (16 groups); words 544 + 512 s + 32 g: abs-max
+    accumulator (float bits) of slot s (3 slots), group g. Inspection only."""
+    import numpy as np
+    w = ws.detach().cpu().numpy().view(np.uint32).reshape(-1)
+    grid = int(w[0])
+    if grid == 0:
+        return 0, 0.0, None
+    G = min(grid, 16)
+    members0 = -(-grid // G)
+    calls = int(w[32]) // members0
+    slot = (calls - 1) % 3
+    acc = w[544 + 512 * slot: 544 + 512 * (slot + 1)].reshape(16, 32)[:G, 0]
+    return calls, float(acc.view(np.float32).max()), slot

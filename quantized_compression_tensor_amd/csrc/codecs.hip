@@ -205,8 +205,9 @@ TACO_DEV void store_lane(const LaneCodes& r, int64_t e0, uint8_t* codes, void* s
 template <int FMT, int B>
 struct LaneIn {
   uint4 q;
-  float s;   // INT scale, FP8 combined scale g * 2^-k
-  float zf;  // zero point as float
+  float s;      // INT scale, FP8 combined scale g * 2^-k
+  float zf;     // asymmetric zero point as float
+  uint32_t zi;  // asymmetric zero point
 };
 
 template <int FMT, int B>
@@ -220,20 +221,33 @@ TACO_DEV LaneIn<FMT, B> load_in(const uint8_t* codes, const void* scale, const u
   } else {
     r.q = *reinterpret_cast<const uint4*>(codes + e0);
   }
+  r.zi = 0;
   if constexpr (FMT == kFP8) {
     const int k = static_cast<const int8_t*>(scale)[blk];
     r.s = (*g_hdr) * pow2f(-k);
     r.zf = 0.0f;
   } else {
     r.s = static_cast<const float*>(scale)[blk];
-    r.zf = (FMT == kINT8S) ? 0.0f : (float)zero[blk];
+    r.zi = (FMT == kINT8S) ? 0u : (uint32_t)zero[blk];
+    r.zf = (float)r.zi;
   }
   return r;
 }
 
-// Dequantized values of one lane: FP8 dec(q) * (g * 2^-k) (dec(q) * 2^-k is
-// exact, so this is the single rounding of dec(q) * 2^-k * g); INT8 q * s;
-// asymmetric (q - z) * s with q - z an exact small integer.
+// Byte b of w as a float (one v_cvt_f32_ubyte{b}).
+TACO_DEV float ubyte(uint32_t w, int b) { return (float)((w >> (8 * b)) & 0xFFu); }
+
+// Dequantized values of one lane.
+//  FP8:  dec(q) * (g * 2^-k); dec(q) * 2^-k is exact, so this is the single
+//        rounding of dec(q) * 2^-k * g.
+//  INT8 symmetric: RN(q * s). The bytes are biased to q + 128 (xor 0x80) and
+//        converted unsigned; fma(q + 128, s, -128 s) rounds the exact real
+//        (q + 128) s - 128 s = q s once (-128 s is an exact power-of-two
+//        multiple while s <= 2^120).
+//  INT4 asymmetric: RN((q - z) * s). q - z + 16 is formed on packed bytes
+//        (no carries: it lies in [1, 31]); fma(q - z + 16, s, -16 s) again
+//        rounds (q - z) s exactly once.
+//  INT8 asymmetric: RN((q - z) * s) with q - z formed in float (exact).
 template <int FMT, int B>
 TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
   if constexpr (FMT == kFP8) {
@@ -242,27 +256,50 @@ TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) d[i] = d[i] * in.s;
   } else if constexpr (FMT == kINT8S) {
-    const uint32_t w[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
+    const uint32_t w[4] = {in.q.x ^ 0x80808080u, in.q.y ^ 0x80808080u, in.q.z ^ 0x80808080u,
+                           in.q.w ^ 0x80808080u};
+    if (__builtin_expect(in.s <= 0x1p120f, 1)) {
+      const float bias = -128.0f * in.s;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d[4 * j + b] = (float)(int)(int8_t)((w[j] >> (8 * b)) & 0xFF) * in.s;
+        for (int b = 0; b < 4; ++b) d[4 * j + b] = fmaf(ubyte(w[j], b), in.s, bias);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) d[4 * j + b] = (ubyte(w[j], b) - 128.0f) * in.s;
+    }
   } else if constexpr (FMT == kINT8A) {
     const uint32_t w[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d[4 * j + b] = ((float)((w[j] >> (8 * b)) & 0xFF) - in.zf) * in.s;
+      for (int b = 0; b < 4; ++b) d[4 * j + b] = (ubyte(w[j], b) - in.zf) * in.s;
   } else {
-    const uint32_t w[2] = {in.q.x, in.q.y};
+    const uint32_t zrep = 0x10101010u - in.zi * 0x01010101u;   // 16 - z in every byte
+    uint32_t t[4];
+    t[0] = (in.q.x & 0x0F0F0F0Fu) + zrep;          // elements 0, 2, 4, 6
+    t[1] = ((in.q.x >> 4) & 0x0F0F0F0Fu) + zrep;   // elements 1, 3, 5, 7
+    t[2] = (in.q.y & 0x0F0F0F0Fu) + zrep;
+    t[3] = ((in.q.y >> 4) & 0x0F0F0F0Fu) + zrep;
+    if (__builtin_expect(in.s <= 0x1p120f, 1)) {
+      const float bias = -16.0f * in.s;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t lo = w[j] & 0x0F0F0F0Fu, hi = (w[j] >> 4) & 0x0F0F0F0Fu;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        d[8 * j + 2 * b] = ((float)((lo >> (8 * b)) & 0xFF) - in.zf) * in.s;
-        d[8 * j + 2 * b + 1] = ((float)((hi >> (8 * b)) & 0xFF) - in.zf) * in.s;
-      }
+        for (int b = 0; b < 4; ++b) {
+          d[8 * j + 2 * b] = fmaf(ubyte(t[2 * j], b), in.s, bias);
+          d[8 * j + 2 * b + 1] = fmaf(ubyte(t[2 * j + 1], b), in.s, bias);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          d[8 * j + 2 * b] = (ubyte(t[2 * j], b) - 16.0f) * in.s;
+          d[8 * j + 2 * b + 1] = (ubyte(t[2 * j + 1], b) - 16.0f) * in.s;
+        }
     }
   }
 }
@@ -282,40 +319,55 @@ struct QuantK {
   float* dbg;
 };
 
+// Quantization without a transform. Grid-stride over 1024-element wave tiles;
+// with a workspace (FP8 tensor-scale history) the grid is the fixed persistent
+// one the workspace protocol needs.
 template <int FMT, int B, bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   __shared__ float lds4[4];
+  __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t tile = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
-  const bool valid = e0 < a.n;   // n is a multiple of B, B a multiple of 16
+  const int64_t ntiles = (a.n + kWaveElems - 1) / kWaveElems;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float inv_g = 0.0f;
+  uint32_t t = 0;
   if constexpr (FMT == kFP8) {
-    const float g = a.g_from_ws ? tensor_scale_from_amax(ws_load_amax_last(a.ws)) : a.g;
+    if (a.ws != nullptr) {
+      if (threadIdx.x == 0) lds_t = ws_ticket(a.ws);
+      __syncthreads();
+      t = lds_t;
+    }
+    const float g = a.g_from_ws ? tensor_scale_from_amax(ws_prev_amax(a.ws, t)) : a.g;
     inv_g = 1.0f / g;
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.g_hdr = g;
   }
-  float v[16];
-  if (valid) load_lane<F32IN>(a.x, e0, v);
-  else {
+  float run_max = 0.0f;
+  for (int64_t tile = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); tile < ntiles;
+       tile += stride) {
+    const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
+    const bool valid = e0 < a.n;   // n is a multiple of B, B a multiple of 16
+    float v[16];
+    if (valid) load_lane<F32IN>(a.x, e0, v);
+    else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-  }
-  const float amax = (FMT == kFP8) ? absmax16(v) : 0.0f;
-  float pre[16];
-  LaneCodes r = quant_lane<FMT, B>(v, inv_g, a.dbg ? pre : nullptr);
-  if (valid) {
-    store_lane<FMT, B>(r, e0, a.codes, a.scale, a.zero);
-    if (a.dbg) {
-      float4* d = reinterpret_cast<float4*>(a.dbg + e0);
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    if constexpr (FMT == kFP8) run_max = fmaxf(run_max, absmax16(v));
+    float pre[16];
+    LaneCodes r = quant_lane<FMT, B>(v, inv_g, a.dbg ? pre : nullptr);
+    if (valid) {
+      store_lane<FMT, B>(r, e0, a.codes, a.scale, a.zero);
+      if (a.dbg) {
+        float4* d = reinterpret_cast<float4*>(a.dbg + e0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = make_float4(pre[4 * q], pre[4 * q + 1], pre[4 * q + 2], pre[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) d[q] = make_float4(pre[4 * q], pre[4 * q + 1], pre[4 * q + 2], pre[4 * q + 3]);
+      }
     }
   }
   if constexpr (FMT == kFP8) {
     if (a.ws != nullptr) {
-      const float wg = block_max(amax, lds4);
-      if (threadIdx.x == 0) ws_publish_amax(a.ws, wg, gridDim.x);
+      const float wg = block_max(run_max, lds4);
+      if (wave_in_group() == 0) ws_record(a.ws, t, wg);
     }
   }
 }
@@ -324,17 +376,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
 template <bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void k_amax(const void* x, int64_t n, Workspace* ws) {
   __shared__ float lds4[4];
+  __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t tile = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-  const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
+  if (threadIdx.x == 0) lds_t = ws_ticket(ws);
+  const int64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float m = 0.0f;
-  if (e0 < n) {
-    float v[16];
-    load_lane<F32IN>(x, e0, v);
-    m = absmax16(v);
+  for (int64_t tile = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); tile < ntiles;
+       tile += stride) {
+    const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
+    if (e0 < n) {
+      float v[16];
+      load_lane<F32IN>(x, e0, v);
+      m = fmaxf(m, absmax16(v));
+    }
   }
-  const float wg = block_max(m, lds4);
-  if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
+  const float wg = block_max(m, lds4);   // its barrier also publishes lds_t
+  if (wave_in_group() == 0) ws_record(ws, lds_t, wg);
 }
 
 struct DequantK {
@@ -406,13 +464,15 @@ TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0) {
   } else {
     r.q = bload128<kNT>(s.codes, e0, 0);
   }
+  r.zi = 0;
   if constexpr (FMT == kFP8) {
     const int k = (int)(int8_t)bload8(s.scale, blk, 0);
     r.s = __uint_as_float(bload32(s.g, 0, 0)) * pow2f(-k);
     r.zf = 0.0f;
   } else {
     r.s = __uint_as_float(bload32(s.scale, blk * 4, 0));
-    r.zf = (FMT == kINT8S) ? 0.0f : (float)bload8(s.zero, blk, 0);
+    r.zi = (FMT == kINT8S) ? 0u : bload8(s.zero, blk, 0);
+    r.zf = (float)r.zi;
   }
   return r;
 }
@@ -445,8 +505,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    constexpr int GRP = NMAX < 8 ? NMAX : 8;
-#pragma unroll
+    // groups of four shards; the group loop is not unrolled so that only four
+    // shards' buffer resources are live at a time (no scalar-register spills)
+    constexpr int GRP = NMAX < 4 ? NMAX : 4;
+#pragma unroll 1
     for (int r0 = 0; r0 < NMAX; r0 += GRP) {
       LaneIn<FIN, BIN> in[GRP];
 #pragma unroll
@@ -499,9 +561,19 @@ static dim3 grid_for(int64_t n) {
   return dim3((unsigned)((tiles + 3) / 4));
 }
 
+// With a workspace every call runs the same persistent grid (its protocol
+// needs it); otherwise one wave per tile, capped at the persistent size.
+static dim3 quant_grid(const QuantArgs& a) {
+  const unsigned cap = (unsigned)(device_cu_count() * kPersistentGroupsPerCU);
+  if (a.fmt == kFP8 && a.ws != nullptr) return dim3(cap);
+  dim3 g = grid_for(a.n);
+  if (g.x > cap) g.x = cap;
+  return g;
+}
+
 template <int FMT, int B>
 static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
-  dim3 grid = grid_for(a.n), block(kBlockThreads);
+  dim3 grid = quant_grid(a), block(kBlockThreads);
   if (a.f32_in) hipLaunchKernelGGL((k_quantize<FMT, B, true>), grid, block, 0, s, k);
   else hipLaunchKernelGGL((k_quantize<FMT, B, false>), grid, block, 0, s, k);
 }
@@ -511,7 +583,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   QuantK k{a.x, a.n, a.codes, a.scale, a.zero, a.g_hdr, a.g, a.g_from_ws ? 1 : 0,
            static_cast<Workspace*>(a.ws), a.dbg};
   if (a.fmt == kFP8 && a.auto_prepass) {
-    dim3 grid = grid_for(a.n), block(kBlockThreads);
+    dim3 grid = quant_grid(a), block(kBlockThreads);
     if (a.f32_in) hipLaunchKernelGGL((k_amax<true>), grid, block, 0, s, a.x, a.n, k.ws);
     else hipLaunchKernelGGL((k_amax<false>), grid, block, 0, s, a.x, a.n, k.ws);
   }

@@ -184,72 +184,65 @@ TACO_DEV float wave_max(float a) {
 }
 
 // ------------------------------------------------------------- workspace --
-// Caller-owned, zero-filled once; every kernel that uses it leaves all its
-// counters and accumulators at zero again. `amax_last` holds the abs-max of
-// the transformed tensor seen by the most recent call.
+// Abs-max history of an FP8 tensor scale, in caller-owned memory that is
+// zero-filled once. Kernels that use it always run a fixed grid of P
+// workgroups (P = kPersistentGroupsPerCU * CUs) split into G = 16 groups.
 //
-// Workgroups fold their maxima in two levels: into one of kPubGroups group
-// accumulators (each counter and each max on its own 128-byte line, so that
-// atomics to them proceed in parallel), then the last arrival of each group
-// into the top accumulator. A single shared address would serialize one
-// atomic per workgroup.
+// At its start a workgroup takes a ticket from its group's counter (one
+// returning atomic add; each counter sits on its own 128-byte line). Every call
+// adds exactly `members` to each counter, so ticket / members is the same call
+// index t in every workgroup of a call. Call t
+//   * reads the previous call's maxima from slot (t + 2) % 3,
+//   * folds its own workgroup maxima into slot t % 3 (atomic max, not awaited),
+//   * zeroes slot (t + 1) % 3 for the next call (workgroup 0).
+// No slot is read and written by the same call, and the kernel boundary orders
+// calls, so no fence and no "last workgroup" chain is needed.
 constexpr int kPubGroups = 16;
 constexpr int kLineWords = 32;
 
 struct Workspace {
-  uint32_t amax_last;   // float bits
-  uint32_t calls;
-  uint32_t top_arrivals;
-  uint32_t top_max;
-  uint32_t pad0[kLineWords - 4];
-  uint32_t grp_arrivals[kPubGroups][kLineWords];
-  uint32_t grp_max[kPubGroups][kLineWords];
+  uint32_t grid;                                 // P of the most recent call
+  uint32_t pad0[kLineWords - 1];
+  uint32_t calls[kPubGroups][kLineWords];        // ticket counters
+  uint32_t acc[3][kPubGroups][kLineWords];       // abs-max accumulators (float bits)
 };
-static_assert(sizeof(Workspace) <= 8192, "workspace size");
-
-TACO_DEV float ws_load_amax_last(Workspace* ws) {
-  return __uint_as_float(__hip_atomic_load(&ws->amax_last, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
+static_assert(sizeof(Workspace) <= 16384, "workspace size");
 
 #define TACO_AT_MAX(p, v) __hip_atomic_fetch_max((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_ADD(p, v) __hip_atomic_fetch_add((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-#define TACO_AT_XCHG(p, v) __hip_atomic_exchange((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_STORE(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-#define TACO_WAIT_MEM() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+#define TACO_AT_LOAD(p) __hip_atomic_load((p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 
-// Fold this workgroup's non-negative max into the workspace; the last
-// workgroup to arrive publishes the tensor max. Called once per workgroup of
-// the grid, by thread 0.
-//
-// Ordering without fences: device-scope read-modify-writes are performed at
-// the device's coherence point, and each one here waits for its returned
-// value before the next is issued. A workgroup's max is therefore performed
-// before its arrival is counted, and the arrival that completes a count reads
-// the accumulator after every max that count covers. (Release/acquire fences
-// would instead write back and invalidate the issuing XCD's L2 once per
-// workgroup.)
-TACO_DEV void ws_publish_amax(Workspace* ws, float wg_max, uint32_t num_groups) {
-  const uint32_t G = num_groups < (uint32_t)kPubGroups ? num_groups : (uint32_t)kPubGroups;
+TACO_DEV uint32_t ws_groups(uint32_t grid) { return grid < (uint32_t)kPubGroups ? grid : (uint32_t)kPubGroups; }
+
+// Call index of this launch (thread 0 of each workgroup).
+TACO_DEV uint32_t ws_ticket(Workspace* ws) {
+  const uint32_t G = ws_groups(gridDim.x);
   const uint32_t g = blockIdx.x % G;
-  const uint32_t members = (num_groups - g + G - 1) / G;
-  TACO_AT_MAX(&ws->grp_max[g][0], __float_as_uint(wg_max));
-  TACO_WAIT_MEM();
-  const uint32_t prev = TACO_AT_ADD(&ws->grp_arrivals[g][0], 1u);
-  TACO_WAIT_MEM();
-  if (prev != members - 1) return;
-  const uint32_t gm = TACO_AT_XCHG(&ws->grp_max[g][0], 0u);
-  TACO_WAIT_MEM();
-  TACO_AT_STORE(&ws->grp_arrivals[g][0], 0u);
-  TACO_AT_MAX(&ws->top_max, gm);
-  TACO_WAIT_MEM();
-  const uint32_t prev2 = TACO_AT_ADD(&ws->top_arrivals, 1u);
-  TACO_WAIT_MEM();
-  if (prev2 != G - 1) return;
-  const uint32_t a = TACO_AT_XCHG(&ws->top_max, 0u);
-  TACO_WAIT_MEM();
-  TACO_AT_STORE(&ws->amax_last, a);
-  TACO_AT_ADD(&ws->calls, 1u);
-  TACO_AT_STORE(&ws->top_arrivals, 0u);
+  const uint32_t members = (gridDim.x - g + G - 1) / G;
+  return TACO_AT_ADD(&ws->calls[g][0], 1u) / members;
+}
+
+// Abs-max recorded by the previous call (any wave; the result is wave-uniform).
+TACO_DEV float ws_prev_amax(Workspace* ws, uint32_t t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t slot = (t + 2) % 3;
+  float v = 0.0f;
+  if (lane < kPubGroups) v = __uint_as_float(TACO_AT_LOAD(&ws->acc[slot][lane][0]));
+  v = group_max<16>(v);   // lanes 0-15 now all hold the max
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+}
+
+// Fold this workgroup's max into call t's slot; workgroup 0 clears the next
+// slot. Called by every thread of wave 0 (lanes beyond the first do nothing).
+TACO_DEV void ws_record(Workspace* ws, uint32_t t, float wg_max) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t G = ws_groups(gridDim.x);
+  if (lane == 0) TACO_AT_MAX(&ws->acc[t % 3][blockIdx.x % G][0], __float_as_uint(wg_max));
+  if (blockIdx.x == 0) {
+    if (lane < kPubGroups) TACO_AT_STORE(&ws->acc[(t + 1) % 3][lane][0], 0u);
+    if (lane == 0) TACO_AT_STORE(&ws->grid, gridDim.x);
+  }
 }
 
 // Workgroup max of a non-negative float through LDS (all threads call it).

@@ -209,22 +209,30 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB>;
   __shared__ float lds4[4];
+  __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
   const int row = lane / Gm::G;
-
-  const float g = GFROM_WS ? tensor_scale_from_amax(ws_load_amax_last(ws)) : g_arg;
-  const float inv_g = 1.0f / g;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
 
   const int64_t elems = nblocks << LOGB;
   const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
 
-  float run_max = 0.0f;
   uint4 ra[CH::T], rb[CH::T];
-  CH::load(x, c, elems, ls.elem_off, ra);
+  CH::load(x, c, elems, ls.elem_off, ra);   // first chunk in flight during the ticket
+
+  uint32_t t = 0;
+  if (ws != nullptr) {
+    if (threadIdx.x == 0) lds_t = ws_ticket(ws);
+    __syncthreads();
+    t = lds_t;
+  }
+  const float g = GFROM_WS ? tensor_scale_from_amax(ws_prev_amax(ws, t)) : g_arg;
+  const float inv_g = 1.0f / g;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
+
+  float run_max = 0.0f;
   while (c < nchunks) {
     CH::load(x, c + stride, elems, ls.elem_off, rb);
     had_compress_chunk<LOGB, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
@@ -236,20 +244,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   }
   if (ws != nullptr) {
     const float wg = block_max(run_max, lds4);
-    if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
+    if (wave_in_group() == 0) ws_record(ws, t, wg);
   }
 }
 
-// Abs-max of the transformed tensor, published into the workspace.
+// Abs-max of the transformed tensor, recorded in the workspace.
 template <int LOGB>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* __restrict__ x, int64_t nblocks,
                                                                 Workspace* __restrict__ ws) {
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB>;
   __shared__ float lds4[4];
+  __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
-  const int row = lane / Gm::G;
+  if (threadIdx.x == 0) lds_t = ws_ticket(ws);
   const int64_t elems = nblocks << LOGB;
   const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
@@ -266,8 +275,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
       run_max = fmaxf(run_max, absmax8(v));
     }
   }
-  const float wg = block_max(run_max, lds4);
-  if (threadIdx.x == 0) ws_publish_amax(ws, wg, gridDim.x);
+  const float wg = block_max(run_max, lds4);   // its barrier also publishes lds_t
+  if (wave_in_group() == 0) ws_record(ws, lds_t, wg);
 }
 
 // --------------------------------------------------------------- decode --
@@ -339,17 +348,18 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
 }
 
 // Persistent grid: enough workgroups to keep every CU busy, never more than
-// there are chunks.
-static unsigned persistent_groups(int logb, int64_t nblocks) {
-  const int64_t need = had_groups(logb, nblocks, kChunkTiles);
-  if (kPersistentGroupsPerCU == 0) return (unsigned)need;
+// there are chunks -- except with a workspace, whose protocol needs the same
+// grid on every call.
+static unsigned persistent_groups(int logb, int64_t nblocks, bool fixed) {
   const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
+  if (fixed) return (unsigned)cap;
+  const int64_t need = had_groups(logb, nblocks, kChunkTiles);
   return (unsigned)(need < cap ? need : cap);
 }
 
 template <int LOGB>
 static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
-  const unsigned groups = persistent_groups(LOGB, a.nblocks);
+  const unsigned groups = persistent_groups(LOGB, a.nblocks, a.ws != nullptr);
   if (groups == 0) return hipSuccess;
   dim3 grid(groups), block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);

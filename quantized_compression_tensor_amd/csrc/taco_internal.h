@@ -101,8 +101,8 @@ constexpr int64_t kReducePiece = int64_t(1) << 28;
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
-// Workgroups per CU for the persistent kernels (4 waves each); 0 = one
-// workgroup per four tiles of work (no grid-stride reuse).
+// Workgroups per CU for the persistent kernels (4 waves each); for the
+// reduce, 0 = one workgroup per four tiles of work (no grid-stride reuse).
 #ifndef TACO_GROUPS_PER_CU
 #define TACO_GROUPS_PER_CU 4
 #endif
@@ -110,6 +110,7 @@ int device_cu_count();
 #define TACO_REDUCE_GROUPS_PER_CU 4
 #endif
 constexpr int kPersistentGroupsPerCU = TACO_GROUPS_PER_CU;
+static_assert(kPersistentGroupsPerCU > 0, "persistent kernels need at least one workgroup per CU");
 constexpr int kReduceGroupsPerCU = TACO_REDUCE_GROUPS_PER_CU;
 
 hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s);
