@@ -35,7 +35,7 @@ MALL_BYTES = 256 << 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt-tp")
     ap.add_argument("--scale-mode", choices=["delayed", "auto", "given"], default="delayed",
@@ -388,41 +388,38 @@ def main():
 
         K = args.steps
         mk = lambda: torch.cuda.Event(enable_timing=True)
-        # timed region: K whole steps, one event pair per step (event records
-        # between kernels cost GPU time, so none inside a step)
-        ev_s = [(mk(), mk()) for _ in range(K)]
+        # timed region: K whole steps between one pair of events (an event
+        # record between kernels costs GPU time, so none inside the region)
+        ev0, ev1 = mk(), mk()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        ev0.record(stream)
         for i in range(K):
-            ev_s[i][0].record(stream)
             step(i % nsets)
-            ev_s[i][1].record(stream)
+        ev1.record(stream)
         host = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
         # per-kernel launch durations (roofline): the same launches again, each
-        # between its own pair of events on the launch stream
-        ev_c, ev_r = [], []
+        # kernel's K steps' worth back to back between one pair of events on the
+        # launch stream; the average includes the short gap between dependent
+        # launches, so it is an upper bound on the kernel's own duration
+        a_c, b_c, a_r, b_r = mk(), mk(), mk(), mk()
+        a_c.record(stream)
         for i in range(K):
-            s = i % nsets
-            for r in range(w.shards):
-                a, b = mk(), mk()
-                a.record(stream)
-                compress_one(s, r)
-                b.record(stream)
-                ev_c.append((a, b))
-            a, b = mk(), mk()
-            a.record(stream)
-            reduce(s)
-            b.record(stream)
-            ev_r.append((a, b))
+            compress(i % nsets)
+        b_c.record(stream)
+        a_r.record(stream)
+        for i in range(K):
+            reduce(i % nsets)
+        b_r.record(stream)
         torch.cuda.synchronize()
 
-    t_comp = float(np.mean([a.elapsed_time(b) for a, b in ev_c]))   # ms per compress launch
-    t_red = float(np.mean([a.elapsed_time(b) for a, b in ev_r]))    # ms per reduce launch
+    t_comp = a_c.elapsed_time(b_c) / (K * w.shards)   # ms per compress launch
+    t_red = a_r.elapsed_time(b_r) / K                 # ms per reduce call
     ms_step = wall * 1e3 / K
-    gpu_ms_step = float(np.mean([a.elapsed_time(b) for a, b in ev_s]))
+    gpu_ms_step = ev0.elapsed_time(ev1) / K
     value = in_bytes / (ms_step * 1e-3) / 1e9
 
     b_comp, b_red = algorithmic_bytes(w)

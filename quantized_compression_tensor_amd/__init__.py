@@ -210,20 +210,26 @@ def regions(buf, c, rows, cols):
     return codes, sc, aux, ten
 
 
+WS_GROUPS = 16      # workspace counter groups (kernel-side constant)
+WS_LINE = 32        # uint32 words per 128-byte line
+
+
 def workspace_history(ws):
-    """Read an FP8 tensor-scale workspace (a device tensor, 16 KiB): returns
-    (calls recorded, abs-max recorded by the most recent call, that call's slot
-    index). Layout (uint32 words): [0] grid P of the last call; words 32 + 32 g:
-    ticket counter of group g (16 groups); words 544 + 512 s + 32 g: abs-max
-    accumulator (float bits) of slot s (3 slots), group g. Inspection only."""
+    """Read an FP8 tensor-scale workspace (a device tensor of
+    TACO_WORKSPACE_BYTES): returns (calls recorded, abs-max recorded by the most
+    recent call, that call's slot index). Layout (uint32 words, 32 per line):
+    line 0 word 0: grid P of the last call; line 1 + g: ticket counter of group
+    g (16 groups); line 17 + g, words 0-2: abs-max accumulators (float bits) of
+    group g in slots 0-2. Inspection only."""
     import numpy as np
     w = ws.detach().cpu().numpy().view(np.uint32).reshape(-1)
     grid = int(w[0])
     if grid == 0:
         return 0, 0.0, None
-    G = min(grid, 16)
+    G = min(grid, WS_GROUPS)
     members0 = -(-grid // G)
-    calls = int(w[32]) // members0
+    calls = int(w[WS_LINE]) // members0
     slot = (calls - 1) % 3
-    acc = w[544 + 512 * slot: 544 + 512 * (slot + 1)].reshape(16, 32)[:G, 0]
+    accl = w[WS_LINE * (1 + WS_GROUPS): WS_LINE * (1 + 2 * WS_GROUPS)].reshape(WS_GROUPS, WS_LINE)
+    acc = accl[:G, slot].copy()
     return calls, float(acc.view(np.float32).max()), slot

@@ -26,12 +26,16 @@ ARCH = "gfx950"
 # -ffp-contract=off: no fused multiply-adds except the explicit fmaf calls,
 # so every product and sum rounds once, as the codec definitions require.
 # Correctly rounded float32 division; float32 denormals kept.
-# Packed FP32 instructions are switched off.
+# Packed FP32 instructions are switched off. Atomics stay as written (every
+# one is issued by a single lane): the wave-aggregating rewrite would consume
+# an atomic's result right after issuing it, so the wave would wait for the
+# round trip before issuing the loads that follow.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

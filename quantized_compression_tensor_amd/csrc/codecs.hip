@@ -206,8 +206,7 @@ template <int FMT, int B>
 struct LaneIn {
   uint4 q;
   float s;      // INT scale, FP8 combined scale g * 2^-k
-  float zf;     // asymmetric zero point as float
-  uint32_t zi;  // asymmetric zero point
+  uint32_t z;   // asymmetric zero point
 };
 
 template <int FMT, int B>
@@ -221,33 +220,32 @@ TACO_DEV LaneIn<FMT, B> load_in(const uint8_t* codes, const void* scale, const u
   } else {
     r.q = *reinterpret_cast<const uint4*>(codes + e0);
   }
-  r.zi = 0;
+  r.z = 0;
   if constexpr (FMT == kFP8) {
     const int k = static_cast<const int8_t*>(scale)[blk];
     r.s = (*g_hdr) * pow2f(-k);
-    r.zf = 0.0f;
   } else {
     r.s = static_cast<const float*>(scale)[blk];
-    r.zi = (FMT == kINT8S) ? 0u : (uint32_t)zero[blk];
-    r.zf = (float)r.zi;
+    if constexpr (FMT == kINT4A || FMT == kINT8A) r.z = zero[blk];
   }
   return r;
 }
 
-// Byte b of w as a float (one v_cvt_f32_ubyte{b}).
+// Byte b of w as a float: unsigned (one v_cvt_f32_ubyte{b}) or signed (one
+// v_cvt_f32_i32 with a sign-extended byte operand).
 TACO_DEV float ubyte(uint32_t w, int b) { return (float)((w >> (8 * b)) & 0xFFu); }
+TACO_DEV float sbyte(uint32_t w, int b) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * b)); }
 
-// Dequantized values of one lane.
+// Dequantized values of one lane. Every result is the single rounding of the
+// exact product, for every finite scale:
 //  FP8:  dec(q) * (g * 2^-k); dec(q) * 2^-k is exact, so this is the single
 //        rounding of dec(q) * 2^-k * g.
-//  INT8 symmetric: RN(q * s). The bytes are biased to q + 128 (xor 0x80) and
-//        converted unsigned; fma(q + 128, s, -128 s) rounds the exact real
-//        (q + 128) s - 128 s = q s once (-128 s is an exact power-of-two
-//        multiple while s <= 2^120).
-//  INT4 asymmetric: RN((q - z) * s). q - z + 16 is formed on packed bytes
-//        (no carries: it lies in [1, 31]); fma(q - z + 16, s, -16 s) again
-//        rounds (q - z) s exactly once.
-//  INT8 asymmetric: RN((q - z) * s) with q - z formed in float (exact).
+//  INT8 symmetric: q * s, q converted from its signed byte (exact).
+//  INT4 asymmetric: (q - z) * s. For four codes at once the bytes
+//        ((q | 0x80) - z) ^ 0x80 are formed on a packed word: q + 128 - z lies
+//        in [113, 143], so no byte borrows from its neighbour, and the xor
+//        turns it into q - z as a signed byte, converted exactly.
+//  INT8 asymmetric: (q - z) * s with q - z formed in float (exact).
 template <int FMT, int B>
 TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
   if constexpr (FMT == kFP8) {
@@ -256,51 +254,33 @@ TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) d[i] = d[i] * in.s;
   } else if constexpr (FMT == kINT8S) {
-    const uint32_t w[4] = {in.q.x ^ 0x80808080u, in.q.y ^ 0x80808080u, in.q.z ^ 0x80808080u,
-                           in.q.w ^ 0x80808080u};
-    if (__builtin_expect(in.s <= 0x1p120f, 1)) {
-      const float bias = -128.0f * in.s;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) d[4 * j + b] = fmaf(ubyte(w[j], b), in.s, bias);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) d[4 * j + b] = (ubyte(w[j], b) - 128.0f) * in.s;
-    }
-  } else if constexpr (FMT == kINT8A) {
     const uint32_t w[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d[4 * j + b] = (ubyte(w[j], b) - in.zf) * in.s;
+      for (int b = 0; b < 4; ++b) d[4 * j + b] = sbyte(w[j], b) * in.s;
+  } else if constexpr (FMT == kINT8A) {
+    const uint32_t w[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
+    const float zf = (float)in.z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) d[4 * j + b] = (ubyte(w[j], b) - zf) * in.s;
   } else {
-    const uint32_t zrep = 0x10101010u - in.zi * 0x01010101u;   // 16 - z in every byte
+    // 128 - z in every byte (v_perm with selector 0 copies byte 0 of z into all four)
+    const uint32_t zrep = 0x80808080u - __builtin_amdgcn_perm(in.z, in.z, 0u);
     uint32_t t[4];
-    t[0] = (in.q.x & 0x0F0F0F0Fu) + zrep;          // elements 0, 2, 4, 6
-    t[1] = ((in.q.x >> 4) & 0x0F0F0F0Fu) + zrep;   // elements 1, 3, 5, 7
-    t[2] = (in.q.y & 0x0F0F0F0Fu) + zrep;
-    t[3] = ((in.q.y >> 4) & 0x0F0F0F0Fu) + zrep;
-    if (__builtin_expect(in.s <= 0x1p120f, 1)) {
-      const float bias = -16.0f * in.s;
+    t[0] = ((in.q.x & 0x0F0F0F0Fu) + zrep) ^ 0x80808080u;          // elements 0, 2, 4, 6
+    t[1] = (((in.q.x >> 4) & 0x0F0F0F0Fu) + zrep) ^ 0x80808080u;   // elements 1, 3, 5, 7
+    t[2] = ((in.q.y & 0x0F0F0F0Fu) + zrep) ^ 0x80808080u;
+    t[3] = (((in.q.y >> 4) & 0x0F0F0F0Fu) + zrep) ^ 0x80808080u;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          d[8 * j + 2 * b] = fmaf(ubyte(t[2 * j], b), in.s, bias);
-          d[8 * j + 2 * b + 1] = fmaf(ubyte(t[2 * j + 1], b), in.s, bias);
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          d[8 * j + 2 * b] = (ubyte(t[2 * j], b) - 16.0f) * in.s;
-          d[8 * j + 2 * b + 1] = (ubyte(t[2 * j + 1], b) - 16.0f) * in.s;
-        }
-    }
+      for (int b = 0; b < 4; ++b) {
+        d[8 * j + 2 * b] = sbyte(t[2 * j], b) * in.s;
+        d[8 * j + 2 * b + 1] = sbyte(t[2 * j + 1], b) * in.s;
+      }
   }
 }
 
@@ -326,18 +306,26 @@ template <int FMT, int B, bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   __shared__ float lds4[4];
   __shared__ uint32_t lds_t;
+  __shared__ float lds_g;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t ntiles = (a.n + kWaveElems - 1) / kWaveElems;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float inv_g = 0.0f;
   uint32_t t = 0;
   if constexpr (FMT == kFP8) {
+    float g = a.g;
     if (a.ws != nullptr) {
-      if (threadIdx.x == 0) lds_t = ws_ticket(a.ws);
-      __syncthreads();
+      if (wave_in_group() == 0) {
+        const WsStart st = ws_begin(a.ws, a.g_from_ws != 0);
+        const uint32_t tt = ws_call(__builtin_amdgcn_readfirstlane(st.ticket));
+        float gg = a.g;
+        if (a.g_from_ws) gg = tensor_scale_from_amax(ws_prev_amax(st.hist, tt));
+        if (lane == 0) { lds_t = tt; lds_g = gg; }
+      }
+      lds_barrier();
       t = lds_t;
+      if (a.g_from_ws) g = lds_g;
     }
-    const float g = a.g_from_ws ? tensor_scale_from_amax(ws_prev_amax(a.ws, t)) : a.g;
     inv_g = 1.0f / g;
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.g_hdr = g;
   }
@@ -378,7 +366,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_amax(const void* x, int64_t n
   __shared__ float lds4[4];
   __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
-  if (threadIdx.x == 0) lds_t = ws_ticket(ws);
+  if (threadIdx.x == 0) lds_t = ws_call(ws_ticket(ws));
   const int64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float m = 0.0f;
@@ -431,31 +419,40 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
 // Decompress N shards, sum in float32 in shard order, then optionally store
 // the sum and/or re-quantize it (FP8: g' = g_0 + ... + g_{N-1}, clamped).
 //
-// Persistent grid over 1024-element wave tiles. All NMAX shard slots are read
+// Persistent grid over 1024-element wave tiles. A wave walks a flat sequence
+// of steps -- (tile, group of up to four shards), the groups of a tile in
+// shard order -- with two register sets used alternately: the loads of the
+// next step are issued before the current step is dequantized and added, so
+// one step's loads are always in flight. All NMAX shard slots are read
 // through buffer resources; slots r >= N get an empty resource, load zeros and
 // add an exact +0 (acc is never -0), so the instruction stream is the same for
-// every N <= NMAX and the compiler can wait for exactly the loads it needs.
-// A launch covers at most kReducePiece elements (the host splits larger
-// tensors), so every byte offset fits 32 bits.
+// every N <= NMAX. Steps past the last tile load nothing (their offsets lie
+// outside every resource). A launch covers at most kReducePiece elements (the
+// host splits larger tensors), so every byte offset fits 32 bits.
+// Two resources per shard: the codes, and the block metadata -- the scales,
+// followed (asymmetric formats) by the zero points a.zero_rel bytes after the
+// first scale byte, the same distance in every shard.
 template <int FMT, int B>
 struct ShardRsrc {
-  rsrc_t codes, scale, zero, g;
+  rsrc_t codes, meta;
 };
 
+// n <= kReducePiece, so every size below is under 2^31.
 template <int FMT, int B>
-TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int64_t n) {
+TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int n) {
   const bool live = r < a.nshards;
-  const int64_t nb = n / B;
+  const int nb = n / B;
+  constexpr bool ASYM = FMT == kINT4A || FMT == kINT8A;
   ShardRsrc<FMT, B> s;
-  s.codes = make_rsrc(a.in.codes[r], live ? (FMT == kINT4A ? n / 2 : n) : 0);
-  s.scale = make_rsrc(a.in.scale[r], live ? (FMT == kFP8 ? nb : 4 * nb) : 0);
-  s.zero = make_rsrc(a.in.zero[r], live && (FMT == kINT4A || FMT == kINT8A) ? nb : 0);
-  s.g = make_rsrc(a.in.g[r], live && FMT == kFP8 ? 4 : 0);
+  s.codes = make_rsrc32(a.in.codes[r], live ? (FMT == kINT4A ? n / 2 : n) : 0);
+  s.meta = make_rsrc32(a.in.scale[r], live ? (FMT == kFP8 ? (nb + 3) & ~3 : (ASYM ? a.zero_rel + nb : 4 * nb)) : 0);
   return s;
 }
 
+// One lane's codes and block metadata of one shard. FP8: g is the shard's
+// tensor scale (0 for an empty slot).
 template <int FMT, int B>
-TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0) {
+TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, float g, int zero_rel) {
   LaneIn<FMT, B> r;
   const int blk = e0 / B;
   if constexpr (FMT == kINT4A) {
@@ -464,26 +461,67 @@ TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0) {
   } else {
     r.q = bload128<kNT>(s.codes, e0, 0);
   }
-  r.zi = 0;
+  r.z = 0;
   if constexpr (FMT == kFP8) {
-    const int k = (int)(int8_t)bload8(s.scale, blk, 0);
-    r.s = __uint_as_float(bload32(s.g, 0, 0)) * pow2f(-k);
-    r.zf = 0.0f;
+    // the aligned dword holding the exponent byte (the resource is rounded up
+    // to whole dwords, inside the region's padding)
+    const uint32_t w = bload32(s.meta, blk & ~3, 0);
+    const int k = (int)(int8_t)(uint8_t)(w >> (8 * (blk & 3)));
+    r.s = g * pow2f(-k);
   } else {
-    r.s = __uint_as_float(bload32(s.scale, blk * 4, 0));
-    r.zi = (FMT == kINT8S) ? 0u : bload8(s.zero, blk, 0);
-    r.zf = (float)r.zi;
+    r.s = __uint_as_float(bload32(s.meta, blk * 4, 0));
+    if constexpr (FMT == kINT4A || FMT == kINT8A) r.z = bload8(s.meta, blk, zero_rel);
   }
   return r;
 }
 
+template <int FIN, int BIN, int NMAX>
+struct ReduceGroup {
+  static constexpr int GRP = NMAX < 8 ? NMAX / 2 : 4;   // shards per step
+  static constexpr int NG = NMAX / GRP;                 // steps per tile (>= 2)
+  LaneIn<FIN, BIN> in[GRP];
+
+  // Issue the loads of shard group `grp` of the tile at element e0. glane:
+  // lane r holds shard r's FP8 tensor scale.
+  TACO_DEV void load(const ReduceArgs& a, int grp, int e0, int n, float glane) {
+#pragma unroll
+    for (int u = 0; u < GRP; ++u) {
+      const int r = grp * GRP + u;
+      float g = 0.0f;
+      if constexpr (FIN == kFP8) g = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), r));
+      in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r, n), e0, g, a.zero_rel);
+    }
+  }
+
+  TACO_DEV void add_to(float* acc) const {
+#pragma unroll
+    for (int u = 0; u < GRP; ++u) {
+      float d[16];
+      dequant_lane<FIN, BIN>(in[u], d);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
+    }
+  }
+};
+
 template <int FIN, int BIN, int FOUT, int BOUT, int NMAX>
 __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
+  using RG = ReduceGroup<FIN, BIN, NMAX>;
+  constexpr int NG = RG::NG;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t n = a.n;
-  const int ntiles = (int)((n + kWaveElems - 1) / kWaveElems);
+  const int n = (int)a.n;   // <= kReducePiece
+  const int ntiles = (n + kWaveElems - 1) / kWaveElems;
   const int stride = (int)gridDim.x * (kBlockThreads / kWave);
   const bool rq = a.rq_codes != nullptr;
+  float glane = 0.0f;
+  if constexpr (FIN == kFP8) {
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+      if (r < a.nshards) {
+        const float gr = *a.in.g[r];
+        if (lane == r) glane = gr;
+      }
+  }
   float inv_g = 0.0f;
   if constexpr (FOUT == kFP8) {
     if (rq) {
@@ -494,33 +532,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
       if (blockIdx.x == 0 && threadIdx.x == 0 && a.write_g) *a.rq_g_hdr = gs;
     }
   }
-  const int64_t nb_out = n / BOUT;
-  const rsrc_t r_sum = make_rsrc(a.sum, a.sum ? 4 * n : 0);
-  const rsrc_t r_qc = make_rsrc(a.rq_codes, rq ? n : 0);
-  const rsrc_t r_qs = make_rsrc(a.rq_scale, rq ? (FOUT == kFP8 ? nb_out : 4 * nb_out) : 0);
-  const rsrc_t r_qz = make_rsrc(a.rq_zero, rq && FOUT == kINT8A ? nb_out : 0);
+  const int nb_out = n / BOUT;
+  const rsrc_t r_sum = make_rsrc32(a.sum, a.sum ? 4 * n : 0);
+  const rsrc_t r_qc = make_rsrc32(a.rq_codes, rq ? n : 0);
+  const rsrc_t r_qs = make_rsrc32(a.rq_scale, rq ? (FOUT == kFP8 ? nb_out : 4 * nb_out) : 0);
+  const rsrc_t r_qz = make_rsrc32(a.rq_zero, rq && FOUT == kINT8A ? nb_out : 0);
 
-  for (int t = (int)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
+  // the finished sum of a tile: store it and/or re-quantize it
+  auto finish = [&](int t, float* acc) {
     const int e0 = t * kWaveElems + lane * kLaneElems;
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    // groups of four shards; the group loop is not unrolled so that only four
-    // shards' buffer resources are live at a time (no scalar-register spills)
-    constexpr int GRP = NMAX < 4 ? NMAX : 4;
-#pragma unroll 1
-    for (int r0 = 0; r0 < NMAX; r0 += GRP) {
-      LaneIn<FIN, BIN> in[GRP];
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r0 + u, n), e0);
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        float d[16];
-        dequant_lane<FIN, BIN>(in[u], d);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
-      }
-    }
     if (a.sum != nullptr) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -541,6 +561,32 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
         if constexpr (FOUT == kINT8A) bstore8((uint32_t)q.z, r_qz, blk, 0);
       }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  };
+
+  // One loop iteration covers one tile: its NG >= 2 shard groups, one step
+  // each. The two register sets alternate by step; the loads of step k + 1
+  // (the next group, or the first group of the wave's next tile) are issued,
+  // and kept ahead of the arithmetic by a scheduling barrier, before step k is
+  // added. The last iteration's look-ahead lies past the end: it loads zeros.
+  static_assert(NG >= 2 && NG % 2 == 0, "an even number of steps per tile");
+  int t = (int)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  RG buf[2];
+  buf[0].load(a, 0, t * kWaveElems + lane * kLaneElems, n, glane);
+  for (; t < ntiles; t += stride) {
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const int tn = k + 1 < NG ? t : t + stride;   // tile and group of step k + 1
+      const int gn = (k + 1) % NG;
+      buf[(k + 1) & 1].load(a, gn, tn * kWaveElems + lane * kLaneElems, n, glane);
+      __builtin_amdgcn_sched_barrier(0);
+      buf[k & 1].add_to(acc);
+    }
+    finish(t, acc);
   }
 }
 
@@ -633,11 +679,20 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Reduce grid. The FP8 and INT8-symmetric inputs are bound by memory: a
+// workgroup per 4 * kReduceTilesPerWave tiles, dispatched by the hardware as
+// CUs free up, keeps every CU streaming until the end. The asymmetric inputs
+// do several times more arithmetic per byte: a persistent grid of
+// kReduceGroupsPerCU workgroups per CU spreads each wave's setup over many
+// tiles.
 template <int FIN, int BIN, int FOUT, int BOUT, int NMAX>
 static void launch_r(const ReduceArgs& a, hipStream_t s) {
-  dim3 grid = grid_for(a.n), block(kBlockThreads);
+  constexpr bool ALU_BOUND = FIN == kINT4A || FIN == kINT8A;
+  const int64_t tiles = (a.n + kWaveElems - 1) / kWaveElems;
+  const int64_t per_group = 4 * (ALU_BOUND ? 1 : kReduceTilesPerWave);
+  dim3 grid((unsigned)((tiles + per_group - 1) / per_group)), block(kBlockThreads);
   const unsigned cap = (unsigned)(device_cu_count() * kReduceGroupsPerCU);
-  if (kReduceGroupsPerCU > 0 && grid.x > cap) grid.x = cap;
+  if (ALU_BOUND && grid.x > cap) grid.x = cap;
   hipLaunchKernelGGL((k_reduce<FIN, BIN, FOUT, BOUT, NMAX>), grid, block, 0, s, a);
 }
 
@@ -682,10 +737,18 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
     p.n = (a.n - e < kReducePiece) ? a.n - e : kReducePiece;
     p.write_g = (e == 0);
     const int64_t bi = e / a.bin, bo = e / a.bout;
+    p.zero_rel = 0;
     for (int r = 0; r < a.nshards; ++r) {
       p.in.codes[r] = a.in.codes[r] + code_bytes(a.fin, e);
       p.in.scale[r] = static_cast<const uint8_t*>(a.in.scale[r]) + scale_bytes(a.fin, bi);
       p.in.zero[r] = a.in.zero[r] + bi;
+      if (a.fin == kINT4A || a.fin == kINT8A) {
+        // the zero points follow the scales at one distance in every shard
+        const int64_t rel = p.in.zero[r] - static_cast<const uint8_t*>(p.in.scale[r]);
+        if (rel < 4 * (p.n / a.bin) || rel + p.n / a.bin > 0x7FFFFFF0 || (r > 0 && rel != p.zero_rel))
+          return hipErrorInvalidValue;
+        p.zero_rel = (int)rel;
+      }
     }
     if (a.sum) p.sum = a.sum + e;
     if (a.rq_codes) {

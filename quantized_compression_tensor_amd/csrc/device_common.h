@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "taco_internal.h"
+#include "taco.h"
 
 #define TACO_DEV __device__ __forceinline__
 
@@ -47,6 +48,10 @@ constexpr int kNT = 2;                   // non-temporal cache policy (read once
 TACO_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int nr = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, kRsrcFlags);
+}
+// The same for a size the caller knows lies in [0, 2^31).
+TACO_DEV rsrc_t make_rsrc32(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcFlags);
 }
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 template <int AUX = 0>
@@ -186,63 +191,111 @@ TACO_DEV float wave_max(float a) {
 // ------------------------------------------------------------- workspace --
 // Abs-max history of an FP8 tensor scale, in caller-owned memory that is
 // zero-filled once. Kernels that use it always run a fixed grid of P
-// workgroups (P = kPersistentGroupsPerCU * CUs) split into G = 16 groups.
+// workgroups (P = kPersistentGroupsPerCU * CUs) split into G groups
+// (workgroup b belongs to group b % G). Group g owns two 128-byte lines: its
+// ticket counter, and its abs-max accumulators of three slots (counters and
+// accumulators on separate lines, so the tickets taken at the start of a call
+// never contend with the history reads).
 //
 // At its start a workgroup takes a ticket from its group's counter (one
-// returning atomic add; each counter sits on its own 128-byte line). Every call
-// adds exactly `members` to each counter, so ticket / members is the same call
-// index t in every workgroup of a call. Call t
+// returning atomic add). Every call adds exactly `members` to each counter, so
+// ticket / members is the same call index t in every workgroup of a call.
+// Call t
 //   * reads the previous call's maxima from slot (t + 2) % 3,
 //   * folds its own workgroup maxima into slot t % 3 (atomic max, not awaited),
 //   * zeroes slot (t + 1) % 3 for the next call (workgroup 0).
 // No slot is read and written by the same call, and the kernel boundary orders
-// calls, so no fence and no "last workgroup" chain is needed.
-constexpr int kPubGroups = 16;
+// calls, so the history is read with plain loads and no fence or "last
+// workgroup" chain is needed. Only the first wave of a workgroup touches the
+// workspace; it hands the call index (and the tensor scale) to the others
+// through LDS.
+#ifndef TACO_WS_GROUPS
+#define TACO_WS_GROUPS 16
+#endif
+constexpr int kPubGroups = TACO_WS_GROUPS;
 constexpr int kLineWords = 32;
+static_assert(kPubGroups <= kWave, "one lane per group");
 
+struct WsAcc {
+  uint32_t slot[3];                              // abs-max accumulators (float bits)
+  uint32_t pad[kLineWords - 3];
+};
 struct Workspace {
   uint32_t grid;                                 // P of the most recent call
   uint32_t pad0[kLineWords - 1];
   uint32_t calls[kPubGroups][kLineWords];        // ticket counters
-  uint32_t acc[3][kPubGroups][kLineWords];       // abs-max accumulators (float bits)
+  WsAcc acc[kPubGroups];
 };
-static_assert(sizeof(Workspace) <= 16384, "workspace size");
+static_assert(sizeof(Workspace) <= TACO_WORKSPACE_BYTES, "workspace size");
 
 #define TACO_AT_MAX(p, v) __hip_atomic_fetch_max((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_ADD(p, v) __hip_atomic_fetch_add((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_STORE(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-#define TACO_AT_LOAD(p) __hip_atomic_load((p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 
 TACO_DEV uint32_t ws_groups(uint32_t grid) { return grid < (uint32_t)kPubGroups ? grid : (uint32_t)kPubGroups; }
 
-// Call index of this launch (thread 0 of each workgroup).
+// This workgroup's ticket: the counter value before its add (one lane).
 TACO_DEV uint32_t ws_ticket(Workspace* ws) {
+  const uint32_t g = blockIdx.x % ws_groups(gridDim.x);
+  return TACO_AT_ADD(&ws->calls[g][0], 1u);
+}
+TACO_DEV uint32_t ws_call(uint32_t ticket) {
   const uint32_t G = ws_groups(gridDim.x);
   const uint32_t g = blockIdx.x % G;
   const uint32_t members = (gridDim.x - g + G - 1) / G;
-  return TACO_AT_ADD(&ws->calls[g][0], 1u) / members;
+  return ticket / members;
 }
 
-// Abs-max recorded by the previous call (any wave; the result is wave-uniform).
-TACO_DEV float ws_prev_amax(Workspace* ws, uint32_t t) {
+// Accumulators of group `lane` (lanes below G; zeros elsewhere), slots 0-2 in
+// x, y, z.
+TACO_DEV uint4 ws_history_lanes(const Workspace* ws) {
   const int lane = threadIdx.x & (kWave - 1);
+  uint4 h = make_uint4(0, 0, 0, 0);
+  if (lane < (int)ws_groups(gridDim.x)) h = *reinterpret_cast<const uint4*>(&ws->acc[lane]);
+  return h;
+}
+
+// Abs-max recorded by call t - 1, from the lanes of ws_history_lanes (the
+// result is wave-uniform).
+TACO_DEV float ws_prev_amax(uint4 h, uint32_t t) {
   const uint32_t slot = (t + 2) % 3;
-  float v = 0.0f;
-  if (lane < kPubGroups) v = __uint_as_float(TACO_AT_LOAD(&ws->acc[slot][lane][0]));
-  v = group_max<16>(v);   // lanes 0-15 now all hold the max
-  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+  const float v = __uint_as_float(slot == 0 ? h.x : (slot == 1 ? h.y : h.z));
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(v))));
 }
 
 // Fold this workgroup's max into call t's slot; workgroup 0 clears the next
-// slot. Called by every thread of wave 0 (lanes beyond the first do nothing).
+// slot. Called by every thread of the first wave.
 TACO_DEV void ws_record(Workspace* ws, uint32_t t, float wg_max) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t G = ws_groups(gridDim.x);
-  if (lane == 0) TACO_AT_MAX(&ws->acc[t % 3][blockIdx.x % G][0], __float_as_uint(wg_max));
+  if (lane == 0) TACO_AT_MAX(&ws->acc[blockIdx.x % G].slot[t % 3], __float_as_uint(wg_max));
   if (blockIdx.x == 0) {
-    if (lane < kPubGroups) TACO_AT_STORE(&ws->acc[(t + 1) % 3][lane][0], 0u);
+    if (lane < (int)G) TACO_AT_STORE(&ws->acc[lane].slot[(t + 1) % 3], 0u);
     if (lane == 0) TACO_AT_STORE(&ws->grid, gridDim.x);
   }
+}
+
+// Start of a call (first wave only, all its lanes): the call index and, when
+// `history`, the tensor scale from the previous call's abs-max. The ticket and
+// the history are requested here; the caller issues its first loads before
+// calling ws_finish_start, so those stay in flight while the ticket returns.
+struct WsStart {
+  uint32_t ticket;
+  uint4 hist;
+};
+TACO_DEV WsStart ws_begin(Workspace* ws, bool history) {
+  WsStart s{0u, make_uint4(0, 0, 0, 0)};
+  if ((threadIdx.x & (kWave - 1)) == 0) s.ticket = ws_ticket(ws);
+  if (history) s.hist = ws_history_lanes(ws);
+  return s;
+}
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads it does not
+// make every wave wait for its outstanding global loads and stores first.
+TACO_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Workgroup max of a non-negative float through LDS (all threads call it).
@@ -250,7 +303,7 @@ TACO_DEV float block_max(float a, float* lds4) {
   a = wave_max(a);
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) lds4[wave] = a;
-  __syncthreads();
+  lds_barrier();
   float r = fmaxf(fmaxf(lds4[0], lds4[1]), fmaxf(lds4[2], lds4[3]));
   return r;
 }

@@ -137,8 +137,9 @@ TACO_DEV void widen8(uint4 w, float* v) {
 // workspace the kernel also records this tensor's abs-max for the next call.
 //
 // Persistent grid: each wave walks chunks of T consecutive wave tiles
-// (T * 512 elements) with a stride of the whole grid, loading the next chunk
-// while it transforms the current one (two register sets, used alternately).
+// (T * 512 elements) with a stride of the whole grid, loading the chunk after
+// next while it transforms the current one (two register sets, used
+// alternately, so one chunk is always in flight).
 // All accesses go through buffer resources rebased per chunk, so the ragged
 // last chunk reads zeros and drops its out-of-range stores.
 #ifndef TACO_CHUNK_TILES
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   using CH = HadChunk<LOGB>;
   __shared__ float lds4[4];
   __shared__ uint32_t lds_t;
+  __shared__ float lds_g;
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
   const int row = lane / Gm::G;
@@ -219,27 +221,43 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
 
+  // With a workspace the first wave requests the ticket and the abs-max
+  // history first, then every wave its first two chunks. Loads complete in
+  // issue order, so waiting for the ticket never waits for the chunks, and the
+  // barrier that hands the call index and tensor scale to the other waves
+  // orders LDS only.
+  const bool wave0 = wave_in_group() == 0;
+  WsStart st{0u, make_uint4(0, 0, 0, 0)};
+  if (ws != nullptr && wave0) st = ws_begin(ws, GFROM_WS);
+  __builtin_amdgcn_sched_barrier(0);
   uint4 ra[CH::T], rb[CH::T];
-  CH::load(x, c, elems, ls.elem_off, ra);   // first chunk in flight during the ticket
-
+  CH::load(x, c, elems, ls.elem_off, ra);
+  CH::load(x, c + stride, elems, ls.elem_off, rb);
+  __builtin_amdgcn_sched_barrier(0);
+  float g = g_arg;
   uint32_t t = 0;
   if (ws != nullptr) {
-    if (threadIdx.x == 0) lds_t = ws_ticket(ws);
-    __syncthreads();
+    if (wave0) {
+      const uint32_t tt = ws_call(__builtin_amdgcn_readfirstlane(st.ticket));
+      float gg = g_arg;
+      if constexpr (GFROM_WS) gg = tensor_scale_from_amax(ws_prev_amax(st.hist, tt));
+      if (lane == 0) { lds_t = tt; lds_g = gg; }
+    }
+    lds_barrier();
     t = lds_t;
+    if constexpr (GFROM_WS) g = lds_g;
   }
-  const float g = GFROM_WS ? tensor_scale_from_amax(ws_prev_amax(ws, t)) : g_arg;
   const float inv_g = 1.0f / g;
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
 
   float run_max = 0.0f;
   while (c < nchunks) {
-    CH::load(x, c + stride, elems, ls.elem_off, rb);
     had_compress_chunk<LOGB, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+    CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
     c += stride;
     if (c >= nchunks) break;
-    CH::load(x, c + stride, elems, ls.elem_off, ra);
     had_compress_chunk<LOGB, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+    CH::load(x, c + 2 * stride, elems, ls.elem_off, rb);
     c += stride;
   }
   if (ws != nullptr) {
@@ -258,7 +276,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
   __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
-  if (threadIdx.x == 0) lds_t = ws_ticket(ws);
+  if (threadIdx.x == 0) lds_t = ws_call(ws_ticket(ws));
   const int64_t elems = nblocks << LOGB;
   const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);

@@ -93,16 +93,18 @@ struct ReduceArgs {
   uint8_t* rq_zero;
   float* rq_g_hdr;
   bool write_g;         // this launch writes the requantized tensor scale
+  int zero_rel;         // asymmetric input: bytes from a shard's first scale to its first zero point
 };
 
 // Largest number of elements one reduce launch covers (keeps every buffer
 // offset, including the float32 sum's, below 2^31 bytes).
 constexpr int64_t kReducePiece = int64_t(1) << 28;
+static_assert(4 * kReducePiece < (int64_t(1) << 31), "a piece's float32 sum must be addressable with 32-bit offsets");
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
-// Workgroups per CU for the persistent kernels (4 waves each); for the
-// reduce, 0 = one workgroup per four tiles of work (no grid-stride reuse).
+// Workgroups per CU for the persistent kernels (4 waves each) and for the
+// reduce of the asymmetric formats.
 #ifndef TACO_GROUPS_PER_CU
 #define TACO_GROUPS_PER_CU 4
 #endif
@@ -112,6 +114,13 @@ int device_cu_count();
 constexpr int kPersistentGroupsPerCU = TACO_GROUPS_PER_CU;
 static_assert(kPersistentGroupsPerCU > 0, "persistent kernels need at least one workgroup per CU");
 constexpr int kReduceGroupsPerCU = TACO_REDUCE_GROUPS_PER_CU;
+static_assert(kReduceGroupsPerCU > 0, "reduce workgroups per CU");
+// Tiles per wave of the memory-bound reduce (one workgroup per 4 * this many).
+#ifndef TACO_REDUCE_TILES_PER_WAVE
+#define TACO_REDUCE_TILES_PER_WAVE 2
+#endif
+constexpr int kReduceTilesPerWave = TACO_REDUCE_TILES_PER_WAVE;
+static_assert(kReduceTilesPerWave > 0, "tiles per wave");
 
 hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s);
 hipError_t launch_fp8_had_decode(const FP8HadDecodeArgs& a, hipStream_t s);
