@@ -210,26 +210,33 @@ def regions(buf, c, rows, cols):
     return codes, sc, aux, ten
 
 
-WS_GROUPS = 16      # workspace counter groups (kernel-side constant)
-WS_LINE = 32        # uint32 words per 128-byte line
+WS_TICKET_GROUPS = 16   # workspace ticket counters (kernel-side constants)
+WS_ACC_LINES = 64       # workspace abs-max accumulator lines
+WS_LINE = 32            # uint32 words per 128-byte line
 
 
 def workspace_history(ws):
     """Read an FP8 tensor-scale workspace (a device tensor of
     TACO_WORKSPACE_BYTES): returns (calls recorded, abs-max recorded by the most
     recent call, that call's slot index). Layout (uint32 words, 32 per line):
-    line 0 word 0: grid P of the last call; line 1 + g: ticket counter of group
-    g (16 groups); line 17 + g, words 0-2: abs-max accumulators (float bits) of
-    group g in slots 0-2. Inspection only."""
+    line 0 word 0: grid P of the last call; line 1 + g: ticket counter g (16);
+    line 17 + l, words 0-2: abs-max accumulator line l (64) in slots 0-2.
+    Inspection only."""
     import numpy as np
     w = ws.detach().cpu().numpy().view(np.uint32).reshape(-1)
     grid = int(w[0])
     if grid == 0:
         return 0, 0.0, None
-    G = min(grid, WS_GROUPS)
+    G = min(grid, WS_TICKET_GROUPS)
     members0 = -(-grid // G)
     calls = int(w[WS_LINE]) // members0
     slot = (calls - 1) % 3
-    accl = w[WS_LINE * (1 + WS_GROUPS): WS_LINE * (1 + 2 * WS_GROUPS)].reshape(WS_GROUPS, WS_LINE)
-    acc = accl[:G, slot].copy()
+    accl = acc_lines(w)
+    acc = accl[:, slot].copy()
     return calls, float(acc.view(np.float32).max()), slot
+
+
+def acc_lines(words):
+    """The accumulator lines of a workspace given as uint32 words: [64, 32]."""
+    base = WS_LINE * (1 + WS_TICKET_GROUPS)
+    return words[base: base + WS_LINE * WS_ACC_LINES].reshape(WS_ACC_LINES, WS_LINE)

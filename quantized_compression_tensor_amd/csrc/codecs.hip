@@ -304,7 +304,6 @@ struct QuantK {
 // one the workspace protocol needs.
 template <int FMT, int B, bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
-  __shared__ float lds4[4];
   __shared__ uint32_t lds_t;
   __shared__ float lds_g;
   const int lane = threadIdx.x & (kWave - 1);
@@ -353,17 +352,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
     }
   }
   if constexpr (FMT == kFP8) {
-    if (a.ws != nullptr) {
-      const float wg = block_max(run_max, lds4);
-      if (wave_in_group() == 0) ws_record(a.ws, t, wg);
-    }
+    if (a.ws != nullptr) ws_record_wave(a.ws, t, run_max);
   }
 }
 
 // Abs-max pre-pass (FP8 without transform, data-driven tensor scale).
 template <bool F32IN>
 __global__ __launch_bounds__(kBlockThreads) void k_amax(const void* x, int64_t n, Workspace* ws) {
-  __shared__ float lds4[4];
   __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
   if (threadIdx.x == 0) lds_t = ws_call(ws_ticket(ws));
@@ -379,8 +374,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_amax(const void* x, int64_t n
       m = fmaxf(m, absmax16(v));
     }
   }
-  const float wg = block_max(m, lds4);   // its barrier also publishes lds_t
-  if (wave_in_group() == 0) ws_record(ws, lds_t, wg);
+  lds_barrier();   // publishes lds_t
+  ws_record_wave(ws, lds_t, m);
 }
 
 struct DequantK {

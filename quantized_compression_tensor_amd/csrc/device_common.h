@@ -191,30 +191,28 @@ TACO_DEV float wave_max(float a) {
 // ------------------------------------------------------------- workspace --
 // Abs-max history of an FP8 tensor scale, in caller-owned memory that is
 // zero-filled once. Kernels that use it always run a fixed grid of P
-// workgroups (P = kPersistentGroupsPerCU * CUs) split into G groups
-// (workgroup b belongs to group b % G). Group g owns two 128-byte lines: its
-// ticket counter, and its abs-max accumulators of three slots (counters and
-// accumulators on separate lines, so the tickets taken at the start of a call
-// never contend with the history reads).
+// workgroups (P = kPersistentGroupsPerCU * CUs). Workgroup b takes its tickets
+// from counter b % 16; wave w of workgroup b records into accumulator line
+// (4 b + w) % 64, which holds that line's abs-max in each of three slots.
+// Every counter and accumulator line is a 128-byte line of its own, so the
+// tickets taken at the start of a call never contend with the history reads.
 //
-// At its start a workgroup takes a ticket from its group's counter (one
-// returning atomic add). Every call adds exactly `members` to each counter, so
+// At its start a workgroup takes a ticket from its counter (one returning
+// atomic add). Every call adds exactly `members` to each counter, so
 // ticket / members is the same call index t in every workgroup of a call.
 // Call t
 //   * reads the previous call's maxima from slot (t + 2) % 3,
-//   * folds its own workgroup maxima into slot t % 3 (atomic max, not awaited),
-//   * zeroes slot (t + 1) % 3 for the next call (workgroup 0).
+//   * folds each wave's maximum into slot t % 3 (atomic max, not awaited),
+//   * zeroes slot (t + 1) % 3 for the next call (first wave of workgroup 0).
 // No slot is read and written by the same call, and the kernel boundary orders
 // calls, so the history is read with plain loads and no fence or "last
-// workgroup" chain is needed. Only the first wave of a workgroup touches the
-// workspace; it hands the call index (and the tensor scale) to the others
-// through LDS.
-#ifndef TACO_WS_GROUPS
-#define TACO_WS_GROUPS 16
-#endif
-constexpr int kPubGroups = TACO_WS_GROUPS;
+// workgroup" chain is needed. Only the first wave of a workgroup takes the
+// ticket and reads the history; it hands the call index (and the tensor scale)
+// to the others through LDS.
+constexpr int kTicketGroups = 16;
+constexpr int kAccLines = 64;
 constexpr int kLineWords = 32;
-static_assert(kPubGroups <= kWave, "one lane per group");
+static_assert(kAccLines <= kWave, "one lane per accumulator line");
 
 struct WsAcc {
   uint32_t slot[3];                              // abs-max accumulators (float bits)
@@ -223,8 +221,8 @@ struct WsAcc {
 struct Workspace {
   uint32_t grid;                                 // P of the most recent call
   uint32_t pad0[kLineWords - 1];
-  uint32_t calls[kPubGroups][kLineWords];        // ticket counters
-  WsAcc acc[kPubGroups];
+  uint32_t calls[kTicketGroups][kLineWords];     // ticket counters
+  WsAcc acc[kAccLines];
 };
 static_assert(sizeof(Workspace) <= TACO_WORKSPACE_BYTES, "workspace size");
 
@@ -232,26 +230,27 @@ static_assert(sizeof(Workspace) <= TACO_WORKSPACE_BYTES, "workspace size");
 #define TACO_AT_ADD(p, v) __hip_atomic_fetch_add((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_STORE(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 
-TACO_DEV uint32_t ws_groups(uint32_t grid) { return grid < (uint32_t)kPubGroups ? grid : (uint32_t)kPubGroups; }
+TACO_DEV uint32_t ws_ticket_groups(uint32_t grid) {
+  return grid < (uint32_t)kTicketGroups ? grid : (uint32_t)kTicketGroups;
+}
 
 // This workgroup's ticket: the counter value before its add (one lane).
 TACO_DEV uint32_t ws_ticket(Workspace* ws) {
-  const uint32_t g = blockIdx.x % ws_groups(gridDim.x);
+  const uint32_t g = blockIdx.x % ws_ticket_groups(gridDim.x);
   return TACO_AT_ADD(&ws->calls[g][0], 1u);
 }
 TACO_DEV uint32_t ws_call(uint32_t ticket) {
-  const uint32_t G = ws_groups(gridDim.x);
+  const uint32_t G = ws_ticket_groups(gridDim.x);
   const uint32_t g = blockIdx.x % G;
   const uint32_t members = (gridDim.x - g + G - 1) / G;
   return ticket / members;
 }
 
-// Accumulators of group `lane` (lanes below G; zeros elsewhere), slots 0-2 in
-// x, y, z.
+// Accumulator line `lane` (slots 0-2 in x, y, z).
 TACO_DEV uint4 ws_history_lanes(const Workspace* ws) {
   const int lane = threadIdx.x & (kWave - 1);
   uint4 h = make_uint4(0, 0, 0, 0);
-  if (lane < (int)ws_groups(gridDim.x)) h = *reinterpret_cast<const uint4*>(&ws->acc[lane]);
+  if (lane < kAccLines) h = *reinterpret_cast<const uint4*>(&ws->acc[lane]);
   return h;
 }
 
@@ -263,22 +262,23 @@ TACO_DEV float ws_prev_amax(uint4 h, uint32_t t) {
   return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(v))));
 }
 
-// Fold this workgroup's max into call t's slot; workgroup 0 clears the next
-// slot. Called by every thread of the first wave.
-TACO_DEV void ws_record(Workspace* ws, uint32_t t, float wg_max) {
+// Fold this wave's max (any value per lane) into call t's slot; the first wave
+// of workgroup 0 also clears the next slot. Called by every lane of a wave.
+TACO_DEV void ws_record_wave(Workspace* ws, uint32_t t, float lane_max) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t G = ws_groups(gridDim.x);
-  if (lane == 0) TACO_AT_MAX(&ws->acc[blockIdx.x % G].slot[t % 3], __float_as_uint(wg_max));
-  if (blockIdx.x == 0) {
-    if (lane < (int)G) TACO_AT_STORE(&ws->acc[lane].slot[(t + 1) % 3], 0u);
+  const int wave = wave_in_group();
+  const float m = wave_max(lane_max);
+  const uint32_t line = (blockIdx.x * (kBlockThreads / kWave) + wave) % kAccLines;
+  if (lane == 0) TACO_AT_MAX(&ws->acc[line].slot[t % 3], __float_as_uint(m));
+  if (blockIdx.x == 0 && wave == 0) {
+    if (lane < kAccLines) TACO_AT_STORE(&ws->acc[lane].slot[(t + 1) % 3], 0u);
     if (lane == 0) TACO_AT_STORE(&ws->grid, gridDim.x);
   }
 }
 
-// Start of a call (first wave only, all its lanes): the call index and, when
-// `history`, the tensor scale from the previous call's abs-max. The ticket and
-// the history are requested here; the caller issues its first loads before
-// calling ws_finish_start, so those stay in flight while the ticket returns.
+// Start of a call (first wave only, all its lanes): the ticket and, when
+// `history`, the accumulator lines are requested; the caller issues its first
+// loads before it uses them, so those stay in flight while the ticket returns.
 struct WsStart {
   uint32_t ticket;
   uint4 hist;
@@ -298,14 +298,5 @@ TACO_DEV void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Workgroup max of a non-negative float through LDS (all threads call it).
-TACO_DEV float block_max(float a, float* lds4) {
-  a = wave_max(a);
-  const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) lds4[wave] = a;
-  lds_barrier();
-  float r = fmaxf(fmaxf(lds4[0], lds4[1]), fmaxf(lds4[2], lds4[3]));
-  return r;
-}
 
 }  // namespace taco

@@ -142,15 +142,15 @@ TACO_DEV void widen8(uint4 w, float* v) {
 // alternately, so one chunk is always in flight).
 // All accesses go through buffer resources rebased per chunk, so the ragged
 // last chunk reads zeros and drops its out-of-range stores.
-#ifndef TACO_CHUNK_TILES
-#define TACO_CHUNK_TILES 4
-#endif
-constexpr int kChunkTiles = TACO_CHUNK_TILES;
+// Chunk length in wave tiles: kChunkTiles, or kSmallChunkTiles when every
+// wave would otherwise get only a few chunks (then the arithmetic left after
+// the last loads land is what bounds the launch, and it scales with the chunk).
+constexpr int kChunkTiles = 4;
+constexpr int kSmallChunkTiles = 2;
 
-template <int LOGB>
+template <int LOGB, int T>
 struct HadChunk {
   using Gm = HadGeom<LOGB>;
-  static constexpr int T = kChunkTiles;
   static constexpr int64_t ELEMS = (int64_t)T * kTileElems;
 
   static TACO_DEV void load(const uint16_t* x, int64_t c, int64_t elems, int elem_off, uint4* raw) {
@@ -160,56 +160,80 @@ struct HadChunk {
   }
 };
 
-template <int LOGB, bool DEBUG>
-TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
-                                 float inv_g, uint8_t* codes, int8_t* kexp, float* dbg, float& run_max) {
+// The transform of one tile and its block abs-max (independent of the tensor
+// scale).
+template <int LOGB>
+TACO_DEV float had_transform_tile(uint4 raw, const LaneSigns<LOGB>& ls, float* v) {
   using Gm = HadGeom<LOGB>;
-  constexpr int T = kChunkTiles;
-  constexpr int64_t E = HadChunk<LOGB>::ELEMS;
-  const int64_t rem = elems - c * E;
-  const rsrc_t rc = make_rsrc(codes + c * E, rem);
-  const rsrc_t rk = make_rsrc(kexp + (c * E >> LOGB), rem >> LOGB);
+  widen8(raw, v);
+  fwht_in_lane(v);
+  fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+  return group_max<Gm::G>(absmax8(v));
+}
+
+// Scale, encode and store tile i of chunk c from its transformed values v and
+// block abs-max M.
+template <int LOGB, int T, bool DEBUG>
+TACO_DEV void had_encode_tile(float* v, float M, int i, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
+                              float inv_g, rsrc_t rc, rsrc_t rk, float* dbg) {
+  using Gm = HadGeom<LOGB>;
+  const float m = M * inv_g;
+  const int k = block_exponent(m);
+  const float cs = inv_g * pow2f(k) * ls.parity;
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    float v[8];
-    widen8(raw[i], v);
-    fwht_in_lane(v);
-    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
-    const float M = group_max<Gm::G>(absmax8(v));
-    run_max = fmaxf(run_max, M);
-    const float m = M * inv_g;
-    const int k = block_exponent(m);
-    const float cs = inv_g * pow2f(k) * ls.parity;
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], cs, 0.0f);
+  if (__builtin_expect(m * pow2f(k) > kE4M3Max, 0)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], cs, 0.0f);
-    if (__builtin_expect(m * pow2f(k) > kE4M3Max, 0)) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sat448(v[e]);
-    }
-    uint2 q;
-    q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
-    q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
-    bstore64(q, rc, ls.elem_off, i * kTileElems);
-    // every lane of the block writes the same exponent byte
-    bstore8((uint32_t)k, rk, row, i * Gm::BPT);
-    if constexpr (DEBUG) {
-      const rsrc_t rd = make_rsrc(dbg + c * E, rem * 4);
-      bstore128(make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                           __float_as_uint(v[3])), rd, ls.elem_off * 4, i * kTileElems * 4);
-      bstore128(make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                           __float_as_uint(v[7])), rd, ls.elem_off * 4 + 16, i * kTileElems * 4);
-    }
+    for (int e = 0; e < 8; ++e) v[e] = sat448(v[e]);
+  }
+  uint2 q;
+  q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
+  q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
+  bstore64(q, rc, ls.elem_off, i * kTileElems);
+  // every lane of the block writes the same exponent byte
+  bstore8((uint32_t)k, rk, row, i * Gm::BPT);
+  if constexpr (DEBUG) {
+    constexpr int64_t E = HadChunk<LOGB, T>::ELEMS;
+    const rsrc_t rd = make_rsrc(dbg + c * E, (elems - c * E) * 4);
+    bstore128(make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                         __float_as_uint(v[3])), rd, ls.elem_off * 4, i * kTileElems * 4);
+    bstore128(make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                         __float_as_uint(v[7])), rd, ls.elem_off * 4 + 16, i * kTileElems * 4);
   }
 }
 
-template <int LOGB, bool GFROM_WS, bool DEBUG>
+template <int LOGB, int T>
+struct ChunkOut {
+  rsrc_t rc, rk;
+  TACO_DEV ChunkOut(uint8_t* codes, int8_t* kexp, int64_t c, int64_t elems) {
+    constexpr int64_t E = HadChunk<LOGB, T>::ELEMS;
+    const int64_t rem = elems - c * E;
+    rc = make_rsrc(codes + c * E, rem);
+    rk = make_rsrc(kexp + (c * E >> LOGB), rem >> LOGB);
+  }
+};
+
+// Transform, scale, encode and store one chunk.
+template <int LOGB, int T, bool DEBUG>
+TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
+                                 float inv_g, uint8_t* codes, int8_t* kexp, float* dbg, float& run_max) {
+  const ChunkOut<LOGB, T> o(codes, kexp, c, elems);
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    float v[8];
+    const float M = had_transform_tile<LOGB>(raw[i], ls, v);
+    run_max = fmaxf(run_max, M);
+    had_encode_tile<LOGB, T, DEBUG>(v, M, i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
+  }
+}
+
+template <int LOGB, int T, bool GFROM_WS, bool DEBUG>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
     float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
     float* __restrict__ dbg) {
   using Gm = HadGeom<LOGB>;
-  using CH = HadChunk<LOGB>;
-  __shared__ float lds4[4];
+  using CH = HadChunk<LOGB, T>;
   __shared__ uint32_t lds_t;
   __shared__ float lds_g;
   const int lane = threadIdx.x & (kWave - 1);
@@ -230,13 +254,22 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   WsStart st{0u, make_uint4(0, 0, 0, 0)};
   if (ws != nullptr && wave0) st = ws_begin(ws, GFROM_WS);
   __builtin_amdgcn_sched_barrier(0);
-  uint4 ra[CH::T], rb[CH::T];
+  uint4 ra[T], rb[T];
   CH::load(x, c, elems, ls.elem_off, ra);
   CH::load(x, c + stride, elems, ls.elem_off, rb);
   __builtin_amdgcn_sched_barrier(0);
+  // With a workspace the first chunk is transformed while the ticket returns;
+  // only its scaling and encoding wait for the tensor scale.
+  float v0[T][8], M0[T];
+  float run_max = 0.0f;
   float g = g_arg;
   uint32_t t = 0;
   if (ws != nullptr) {
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      M0[i] = had_transform_tile<LOGB>(ra[i], ls, v0[i]);
+      run_max = fmaxf(run_max, M0[i]);
+    }
     if (wave0) {
       const uint32_t tt = ws_call(__builtin_amdgcn_readfirstlane(st.ticket));
       float gg = g_arg;
@@ -250,20 +283,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   const float inv_g = 1.0f / g;
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
 
-  float run_max = 0.0f;
-  while (c < nchunks) {
-    had_compress_chunk<LOGB, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+  if (c < nchunks) {
+    // first chunk (ra), then the chunks alternate between rb and ra
+    if (ws != nullptr) {
+      const ChunkOut<LOGB, T> o(codes, kexp, c, elems);
+#pragma unroll
+      for (int i = 0; i < T; ++i) had_encode_tile<LOGB, T, DEBUG>(v0[i], M0[i], i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
+    } else {
+      had_compress_chunk<LOGB, T, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+    }
     CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
     c += stride;
-    if (c >= nchunks) break;
-    had_compress_chunk<LOGB, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
-    CH::load(x, c + 2 * stride, elems, ls.elem_off, rb);
-    c += stride;
+    while (c < nchunks) {
+      had_compress_chunk<LOGB, T, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+      CH::load(x, c + 2 * stride, elems, ls.elem_off, rb);
+      c += stride;
+      if (c >= nchunks) break;
+      had_compress_chunk<LOGB, T, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+      CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
+      c += stride;
+    }
   }
-  if (ws != nullptr) {
-    const float wg = block_max(run_max, lds4);
-    if (wave_in_group() == 0) ws_record(ws, t, wg);
-  }
+  if (ws != nullptr) ws_record_wave(ws, t, run_max);
 }
 
 // Abs-max of the transformed tensor, recorded in the workspace.
@@ -271,8 +312,7 @@ template <int LOGB>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* __restrict__ x, int64_t nblocks,
                                                                 Workspace* __restrict__ ws) {
   using Gm = HadGeom<LOGB>;
-  using CH = HadChunk<LOGB>;
-  __shared__ float lds4[4];
+  using CH = HadChunk<LOGB, kChunkTiles>;
   __shared__ uint32_t lds_t;
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
@@ -282,10 +322,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float run_max = 0.0f;
   for (int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); c < nchunks; c += stride) {
-    uint4 raw[CH::T];
+    uint4 raw[kChunkTiles];
     CH::load(x, c, elems, ls.elem_off, raw);
 #pragma unroll
-    for (int i = 0; i < CH::T; ++i) {
+    for (int i = 0; i < kChunkTiles; ++i) {
       float v[8];
       widen8(raw[i], v);
       fwht_in_lane(v);
@@ -293,8 +333,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
       run_max = fmaxf(run_max, absmax8(v));
     }
   }
-  const float wg = block_max(run_max, lds4);   // its barrier also publishes lds_t
-  if (wave_in_group() == 0) ws_record(ws, lds_t, wg);
+  lds_barrier();   // publishes lds_t
+  ws_record_wave(ws, lds_t, run_max);
 }
 
 // --------------------------------------------------------------- decode --
@@ -368,35 +408,55 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
 // Persistent grid: enough workgroups to keep every CU busy, never more than
 // there are chunks -- except with a workspace, whose protocol needs the same
 // grid on every call.
-static unsigned persistent_groups(int logb, int64_t nblocks, bool fixed) {
+static unsigned persistent_groups(int logb, int64_t nblocks, int T, bool fixed) {
   const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
   if (fixed) return (unsigned)cap;
-  const int64_t need = had_groups(logb, nblocks, kChunkTiles);
+  const int64_t need = had_groups(logb, nblocks, T);
   return (unsigned)(need < cap ? need : cap);
+}
+
+template <int LOGB, int T>
+static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s) {
+  dim3 block(kBlockThreads);
+  auto* x = static_cast<const uint16_t*>(a.x);
+  auto* ws = static_cast<Workspace*>(a.ws);
+  if (a.g_from_ws)
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, true, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                       a.nblocks, a.g, ws, a.dbg);
+  else
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, false, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
+                       a.nblocks, a.g, ws, a.dbg);
 }
 
 template <int LOGB>
 static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
-  const unsigned groups = persistent_groups(LOGB, a.nblocks, a.ws != nullptr);
+  // fewer than four chunks of kChunkTiles per wave: the small chunks
+  const int64_t elems = a.nblocks << LOGB;
+  const int64_t chunks = (elems + kChunkTiles * kTileElems - 1) / (kChunkTiles * kTileElems);
+  const int64_t waves = (int64_t)device_cu_count() * kPersistentGroupsPerCU * (kBlockThreads / kWave);
+  const bool small = !a.dbg && chunks < 4 * waves;
+  const int T = small ? kSmallChunkTiles : kChunkTiles;
+  const unsigned groups = persistent_groups(LOGB, a.nblocks, T, a.ws != nullptr);
   if (groups == 0) return hipSuccess;
   dim3 grid(groups), block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
-  if (a.auto_prepass) hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), grid, block, 0, s, x, a.nblocks, ws);
-  if (a.g_from_ws) {
-    if (a.dbg)
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, true>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
-                         a.nblocks, a.g, ws, a.dbg);
+  if (a.auto_prepass) {
+    const unsigned pg = persistent_groups(LOGB, a.nblocks, kChunkTiles, true);
+    hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), dim3(pg), block, 0, s, x, a.nblocks, ws);
+  }
+  if (a.dbg) {
+    // test hook: always the large chunks
+    if (a.g_from_ws)
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, kChunkTiles, true, true>), grid, block, 0, s, x, a.codes, a.kexp,
+                         a.g_hdr, a.nblocks, a.g, ws, a.dbg);
     else
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, true, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
-                         a.nblocks, a.g, ws, a.dbg);
+      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, kChunkTiles, false, true>), grid, block, 0, s, x, a.codes, a.kexp,
+                         a.g_hdr, a.nblocks, a.g, ws, a.dbg);
+  } else if (small) {
+    launch_compress_t<LOGB, kSmallChunkTiles>(a, grid, s);
   } else {
-    if (a.dbg)
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, true>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
-                         a.nblocks, a.g, ws, a.dbg);
-    else
-      hipLaunchKernelGGL((k_fp8_had_compress<LOGB, false, false>), grid, block, 0, s, x, a.codes, a.kexp, a.g_hdr,
-                         a.nblocks, a.g, ws, a.dbg);
+    launch_compress_t<LOGB, kChunkTiles>(a, grid, s);
   }
   return hipGetLastError();
 }

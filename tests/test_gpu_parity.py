@@ -95,8 +95,7 @@ def test_compress_auto_scale_and_workspace(oc):
     assert np.float32(amax) == np.max(np.abs(y))          # recorded abs-max
     w = ws.cpu().numpy().view(np.uint32)
     nxt = (slot + 1) % 3
-    accl = w[T.WS_LINE * (1 + T.WS_GROUPS): T.WS_LINE * (1 + 2 * T.WS_GROUPS)].reshape(T.WS_GROUPS, T.WS_LINE)
-    assert (accl[:, nxt] == 0).all()                                   # next call's slot is clear
+    assert (T.acc_lines(w)[:, nxt] == 0).all()                         # next call's slot is clear
 
 
 def test_compress_delayed_scale_uses_previous_call():
