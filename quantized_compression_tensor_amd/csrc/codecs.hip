@@ -180,26 +180,6 @@ TACO_DEV LaneCodes quant_lane(float* a, float inv_g, float* pre) {
   else return quant_asym<8>(a, pre);
 }
 
-// Store one lane's codes; the first lane of each block stores the metadata.
-template <int FMT, int B>
-TACO_DEV void store_lane(const LaneCodes& r, int64_t e0, uint8_t* codes, void* scale, uint8_t* zero) {
-  constexpr int G = B / kLaneElems;
-  if constexpr (FMT == kINT4A) {
-    *reinterpret_cast<uint2*>(codes + e0 / 2) = make_uint2(r.q.x, r.q.y);
-  } else {
-    *reinterpret_cast<uint4*>(codes + e0) = r.q;
-  }
-  if (((threadIdx.x & (kWave - 1)) & (G - 1)) == 0) {
-    const int64_t blk = e0 / B;
-    if constexpr (FMT == kFP8) {
-      static_cast<int8_t*>(scale)[blk] = (int8_t)r.k;
-    } else {
-      static_cast<float*>(scale)[blk] = r.s;
-      if constexpr (FMT == kINT4A || FMT == kINT8A) zero[blk] = (uint8_t)r.z;
-    }
-  }
-}
-
 // ------------------------------------------------------- dequantization --
 
 template <int FMT, int B>
@@ -299,10 +279,34 @@ struct QuantK {
   float* dbg;
 };
 
-// Quantization without a transform. Grid-stride over 1024-element wave tiles;
-// with a workspace (FP8 tensor-scale history) the grid is the fixed persistent
-// one the workspace protocol needs.
-template <int FMT, int B, bool F32IN>
+// Store one lane's codes (streaming stores, as for the buffer stores); the
+// first lane of each block stores the metadata.
+template <int FMT, int B>
+TACO_DEV void store_lane(const LaneCodes& r, int64_t e0, uint8_t* codes, void* scale, uint8_t* zero) {
+  constexpr int G = B / kLaneElems;
+  if constexpr (FMT == kINT4A) {
+    u32x2 w = {r.q.x, r.q.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(codes + e0 / 2));
+  } else {
+    u32x4 w = {r.q.x, r.q.y, r.q.z, r.q.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(codes + e0));
+  }
+  if (((threadIdx.x & (kWave - 1)) & (G - 1)) == 0) {
+    const int64_t blk = e0 / B;
+    if constexpr (FMT == kFP8) {
+      static_cast<int8_t*>(scale)[blk] = (int8_t)r.k;
+    } else {
+      static_cast<float*>(scale)[blk] = r.s;
+      if constexpr (FMT == kINT4A || FMT == kINT8A) zero[blk] = (uint8_t)r.z;
+    }
+  }
+}
+
+// Quantization without a transform. Grid-stride over 1024-element wave tiles
+// (with 16 waves per CU in flight, no explicit prefetch: measured faster here
+// than a two-buffer pipeline); with a workspace (FP8 tensor-scale history) the
+// grid is the fixed persistent one the workspace protocol needs.
+template <int FMT, int B, bool F32IN, bool DEBUG>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   __shared__ uint32_t lds_t;
   __shared__ float lds_g;
@@ -341,10 +345,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
     }
     if constexpr (FMT == kFP8) run_max = fmaxf(run_max, absmax16(v));
     float pre[16];
-    LaneCodes r = quant_lane<FMT, B>(v, inv_g, a.dbg ? pre : nullptr);
+    LaneCodes r = quant_lane<FMT, B>(v, inv_g, DEBUG ? pre : nullptr);
     if (valid) {
       store_lane<FMT, B>(r, e0, a.codes, a.scale, a.zero);
-      if (a.dbg) {
+      if constexpr (DEBUG) {
         float4* d = reinterpret_cast<float4*>(a.dbg + e0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) d[q] = make_float4(pre[4 * q], pre[4 * q + 1], pre[4 * q + 2], pre[4 * q + 3]);
@@ -615,8 +619,13 @@ static dim3 quant_grid(const QuantArgs& a) {
 template <int FMT, int B>
 static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
   dim3 grid = quant_grid(a), block(kBlockThreads);
-  if (a.f32_in) hipLaunchKernelGGL((k_quantize<FMT, B, true>), grid, block, 0, s, k);
-  else hipLaunchKernelGGL((k_quantize<FMT, B, false>), grid, block, 0, s, k);
+  if (a.dbg) {
+    if (a.f32_in) hipLaunchKernelGGL((k_quantize<FMT, B, true, true>), grid, block, 0, s, k);
+    else hipLaunchKernelGGL((k_quantize<FMT, B, false, true>), grid, block, 0, s, k);
+  } else {
+    if (a.f32_in) hipLaunchKernelGGL((k_quantize<FMT, B, true, false>), grid, block, 0, s, k);
+    else hipLaunchKernelGGL((k_quantize<FMT, B, false, false>), grid, block, 0, s, k);
+  }
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {

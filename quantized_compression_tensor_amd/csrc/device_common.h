@@ -43,7 +43,7 @@ TACO_DEV uint4 ld16_nt(const void* p) {
 // also lets the compiler wait for exactly the loads it needs).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;   // gfx9-family raw buffer, 32-bit data format
-constexpr int kNT = 2;                   // non-temporal cache policy (read once)
+constexpr int kNT = 2;                   // non-temporal cache policy (streamed once)
 
 TACO_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int nr = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
@@ -66,15 +66,20 @@ TACO_DEV uint2 bload64(rsrc_t r, int voff, int soff) {
 }
 TACO_DEV uint32_t bload32(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0); }
 TACO_DEV uint32_t bload8(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0); }
+// Stores of the codes and scales are streaming (non-temporal): the compressed
+// tensors are written once and consumed elsewhere, so they should not displace
+// other data in the caches.
 TACO_DEV void bstore128(uint4 v, rsrc_t r, int voff, int soff) {
   u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kNT);
 }
 TACO_DEV void bstore64(uint2 v, rsrc_t r, int voff, int soff) {
   u32x2 w = {v.x, v.y};
-  __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, kNT);
 }
-TACO_DEV void bstore32(uint32_t v, rsrc_t r, int voff, int soff) { __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0); }
+TACO_DEV void bstore32(uint32_t v, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, kNT);
+}
 TACO_DEV void bstore8(uint32_t v, rsrc_t r, int voff, int soff) {
   __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, voff, soff, 0);
 }
