@@ -49,8 +49,9 @@ def parse():
                          "next activation, on a second stream, and report the overlap")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (known bytes) for counter calibration")
-    ap.add_argument("--summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
-                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE / kernel-trace output into the "
+    ap.add_argument("--summarize", nargs="+", metavar="PATH",
+                    help="FETCH_DIR WRITE_DIR TRACE_DIR [TRACE_LOG]: turn rocprofv3 FETCH_SIZE / WRITE_SIZE / "
+                         "kernel-trace output (and the bench line printed under the trace) into the "
                          "profiles/ summaries and exit")
     ap.add_argument("--command", default="", help="with --summarize: the profiled command, recorded")
     return ap.parse_args()
@@ -123,12 +124,20 @@ def _csv_rows(d, suffix):
     return out
 
 
-def summarize(fetch_dir, write_dir, trace_dir, workload, command):
+def summarize(fetch_dir, write_dir, trace_dir, workload, command, trace_log=None):
     """Per-launch HBM bytes of the hot kernels from two counter passes, scaled by
     what the same counters read for a plain copy of COPY_BYTES (read and write),
-    plus the kernel-trace averages; written to profiles/<kernel>_<workload>_*.txt."""
+    plus the kernel-trace averages and, when the profiled run's output is given,
+    the bench's own event timing in that same run; written to
+    profiles/<kernel>_<workload>_*.txt."""
     import numpy as np
     src_hash = kernel_source_hash()
+    bench_ms = {}
+    if trace_log:
+        lines = [l for l in open(trace_log) if l.startswith("{")]
+        if lines:
+            k = json.loads(lines[-1]).get("kernels", {})
+            bench_ms = {"compress": k.get("compress_ms"), "reduce": k.get("reduce_ms")}
     per = {}
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         for row in _csv_rows(d, "counter_collection.csv"):
@@ -182,6 +191,10 @@ def summarize(fetch_dir, write_dir, trace_dir, workload, command):
                 fh.write(f"trace_average_ns: {tr.get('AverageNs')}\n")
                 fh.write(f"trace_min_ns: {tr.get('MinNs')}\n")
                 fh.write(f"trace_max_ns: {tr.get('MaxNs')}\n")
+            if bench_ms.get(key) is not None:
+                fh.write("# the bench's own HIP-event average in the profiled run (back-to-back launches,\n"
+                         "# including the gap before each launch, which the profiler widens)\n")
+                fh.write(f"bench_event_average_ns_under_profiler: {bench_ms[key] * 1e6:.0f}\n")
         written.append(path)
     if trace:
         path = os.path.join(ROOT, "profiles", f"kernels_{workload}_trace.txt")
@@ -306,7 +319,11 @@ def measure_overlap(w, step_fn, nsets, stream, codec_ms, K):
 def main():
     args = parse()
     if args.summarize:
-        summarize(*args.summarize, args.workload, args.command)
+        if len(args.summarize) not in (3, 4):
+            sys.exit("--summarize takes FETCH_DIR WRITE_DIR TRACE_DIR [TRACE_LOG]")
+        fetch, write, trace = args.summarize[:3]
+        log = args.summarize[3] if len(args.summarize) == 4 else None
+        summarize(fetch, write, trace, args.workload, args.command, log)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
