@@ -99,3 +99,52 @@ def test_full_size_workload(name):
     assert worst < limit and np.isfinite(worst)
     if fp8:
         assert rows_of(out, cout, w.rows, w.cols, idx[:1])["g"] == np.float32(w.shards)   # g' = sum of g_r = N
+
+
+# A reduce launch covers at most 2^28 elements; the host splits larger tensors
+# into pieces over offset pointers. 65600 x 4096 is 262144 elements past 2^28,
+# so the second piece holds the last 64 rows.
+PIECE_PAIRS = [
+    (cd.Codec(cd.FP8_DUAL, 128, True), cd.Codec(cd.FP8_DUAL, 128, True), "normal"),
+    (cd.Codec(cd.INT8_SYM, 64, False), cd.Codec(cd.INT8_SYM, 64, False), "normal"),
+    (cd.Codec(cd.INT4_ASYM, 128, False), cd.Codec(cd.INT8_ASYM, 128, False), "t3"),
+    (cd.Codec(cd.INT8_ASYM, 128, False), cd.Codec(cd.INT8_ASYM, 128, False), "t3"),
+]
+
+
+@pytest.mark.parametrize("cin,cout,body", PIECE_PAIRS,
+                         ids=lambda p: f"fmt{p.format}" if isinstance(p, cd.Codec) else p)
+def test_reduce_split_into_pieces(cin, cout, body):
+    rows, cols, shards = 65600, 4096, 2
+    assert rows * cols > (1 << 28)
+    w = W.Workload("piece-split", rows, cols, shards, 6000 + cin.format, body, 0.02,
+                   cin.format, cin.block, cin.hadamard, cout.format, cout.block)
+    fp8 = cin.format == cd.FP8_DUAL
+    g = np.float32(0.0125)
+    n_chunks = (rows + W.ROW_CHUNK - 1) // W.ROW_CHUNK
+    chunks = [0, (1 << 28) // cols // W.ROW_CHUNK - 1, n_chunks - 1]   # first, last of piece 0, piece 1
+    idx = W.chunk_rows(chunks, rows)
+    print(f"[piece-split {cin.format}->{cout.format}] n = {rows * cols}, sampled rows {len(idx)}", flush=True)
+    bufs = []
+    for r in range(shards):
+        x = torch.from_numpy(W.make_shard(w, r).view(np.int16)).to(DEV)
+        buf = T.empty_compressed(ccodec(cin), rows, cols, DEV)
+        T.taco_compress(ccodec(cin), x, rows, cols, float(g) if fp8 else 1.0, buf)
+        del x
+        bufs.append(buf)
+    s = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+    out = T.empty_compressed(ccodec(cout), rows, cols, DEV)
+    T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, s, ccodec(cout), out)
+    torch.cuda.synchronize()
+
+    refs = []
+    for r in range(shards):
+        ref = oracle.compress(cin, W.make_shard(w, r, chunks=chunks), tensor_scale=g if fp8 else None)
+        check_rows(rows_of(bufs[r], cin, rows, cols, idx), ref, f"shard {r}")
+        refs.append(ref)
+    acc, rq = oracle.decompress_reduce(refs, cout)
+    it = torch.from_numpy(idx).to(DEV)
+    assert same_f32_bits(s.view(rows, cols)[it].cpu().numpy(), acc).all(), "FP32 sum differs"
+    check_rows(rows_of(out, cout, rows, cols, idx), rq, "requantized")
+    if fp8:
+        assert rows_of(out, cout, rows, cols, idx[:1])["g"] == np.float32(g + g)   # written once, by piece 0
