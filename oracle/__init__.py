@@ -37,9 +37,9 @@ Where the pages leave a step open the oracle takes one plain reading; each is
 listed, with its reason, in the repository's design notes and repeated in the
 docstring of the function that implements it.
 
-Parity status. Formats, transform, reduction and the INT8 / asymmetric
-codecs are pinned by closed forms, brute force and library cross-checks in
-``tests/``. TACO's reshaping, ASH transform and dual-scale quantization are
+Parity status. Formats, transform, reduction, the ring hop and the INT8 /
+asymmetric codecs are pinned by closed forms, brute force and library
+cross-checks in ``tests/``. TACO's reshaping, ASH transform and dual-scale quantization are
 never defined on the pages (the referee on the TACO page says the reshaping
 and adaptive scales are "not quantified"), so ``compress_fp8_dual`` and its
 inverse are pinned only to the readings they implement: parity unpinned
@@ -66,6 +66,7 @@ from .codecs import (  # noqa: F401
     compress,
     dequantize,
     decompress_reduce,
+    ring_hop,
     requantize,
     decode,
     auto_tensor_scale,

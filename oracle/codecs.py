@@ -361,6 +361,37 @@ def decompress_reduce(shards: List[Compressed], out_codec: Optional[Codec] = Non
     return acc.reshape(c0.rows, c0.cols), rq
 
 
+def ring_hop(incoming: Optional[Compressed], local_bits, out_codec: Codec, in_codec: Optional[Codec] = None):
+    """One hop of a quantized ring reduce-scatter.
+
+    [EQuARX] "What carries the argument": on each hop the received shard is
+    dequantized to FP32 before the receiver adds its own contribution, and the
+    partial sum is quantized again before it is sent on; the full-loop ring
+    takes N - 1 such hops ("Extended reading notes"). Reading: the sum is
+    acc = (0 + dequant(incoming)) + f32(local), one float32 rounding per add
+    (the order of the decompress-reduce with the local bf16 shard as the last
+    addend); incoming None is the first hop (acc = 0 + f32(local)). The
+    partial sum is quantized with out_codec (INT8_SYM -> INT8_SYM,
+    INT4_ASYM / INT8_ASYM -> INT8_ASYM). Transform-free formats only: the FP8
+    codec's shards live in the Hadamard domain and its gather scale needs the
+    local tensor's abs-max, so it is not a ring codec here.
+
+    Returns (acc float32 [rows, cols], Compressed in out_codec).
+    """
+    x = bf16_bits_to_f32(np.asarray(local_bits, dtype=np.uint16))
+    rows, cols = x.shape
+    assert out_codec.format in (INT8_SYM, INT8_ASYM), "ring hops use INT8 codecs"
+    acc = np.zeros(rows * cols, dtype=np.float32)
+    if incoming is not None:
+        assert (incoming.rows, incoming.cols) == (rows, cols)
+        check_pair(incoming.codec, out_codec)
+        acc = (acc + dequantize(incoming)).astype(np.float32)
+    elif in_codec is not None:
+        check_pair(in_codec, out_codec)
+    acc = (acc + x.reshape(-1)).astype(np.float32)
+    return acc.reshape(rows, cols), quantize_values(out_codec, acc, rows, cols, None)
+
+
 def requantize(codec, x_f32, tensor_scale=None):
     """Quantize a caller-supplied float32 tensor (FP8: taken as transformed values)."""
     x = np.asarray(x_f32, dtype=np.float32)

@@ -119,3 +119,27 @@ def test_int4_nibble_order_swap_is_caught(monkeypatch):
         return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
     monkeypatch.setattr(fm, "pack_int4", bad)
     assert _fails(TF.test_int4_pack_roundtrip_exhaustive)
+
+
+def _bad_ring_hop(sign, keep_incoming):
+    """A ring hop with the local term's sign flipped, or the incoming dropped."""
+    import oracle
+
+    def bad(incoming, local_bits, out_codec, in_codec=None):
+        x = fm.bf16_bits_to_f32(np.asarray(local_bits, dtype=np.uint16))
+        rows, cols = x.shape
+        acc = np.zeros(rows * cols, dtype=np.float32)
+        if incoming is not None and keep_incoming:
+            acc = (acc + cd.dequantize(incoming)).astype(np.float32)
+        acc = (acc + np.float32(sign) * x.reshape(-1)).astype(np.float32)
+        return acc.reshape(rows, cols), cd.quantize_values(out_codec, acc, rows, cols, None)
+    return bad
+
+
+@pytest.mark.parametrize("sign,keep", [(-1.0, True), (1.0, False)], ids=["sign", "dropped"])
+def test_ring_hop_mistakes_are_caught(monkeypatch, sign, keep):
+    import oracle
+    import tests.test_oracle_ring as TR
+    monkeypatch.setattr(oracle, "ring_hop", _bad_ring_hop(sign, keep))
+    assert _fails(TR.test_hop_sum_is_exact_when_every_term_is_representable)
+    assert _fails(TR.test_ring_mse_matches_the_reported_values)

@@ -1,0 +1,119 @@
+"""Pins of the oracle's ring hop ([EQuARX] "What carries the argument": a
+received shard is dequantized to FP32, the local contribution added, and the
+partial sum quantized again for the next hop; full-loop ring of N - 1 hops).
+
+The hop is one float32 add between two already pinned steps, so it is pinned
+by the cases that reduce to them, by an exact case checked against float64
+arithmetic, and by the error statistics of a whole ring."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import codecs as cd
+from oracle.formats import bf16_bits_to_f32, f32_to_bf16_bits
+
+PAIRS = [(cd.Codec(cd.INT8_SYM, 64, False), cd.Codec(cd.INT8_SYM, 64, False)),
+         (cd.Codec(cd.INT4_ASYM, 128, False), cd.Codec(cd.INT8_ASYM, 128, False)),
+         (cd.Codec(cd.INT8_ASYM, 128, False), cd.Codec(cd.INT8_ASYM, 128, False))]
+
+
+def bits(shape, seed, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits((rng.standard_normal(shape) * sigma).astype(np.float32))
+
+
+def same(a: cd.Compressed, b: cd.Compressed):
+    assert (a.codes == b.codes).all()
+    assert (a.scale.view(np.uint32) == b.scale.view(np.uint32)).all()
+    if a.zero is not None or b.zero is not None:
+        assert (a.zero == b.zero).all()
+
+
+@pytest.mark.parametrize("cin,cout", PAIRS, ids=["i8s", "i4a", "i8a"])
+def test_first_hop_is_the_compress_of_the_local_shard(cin, cout):
+    x = bits((6, 256), 1)
+    acc, q = oracle.ring_hop(None, x, cout, in_codec=cin)
+    assert (acc == bf16_bits_to_f32(x)).all()
+    same(q, oracle.compress(cout, x))
+
+
+@pytest.mark.parametrize("cin,cout", PAIRS, ids=["i8s", "i4a", "i8a"])
+def test_hop_with_zero_local_is_the_reduce_of_one_shard(cin, cout):
+    inc = oracle.compress(cin, bits((6, 256), 2))
+    zero = np.zeros((6, 256), dtype=np.uint16)
+    acc, q = oracle.ring_hop(inc, zero, cout)
+    acc2, q2 = oracle.decompress_reduce([inc], cout)
+    assert (acc.view(np.uint32) == acc2.view(np.uint32)).all()
+    same(q, q2)
+
+
+def test_hop_sum_is_exact_when_every_term_is_representable():
+    # Incoming: INT8 codes with the power-of-two scale 2^-4 (block abs-max 127/16
+    # quantizes to itself); local: multiples of 2^-6. Every sum is exact in
+    # float32, so acc must equal the float64 sum of the two terms, in the right
+    # order and with the right signs.
+    rows, cols = 4, 128
+    q = (np.arange(rows * cols) % 255 - 127).astype(np.int8).reshape(rows, cols)
+    q[:, ::64] = 127                                   # every block reaches 127
+    inc_vals = q.astype(np.float64) / 16.0
+    inc = oracle.compress(cd.Codec(cd.INT8_SYM, 64, False), f32_to_bf16_bits(inc_vals.astype(np.float32)))
+    assert (inc.codes.view(np.int8).reshape(rows, cols) == q).all()
+    assert (inc.scale == np.float32(127.0 / 16.0 / 127.0)).all()
+    loc = (np.arange(rows * cols).reshape(rows, cols) % 97 - 48) / 64.0
+    acc, _ = oracle.ring_hop(inc, f32_to_bf16_bits(loc.astype(np.float32)), cd.Codec(cd.INT8_SYM, 64, False))
+    assert (acc.astype(np.float64) == inc_vals + loc).all()
+
+
+def block_absmax_sq(var, trials=20000, seed=7):
+    """E[A^2] for A the abs-max of a block of 64 N(0, var) samples, by sampling."""
+    rng = np.random.default_rng(seed)
+    a = np.abs(rng.standard_normal((trials, 64))).max(axis=1)
+    return float((a ** 2).mean()) * var
+
+
+def test_full_loop_ring_error_statistics():
+    # N = 8 ranks of N(0, 1) data, block-64 INT8. Closed form of one
+    # quantization of a block: the rounding error is uniform over a step
+    # s = A / 127, so its MSE is E[A^2] / (12 * 127^2), A the block abs-max.
+    #  * gather-only: one quantization of the exact sum (variance N);
+    #  * full loop: each rank's chunk is quantized after 1, 2, ..., N addends
+    #    (the partial sums sent on N - 1 hops, then the gather), and the
+    #    independent errors add up: sum over i of E[A_i^2] / (12 * 127^2) with
+    #    A_i the abs-max of a variance-i block.
+    N, shape = 8, (64, 1024)
+    codec = cd.Codec(cd.INT8_SYM, 64, False)
+    xs = [bits(shape, 100 + r) for r in range(N)]
+    exact = sum(bf16_bits_to_f32(x).astype(np.float64) for x in xs)
+    q = None
+    for r in range(N):
+        acc, q = oracle.ring_hop(q, xs[r], codec, in_codec=codec)
+    ring = oracle.dequantize(q).reshape(shape).astype(np.float64)
+    once = oracle.dequantize(oracle.requantize(codec, exact.astype(np.float32))).reshape(shape)
+    mse_ring = float(((ring - exact) ** 2).mean())
+    mse_once = float(((once - exact) ** 2).mean())
+    step = 12 * 127 ** 2
+    want_once = block_absmax_sq(N) / step
+    want_ring = sum(block_absmax_sq(i) for i in range(1, N + 1)) / step
+    assert 0.8 * want_once < mse_once < 1.25 * want_once, (mse_once, want_once)
+    assert 0.8 * want_ring < mse_ring < 1.25 * want_ring, (mse_ring, want_ring)
+
+
+def test_ring_mse_matches_the_reported_values():
+    # The pages' MSE for the full-loop ring and for all-gather-only
+    # quantization (tests/golden/equarx_ring_mse.txt), reproduced within 25 %
+    # by 8 ranks of N(0, 1) data.
+    from tests.conftest import read_golden
+    want = {k: float(v) for k, v in read_golden("equarx_ring_mse.txt")}
+    N, shape = 8, (64, 1024)
+    codec = cd.Codec(cd.INT8_SYM, 64, False)
+    xs = [bits(shape, 300 + r) for r in range(N)]
+    exact = sum(bf16_bits_to_f32(x).astype(np.float64) for x in xs)
+    q = None
+    for r in range(N):
+        _, q = oracle.ring_hop(q, xs[r], codec, in_codec=codec)
+    ring = oracle.dequantize(q).reshape(shape).astype(np.float64)
+    once = oracle.dequantize(oracle.requantize(codec, exact.astype(np.float32))).reshape(shape)
+    got = {"full-loop": float(((ring - exact) ** 2).mean()), "ag-only": float(((once - exact) ** 2).mean())}
+    for k in want:
+        assert abs(got[k] - want[k]) < 0.25 * want[k], (k, got[k], want[k])
