@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--launch", choices=["graph", "eager"], default="eager")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--ring", action="store_true",
+                    help="INT workloads: also time one quantized ring reduce-scatter hop (taco_ring_hop) at "
+                         "full size and run the whole full-loop ring over the shards for its MSE")
     ap.add_argument("--overlap", action="store_true",
                     help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
                          "next activation, on a second stream, and report the overlap")
@@ -80,6 +83,54 @@ def algorithmic_bytes(w):
         out = n + 5 * (n // 128)
     reduce = w.shards * shard + out
     return compress, reduce
+
+
+def measure_ring(w, xs, stream, K):
+    """One hop of the full-loop ring (dequantize the incoming shard, add the
+    local bf16 shard, quantize for the next hop) timed at full size, and the
+    whole ring over the workload's shards: its MSE against the exact sum, next
+    to the MSE of quantizing the exact sum once (the all-gather alone)."""
+    import torch
+    import quantized_compression_tensor_amd as T
+    c_in = T.codec(w.in_format, w.in_block, 0)
+    c_out = T.codec(w.out_format, w.out_block, 0)
+    dev = "cuda"
+    N = len(xs)
+    sh = stream.cuda_stream
+    bufs = [T.empty_compressed(c_out, w.rows, w.cols, dev) for _ in range(3)]
+    with torch.cuda.stream(stream):
+        # the ring: the first rank quantizes its shard, every later rank adds its own
+        T.taco_ring_hop(c_out, None, xs[0], w.rows, w.cols, None, c_out, bufs[0], stream=sh)
+        for r in range(1, N):
+            T.taco_ring_hop(c_out, bufs[(r - 1) % 2], xs[r], w.rows, w.cols, None, c_out, bufs[r % 2], stream=sh)
+        ring = torch.empty(w.n, dtype=torch.float32, device=dev)
+        T.taco_decompress(c_out, bufs[(N - 1) % 2], w.rows, w.cols, ring, 0, stream=sh)
+        exact = torch.zeros(w.n, dtype=torch.float64, device=dev)
+        for x in xs:
+            exact += x.view(torch.bfloat16).reshape(-1).to(torch.float64)
+        once_q = T.empty_compressed(c_out, w.rows, w.cols, dev)
+        T.taco_requantize(c_out, exact.to(torch.float32), w.rows, w.cols, 1.0, once_q, stream=sh)
+        once = torch.empty(w.n, dtype=torch.float32, device=dev)
+        T.taco_decompress(c_out, once_q, w.rows, w.cols, once, 0, stream=sh)
+        # timing: K hops back to back between one pair of events
+        for i in range(3):
+            T.taco_ring_hop(c_out, bufs[i % 2], xs[i % N], w.rows, w.cols, None, c_out, bufs[2], stream=sh)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            T.taco_ring_hop(c_out, bufs[i % 2], xs[i % N], w.rows, w.cols, None, c_out, bufs[2], stream=sh)
+        b.record(stream)
+    torch.cuda.synchronize()
+    hop_ms = a.elapsed_time(b) / K
+    n = w.n
+    qb = n + (4 * (n // 64) if w.out_format == 2 else 5 * (n // 128))   # INT8 codes + metadata
+    hop_bytes = qb + 2 * n + qb
+    mse_ring = float(((ring.double() - exact) ** 2).mean())
+    mse_once = float(((once.double() - exact) ** 2).mean())
+    return {"hop_ms": round(hop_ms, 5), "hop_GBs": round(hop_bytes / (hop_ms * 1e-3) / 1e9, 1),
+            "hop_hbm_frac": round(hop_bytes / (hop_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "hop_algorithmic_bytes": hop_bytes, "ranks": N, "hops": N - 1,
+            "ring_mse": mse_ring, "all_gather_only_mse": mse_once, "ring_codec_in": "INT8 (gather codec)"}
 
 
 def kernel_source_hash():
@@ -450,6 +501,12 @@ def main():
         ach, bytes_launch, kname = red_gbs, b_red, "reduce"
     traffic = read_traffic(kname, w.name, src_hash)
 
+    ring = None
+    if args.ring:
+        if w.in_format == T.TACO_FMT_FP8_DUAL:
+            sys.exit("--ring applies to the INT workloads (the FP8 codec is not a ring codec)")
+        ring = measure_ring(w, xs[0], stream, K=max(10, K // 4))
+
     overlap = None
     if args.overlap:
         overlap = measure_overlap(w, step_fn=lambda s: (compress(s), reduce(s)), nsets=nsets, stream=stream,
@@ -504,6 +561,7 @@ def main():
         "quality": q,
         "cpu_baseline": cpu,
         **({"overlap": overlap} if overlap else {}),
+        **({"ring": ring} if ring else {}),
         "source_hash": src_hash,
     }
     print(json.dumps(out))

@@ -13,7 +13,8 @@
  *  [EQuARX]    "EQuARX: Efficient Quantized AllReduce in XLA for Distributed
  *              Machine Learning Acceleration": "What carries the argument"
  *              (dynamic block-wise symmetric int8, one FP32 scale per 64
- *              entries, dequantize to FP32 before adding).
+ *              entries, dequantize to FP32 before adding; the quantized
+ *              ring reduce-scatter hop).
  *  [FlashComm] "Flash Communication: Reducing Tensor Parallelization
  *              Bottleneck for Fast Large Language Model Inference": "What
  *              carries the argument" (asymmetric group-128 INT4/INT8, local sum
@@ -154,6 +155,26 @@ int taco_compress_debug(taco_codec c, const void* x_bf16, int64_t rows, int64_t 
  *   n        1 .. TACO_MAX_SHARDS                                            */
 int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n, int64_t rows, int64_t cols,
                            float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream);
+
+/* One hop of a quantized ring reduce-scatter ([EQuARX] "What carries the
+ * argument": a received shard is dequantized to FP32 before the receiver adds
+ * its own contribution, and the partial sum is quantized again for the next
+ * hop; the full-loop ring takes N - 1 hops):
+ *   acc = (0 + dequant(incoming)) + local, one float32 rounding per add,
+ * then, optionally,
+ *   sum_fp32     device float32 [rows, cols] receives acc (nullable)
+ *   requant_out  device buffer in c_out's layout receives acc quantized for
+ *                the next hop (nullable)
+ * At least one output must be given.
+ *   incoming     device buffer in c_in's layout, or NULL for the first hop
+ *                (acc = 0 + local; c_in must still be a valid codec)
+ *   local_bf16   device bf16 [rows, cols], this rank's contribution
+ * Pairs: INT8_SYM -> INT8_SYM, INT4_ASYM -> INT8_ASYM, INT8_ASYM -> INT8_ASYM.
+ * The FP8 codec is not a ring codec (its shards live in the Hadamard domain
+ * and its gather scale would need the local tensor's abs-max):
+ * TACO_ERR_FORMAT. */
+int taco_ring_hop(taco_codec c_in, const void* incoming, const void* local_bf16, int64_t rows, int64_t cols,
+                  float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream);
 
 /* Quantize a caller-supplied float32 tensor with c_out (the gather-stage
  * re-quantization on its own). FP8 takes the values as already transformed

@@ -35,7 +35,7 @@ TACO_WORKSPACE_BYTES = 16384
 # Entry points declared in include/taco.h (checked by the ABI tests).
 EXPORTS = (
     "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
-    "taco_compress_debug", "taco_decompress_reduce", "taco_requantize", "taco_decompress",
+    "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
     "taco_e4m3_encode", "taco_status_string",
 )
 
@@ -85,6 +85,7 @@ def _load():
         "taco_compress": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
         "taco_compress_debug": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P, P]),
         "taco_decompress_reduce": (ctypes.c_int, [C, ctypes.POINTER(P), I32, I64, I64, P, C, P, P]),
+        "taco_ring_hop": (ctypes.c_int, [C, P, P, I64, I64, P, C, P, P]),
         "taco_requantize": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
         "taco_decompress": (ctypes.c_int, [C, P, I64, I64, P, I32, P]),
         "taco_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
@@ -171,6 +172,13 @@ def taco_decompress_reduce(c_in, shards, rows, cols, sum_fp32=None, c_out=None, 
     co = c_out if c_out is not None else taco_codec(0, 0, 0, 0)
     return _check(_lib.taco_decompress_reduce(c_in, arr, len(shards), rows, cols, _ptr(sum_fp32), co,
                                               _ptr(requant_out), _stream(stream)), "taco_decompress_reduce")
+
+
+def taco_ring_hop(c_in, incoming, local_bf16, rows, cols, sum_fp32=None, c_out=None, requant_out=None,
+                  stream=None):
+    co = c_out if c_out is not None else taco_codec(0, 0, 0, 0)
+    return _check(_lib.taco_ring_hop(c_in, _ptr(incoming), _ptr(local_bf16), rows, cols, _ptr(sum_fp32), co,
+                                     _ptr(requant_out), _stream(stream)), "taco_ring_hop")
 
 
 def taco_requantize(c_out, x_fp32, rows, cols, tensor_scale, out, workspace=None, ws_bytes=None, stream=None):

@@ -589,6 +589,49 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   }
 }
 
+// One hop of a quantized ring reduce-scatter: acc = (0 + dequant(incoming)) +
+// local, one float32 rounding per add, then the FP32 sum and/or the partial sum
+// quantized for the next hop. Grid-stride over 1024-element wave tiles (as the
+// quantize kernel; 16 lanes' values per lane).
+template <int FIN, int BIN, int FOUT, int BOUT>
+__global__ __launch_bounds__(kBlockThreads) void k_ring_hop(HopArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t ntiles = (a.n + kWaveElems - 1) / kWaveElems;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  for (int64_t tile = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); tile < ntiles;
+       tile += stride) {
+    const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
+    const bool valid = e0 < a.n;   // n is a multiple of the block, a multiple of 16
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    if (valid) {
+      if (a.codes != nullptr) {
+        const LaneIn<FIN, BIN> in = load_in<FIN, BIN>(a.codes, a.scale, a.zero, nullptr, e0);
+        float d[16];
+        dequant_lane<FIN, BIN>(in, d);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
+      }
+      float x[16];
+      load_lane<false>(a.local, e0, x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + x[i];
+      if (a.sum != nullptr) {
+        float4* o = reinterpret_cast<float4*>(a.sum + e0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+      }
+    }
+    if (a.rq_codes != nullptr) {
+      // every lane takes part in the block reductions; lanes past the end
+      // quantize zeros and store nothing
+      const LaneCodes q = quant_lane<FOUT, BOUT>(acc, 0.0f, nullptr);
+      if (valid) store_lane<FOUT, BOUT>(q, e0, a.rq_codes, a.rq_scale, a.rq_zero);
+    }
+  }
+}
+
 // Test hook: the device E4M3 encoder alone (four values per lane).
 __global__ __launch_bounds__(kBlockThreads) void k_e4m3_encode(const float* x, uint8_t* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) * 4;
@@ -764,6 +807,23 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+template <int FIN, int BIN, int FOUT, int BOUT>
+static void launch_hop(const HopArgs& a, hipStream_t s) {
+  dim3 grid = grid_for(a.n), block(kBlockThreads);
+  const unsigned cap = (unsigned)(device_cu_count() * kPersistentGroupsPerCU);
+  if (grid.x > cap) grid.x = cap;
+  hipLaunchKernelGGL((k_ring_hop<FIN, BIN, FOUT, BOUT>), grid, block, 0, s, a);
+}
+
+hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  if (a.fin == kINT8S) launch_hop<kINT8S, 64, kINT8S, 64>(a, s);
+  else if (a.fin == kINT4A) launch_hop<kINT4A, 128, kINT8A, 128>(a, s);
+  else if (a.fin == kINT8A) launch_hop<kINT8A, 128, kINT8A, 128>(a, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s) {

@@ -244,7 +244,54 @@ int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n
     a.rq_codes = O.codes; a.rq_scale = O.scale; a.rq_zero = O.aux; a.rq_g_hdr = O.tensor;
   }
   clear_stale_error();
-    return hip_status(launch_reduce(a, stream));
+  return hip_status(launch_reduce(a, stream));
+}
+
+int taco_ring_hop(taco_codec c_in, const void* incoming, const void* local_bf16, int64_t rows, int64_t cols,
+                  float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream) {
+  int st = check_shape(c_in, rows, cols);
+  if (st != TACO_OK) return st;
+  if (c_in.format == TACO_FMT_FP8_DUAL) return TACO_ERR_FORMAT;
+  if (requant_out != nullptr) {
+    st = check_shape(c_out, rows, cols);
+    if (st != TACO_OK) return st;
+    if (!pair_allowed(c_in, c_out)) return TACO_ERR_FORMAT;
+  }
+  if (local_bf16 == nullptr || (sum_fp32 == nullptr && requant_out == nullptr)) return TACO_ERR_INVALID_ARG;
+  if ((incoming && !aligned16(incoming)) || !aligned16(local_bf16) || (sum_fp32 && !aligned16(sum_fp32)) ||
+      (requant_out && !aligned16(requant_out)))
+    return TACO_ERR_ALIGN;
+  const int64_t elems = rows * cols;
+  taco_layout_t Li, Lo;
+  layout_of(c_in, elems, &Li);
+  layout_of(requant_out ? c_out : c_in, elems, &Lo);
+  const void* outs[2] = {sum_fp32, requant_out};
+  const int64_t out_bytes[2] = {4 * elems, Lo.total_bytes};
+  for (int k = 0; k < 2; ++k) {
+    if (outs[k] == nullptr) continue;
+    if (incoming && overlaps(incoming, Li.total_bytes, outs[k], out_bytes[k])) return TACO_ERR_INVALID_ARG;
+    if (overlaps(local_bf16, 2 * elems, outs[k], out_bytes[k])) return TACO_ERR_INVALID_ARG;
+  }
+  if (sum_fp32 && requant_out && overlaps(sum_fp32, 4 * elems, requant_out, Lo.total_bytes))
+    return TACO_ERR_INVALID_ARG;
+  if (elems == 0) return TACO_OK;
+  HopArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fin = c_in.format; a.bin = c_in.block;
+  a.fout = requant_out ? c_out.format : c_in.format; a.bout = requant_out ? c_out.block : c_in.block;
+  a.n = elems;
+  if (incoming) {
+    Regions R = regions_of(const_cast<void*>(incoming), Li);
+    a.codes = R.codes; a.scale = R.scale; a.zero = R.aux;
+  }
+  a.local = static_cast<const uint16_t*>(local_bf16);
+  a.sum = sum_fp32;
+  if (requant_out) {
+    Regions O = regions_of(requant_out, Lo);
+    a.rq_codes = O.codes; a.rq_scale = O.scale; a.rq_zero = O.aux;
+  }
+  clear_stale_error();
+  return hip_status(launch_ring_hop(a, stream));
 }
 
 int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,

@@ -96,6 +96,20 @@ struct ReduceArgs {
   int zero_rel;         // asymmetric input: bytes from a shard's first scale to its first zero point
 };
 
+struct HopArgs {
+  int fin, fout;
+  int bin, bout;
+  int64_t n;
+  const uint8_t* codes;   // incoming shard (nullptr: first hop)
+  const void* scale;
+  const uint8_t* zero;
+  const uint16_t* local;  // bf16
+  float* sum;             // nullable
+  uint8_t* rq_codes;      // nullable
+  void* rq_scale;
+  uint8_t* rq_zero;
+};
+
 // Largest number of elements one reduce launch covers (keeps every buffer
 // offset, including the float32 sum's, below 2^31 bytes).
 constexpr int64_t kReducePiece = int64_t(1) << 28;
@@ -127,6 +141,7 @@ hipError_t launch_fp8_had_decode(const FP8HadDecodeArgs& a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s);
 hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s);
 
 }  // namespace taco

@@ -127,6 +127,23 @@ def test_reduce_validation():
     assert _st(red, I8S, shards, 0, 64, B_) == 0
 
 
+def test_ring_hop_validation():
+    hop = T.taco_ring_hop
+    L = A + (1 << 16)
+    assert _st(hop, I8S, A, None, 4, 64, B_) == T.TACO_ERR_INVALID_ARG             # no local shard
+    assert _st(hop, I8S, A, L, 4, 64, None, None, None) == T.TACO_ERR_INVALID_ARG  # no output
+    assert _st(hop, FP8, A, L, 4, 128, B_) == T.TACO_ERR_FORMAT                    # FP8 is not a ring codec
+    assert _st(hop, I8S, A, L, 4, 64, None, FP8, B_) == T.TACO_ERR_SHAPE           # 64 cols: no 128 block
+    assert _st(hop, I8S, A, L, 4, 128, None, FP8, B_) == T.TACO_ERR_FORMAT
+    assert _st(hop, I4A, A, L, 4, 128, None, I4A, B_) == T.TACO_ERR_FORMAT         # the gather stage is INT8
+    assert _st(hop, I8S, A + 4, L, 4, 64, B_) == T.TACO_ERR_ALIGN
+    assert _st(hop, I8S, A, L + 2, 4, 64, B_) == T.TACO_ERR_ALIGN
+    assert _st(hop, I8S, A, L, 4, 64, A) == T.TACO_ERR_INVALID_ARG                 # sum overlaps the incoming
+    assert _st(hop, I8S, A, L, 4, 64, L + 64) == T.TACO_ERR_INVALID_ARG            # sum overlaps the local
+    assert _st(hop, I8S, None, L, 0, 64, B_) == 0                                  # empty: nothing to do
+    assert _st(hop, I8S, None, L, 4, 96, B_) == T.TACO_ERR_SHAPE
+
+
 def test_other_entry_points_validation():
     assert _st(T.taco_decompress, I8S, A, 4, 64, B_, 2) == T.TACO_ERR_INVALID_ARG
     assert _st(T.taco_decompress, I8S, A, 4, 64, None, 0) == T.TACO_ERR_INVALID_ARG
