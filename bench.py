@@ -133,6 +133,18 @@ def measure_ring(w, xs, stream, K):
             "ring_mse": mse_ring, "all_gather_only_mse": mse_once, "ring_codec_in": "INT8 (gather codec)"}
 
 
+def decode_bytes(w):
+    """Bytes the consumer-side decode of the gather-stage output to bf16 moves."""
+    n = w.n
+    if w.out_format == 1:
+        src = n + n // w.out_block + 16
+    elif w.out_format == 2:
+        src = n + 4 * (n // 64)
+    else:
+        src = n + 5 * (n // 128)
+    return src + 2 * n
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantized_compression_tensor_amd", "csrc")
@@ -482,10 +494,20 @@ def main():
         for i in range(K):
             reduce(i % nsets)
         b_r.record(stream)
+        # the consumer-side decode of the gather-stage output to bf16 (the next
+        # GEMM's input; FP8: with the inverse transform), outside the step
+        dec_out = torch.empty(w.n, dtype=torch.bfloat16, device=dev) if c_out is not None else None
+        a_d, b_d = mk(), mk()
+        if dec_out is not None:
+            a_d.record(stream)
+            for i in range(K):
+                T.taco_decompress(c_out, outs[i % nsets], w.rows, w.cols, dec_out, 1, stream=sh)
+            b_d.record(stream)
         torch.cuda.synchronize()
 
     t_comp = a_c.elapsed_time(b_c) / (K * w.shards)   # ms per compress launch
     t_red = a_r.elapsed_time(b_r) / K                 # ms per reduce call
+    t_dec = a_d.elapsed_time(b_d) / K if dec_out is not None else None
     ms_step = wall * 1e3 / K
     gpu_ms_step = ev0.elapsed_time(ev1) / K
     value = in_bytes / (ms_step * 1e-3) / 1e9
@@ -554,6 +576,8 @@ def main():
         "kernels": {
             "compress_ms": round(t_comp, 5), "compress_GBs": round(comp_gbs, 1),
             "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
+            **({"decode_bf16_ms": round(t_dec, 5),
+                "decode_bf16_GBs": round(decode_bytes(w) / (t_dec * 1e-3) / 1e9, 1)} if t_dec else {}),
             "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "host_ms_per_step": round(host * 1e3 / K, 5),
             "event_ms_per_step": round(gpu_ms_step, 5),
