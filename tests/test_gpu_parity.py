@@ -358,3 +358,73 @@ def test_codec_overlapped_with_gemm_is_unchanged():
     assert_same(parse(out, oc, rows, cols),
                 oracle.decompress_reduce([oracle.compress(oc, bb) for bb in bits], oc)[1])
     del y
+
+
+# ------------------------------------------------- graph capture and replay ---
+
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(), cd.Codec.int8_sym(), cd.Codec.int4_asym()], ids=cid)
+def test_graph_replays_match_eager_steps(oc):
+    """A step (two compresses, FP8 with the delayed tensor scale, then the
+    decompress-reduce) captured once in a HIP graph and replayed four times,
+    with new input data copied in eagerly between the replays, produces exactly
+    the buffers of the same four steps run eagerly: the workspace history
+    advances with every replay as it does with every eager call."""
+    rows, cols, n, steps = 64, 4096, 2, 4
+    c = ccodec(oc)
+    cout = ccodec(cd.Codec.int8_asym() if oc.format == cd.INT4_ASYM else oc)
+    fp8 = oc.format == cd.FP8_DUAL
+    scale = T.TACO_SCALE_DELAYED if fp8 else 1.0
+    data = [[bits_for((rows, cols), seed=900 + 10 * s + r, sigma=0.02 * (1 + s)) for r in range(n)]
+            for s in range(steps)]
+
+    def alloc():
+        return ([new_workspace() for _ in range(n)], [T.empty_compressed(c, rows, cols) for _ in range(n)],
+                T.empty_compressed(cout, rows, cols), torch.empty(rows * cols, dtype=torch.float32, device=DEV))
+
+    def step(x, ws, bufs, out, s_out, stream):
+        for r in range(n):
+            T.taco_compress(c, x[r], rows, cols, scale, bufs[r], workspace=ws[r] if fp8 else None,
+                            stream=stream.cuda_stream)
+        T.taco_decompress_reduce(c, bufs, rows, cols, s_out, cout, out, stream=stream.cuda_stream)
+
+    # eager reference
+    eager = []
+    ws, bufs, out, s_out = alloc()
+    st = torch.cuda.Stream()
+    for s in range(steps):
+        x = [upload_bits(b) for b in data[s]]
+        torch.cuda.synchronize()
+        step(x, ws, bufs, out, s_out, st)
+        torch.cuda.synchronize()
+        eager.append(([parse(b, oc, rows, cols) for b in bufs], parse(out, cd.Codec(cout.format, cout.block,
+                                                                              bool(cout.hadamard)), rows, cols),
+                      s_out.cpu().numpy().copy()))
+    # captured once, replayed
+    ws, bufs, out, s_out = alloc()
+    x = [torch.empty(rows * cols, dtype=torch.int16, device=DEV) for _ in range(n)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=st):
+        step(x, ws, bufs, out, s_out, st)
+    oc_out = cd.Codec(cout.format, cout.block, bool(cout.hadamard))
+    for s in range(steps):
+        for r in range(n):
+            x[r].copy_(upload_bits(data[s][r]).reshape(-1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_bufs, ref_out, ref_sum = eager[s]
+        for r in range(n):
+            got = parse(bufs[r], oc, rows, cols)
+            for k in ("codes", "scale", "zero"):
+                if ref_bufs[r][k] is not None:
+                    assert (got[k].view(np.uint8) == ref_bufs[r][k].view(np.uint8)).all(), f"replay {s} shard {r} {k}"
+            if fp8:
+                assert np.float32(got["g"]).view(np.uint32) == np.float32(ref_bufs[r]["g"]).view(np.uint32), \
+                    f"replay {s} shard {r} g"
+        got = parse(out, oc_out, rows, cols)
+        assert (got["codes"] == ref_out["codes"]).all() and \
+            (got["scale"].view(np.uint8) == ref_out["scale"].view(np.uint8)).all(), f"replay {s} output"
+        assert (s_out.cpu().numpy().view(np.uint32) == ref_sum.view(np.uint32)).all(), f"replay {s} sum"
