@@ -476,13 +476,19 @@ TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, float g,
 
 template <int FIN, int BIN, int NMAX>
 struct ReduceGroup {
-  static constexpr int GRP = NMAX < 8 ? NMAX / 2 : 4;   // shards per step
+  // shards per step: four for FP8 from eight shards on (more bytes per step
+  // measured faster), two otherwise (fewer registers, more resident waves)
+  static constexpr int GRP = NMAX == 2 ? 1 : (FIN == kFP8 && NMAX >= 8 ? 4 : 2);
   static constexpr int NG = NMAX / GRP;                 // steps per tile (>= 2)
   LaneIn<FIN, BIN> in[GRP];
 
   // Issue the loads of shard group `grp` of the tile at element e0. glane:
   // lane r holds shard r's FP8 tensor scale.
   TACO_DEV void load(const ReduceArgs& a, int grp, int e0, int n, float glane) {
+    // With more than two groups the compiler would hoist every shard's
+    // resources out of the loop and spill them; an opaque group index keeps
+    // each step building only its own group's.
+    if constexpr (NG > 2) asm volatile("" : "+s"(grp));
 #pragma unroll
     for (int u = 0; u < GRP; ++u) {
       const int r = grp * GRP + u;
