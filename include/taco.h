@@ -31,7 +31,8 @@
  *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
  *    the caller synchronizes. All validation happens before anything is
  *    enqueued; a call that returns an error has enqueued nothing.
- *  - rows == 0 is valid and enqueues nothing.
+ *  - rows == 0 is valid and enqueues nothing; rows * cols above 2^35 is
+ *    TACO_ERR_INVALID_ARG.
  *  - Return value: TACO_OK or a negative TACO_ERR_* code
  *    (taco_status_string names it).
  *  - Values are finite: for blocks whose inputs or intermediate results are

@@ -219,32 +219,29 @@ def regions(buf, c, rows, cols):
 
 
 WS_TICKET_GROUPS = 16   # workspace ticket counters (kernel-side constants)
-WS_ACC_LINES = 64       # workspace abs-max accumulator lines
+WS_BANK_LINES = 32      # workspace record lines per bank (three banks)
 WS_LINE = 32            # uint32 words per 128-byte line
+WS_SHARE_SHIFT = 24     # each call adds 2^24 to every ticket counter
 
 
 def workspace_history(ws):
     """Read an FP8 tensor-scale workspace (a device tensor of
-    TACO_WORKSPACE_BYTES): returns (calls recorded, abs-max recorded by the most
-    recent call, that call's slot index). Layout (uint32 words, 32 per line):
-    line 0 word 0: grid P of the last call; line 1 + g: ticket counter g (16);
-    line 17 + l, words 0-2: abs-max accumulator line l (64) in slots 0-2.
+    TACO_WORKSPACE_BYTES) between calls: returns (calls made, abs-max recorded
+    by the most recent call, that call's bank). Layout (uint32 words, 32 per
+    line): line 0 unused; line 1 + g, words 0-1: ticket counter g (16, uint64);
+    line 17 + 32 b + l, word 0: record line l of bank b (3 banks of 32).
     Inspection only."""
     import numpy as np
     w = ws.detach().cpu().numpy().view(np.uint32).reshape(-1)
-    grid = int(w[0])
-    if grid == 0:
+    calls = int(w[WS_LINE:WS_LINE + 2].view(np.uint64)[0]) >> WS_SHARE_SHIFT
+    if calls == 0:
         return 0, 0.0, None
-    G = min(grid, WS_TICKET_GROUPS)
-    members0 = -(-grid // G)
-    calls = int(w[WS_LINE]) // members0
-    slot = (calls - 1) % 3
-    accl = acc_lines(w)
-    acc = accl[:, slot].copy()
-    return calls, float(acc.view(np.float32).max()), slot
+    bank = (calls - 1) % 3
+    amax = bank_lines(w)[bank].copy().view(np.float32).max()
+    return calls, float(amax), bank
 
 
-def acc_lines(words):
-    """The accumulator lines of a workspace given as uint32 words: [64, 32]."""
+def bank_lines(words):
+    """The record words of a workspace given as uint32 words: [3 banks, 32 lines]."""
     base = WS_LINE * (1 + WS_TICKET_GROUPS)
-    return words[base: base + WS_LINE * WS_ACC_LINES].reshape(WS_ACC_LINES, WS_LINE)
+    return words[base: base + WS_LINE * 3 * WS_BANK_LINES].reshape(3, WS_BANK_LINES, WS_LINE)[:, :, 0]

@@ -195,104 +195,106 @@ TACO_DEV float wave_max(float a) {
 
 // ------------------------------------------------------------- workspace --
 // Abs-max history of an FP8 tensor scale, in caller-owned memory that is
-// zero-filled once. Kernels that use it always run a fixed grid of P
-// workgroups (P = kPersistentGroupsPerCU * CUs). Workgroup b takes its tickets
-// from counter b % 16; wave w of workgroup b records into accumulator line
-// (4 b + w) % 64, which holds that line's abs-max in each of three slots.
-// Every counter and accumulator line is a 128-byte line of its own, so the
-// tickets taken at the start of a call never contend with the history reads.
+// zero-filled once. Calls on one workspace are ordered (one stream), and any
+// call may run any grid.
 //
-// At its start a workgroup takes a ticket from its counter (one returning
-// atomic add). Every call adds exactly `members` to each counter, so
-// ticket / members is the same call index t in every workgroup of a call.
-// Call t
-//   * reads the previous call's maxima from slot (t + 2) % 3,
-//   * folds each wave's maximum into slot t % 3 (atomic max, not awaited),
-//   * zeroes slot (t + 1) % 3 for the next call (first wave of workgroup 0).
-// No slot is read and written by the same call, and the kernel boundary orders
-// calls, so the history is read with plain loads and no fence or "last
-// workgroup" chain is needed. Only the first wave of a workgroup takes the
-// ticket and reads the history; it hands the call index (and the tensor scale)
-// to the others through LDS.
+// Call index. The workspace has 16 ticket counters; workgroup b adds to
+// counter b % 16, and the members of each counter add shares that total
+// exactly 2^24 per call (2^24 / members each, the first member the
+// remainder; with fewer than 16 workgroups some take several counters). A counter therefore holds t * 2^24 when call t
+// starts, and every workgroup's ticket (the value before its add) gives the
+// same t = ticket >> 24, whatever the grid.
+//
+// Banks. Three banks of 32 record lines each; call t
+//   * reads the previous call's maxima from bank (t + 2) % 3,
+//   * folds each workgroup's maximum into bank t % 3 (atomic max, not
+//     awaited),
+//   * zeroes bank (t + 1) % 3 for the next call (first wave of workgroup 0).
+// No bank is read and written by the same call, and the kernel boundary orders
+// calls, so there is no fence, no spin and no "last workgroup" chain. Every
+// counter and record line is a 128-byte line of its own. Only the first wave of
+// a workgroup takes the ticket and reads the history; it hands t % 3 (and the
+// tensor scale) to the others through LDS.
 constexpr int kTicketGroups = 16;
-constexpr int kAccLines = 64;
+constexpr int kAccLines = 32;
 constexpr int kLineWords = 32;
-static_assert(kAccLines <= kWave, "one lane per accumulator line");
+constexpr int kShareShift = 24;
+static_assert(kAccLines <= kWave, "one lane per record line");
 
-struct WsAcc {
-  uint32_t slot[3];                              // abs-max accumulators (float bits)
-  uint32_t pad[kLineWords - 3];
+struct WsLine {
+  uint32_t amax;                                 // float bits
+  uint32_t pad[kLineWords - 1];
+};
+struct WsCounter {
+  unsigned long long v;
+  uint32_t pad[kLineWords - 2];
 };
 struct Workspace {
-  uint32_t grid;                                 // P of the most recent call
-  uint32_t pad0[kLineWords - 1];
-  uint32_t calls[kTicketGroups][kLineWords];     // ticket counters
-  WsAcc acc[kAccLines];
+  uint32_t pad0[kLineWords];
+  WsCounter cnt[kTicketGroups];
+  WsLine bank[3][kAccLines];
 };
 static_assert(sizeof(Workspace) <= TACO_WORKSPACE_BYTES, "workspace size");
 
 #define TACO_AT_MAX(p, v) __hip_atomic_fetch_max((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 #define TACO_AT_ADD(p, v) __hip_atomic_fetch_add((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-#define TACO_AT_STORE(p, v) __hip_atomic_store((p), (v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
 
-TACO_DEV uint32_t ws_ticket_groups(uint32_t grid) {
-  return grid < (uint32_t)kTicketGroups ? grid : (uint32_t)kTicketGroups;
-}
-
-// This workgroup's ticket: the counter value before its add (one lane).
-TACO_DEV uint32_t ws_ticket(Workspace* ws) {
-  const uint32_t g = blockIdx.x % ws_ticket_groups(gridDim.x);
-  return TACO_AT_ADD(&ws->calls[g][0], 1u);
-}
-TACO_DEV uint32_t ws_call(uint32_t ticket) {
-  const uint32_t G = ws_ticket_groups(gridDim.x);
+// This workgroup's ticket (first wave, all lanes; lane 0 issues the add and
+// holds the result). The caller issues its data loads next and reads the
+// result only when it needs the call index. With fewer than 16 workgroups,
+// workgroup b also adds the whole 2^24 to every counter b + k * grid < 16
+// (k >= 1, lane k, not awaited), so every counter still advances by exactly
+// 2^24 per call.
+TACO_DEV unsigned long long ws_ticket(Workspace* ws) {
+  const uint32_t G = kTicketGroups;
   const uint32_t g = blockIdx.x % G;
   const uint32_t members = (gridDim.x - g + G - 1) / G;
-  return ticket / members;
+  const unsigned long long total = 1ull << kShareShift;
+  unsigned long long share = total / members;
+  if (blockIdx.x < G) share = total - (unsigned long long)(members - 1) * share;
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  unsigned long long t = 0;
+  if (lane == 0) t = TACO_AT_ADD(&ws->cnt[g].v, share);
+  if (gridDim.x < G && lane > 0) {
+    const uint32_t j = g + lane * gridDim.x;
+    if (j < G) (void)TACO_AT_ADD(&ws->cnt[j].v, total);
+  }
+  return t;
+}
+// The call index mod 3 from lane 0's ticket (wave-uniform).
+TACO_DEV uint32_t ws_bank_of(unsigned long long ticket) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)ticket);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(ticket >> 32));
+  return (uint32_t)(((((unsigned long long)hi) << 32 | lo) >> kShareShift) % 3ull);
 }
 
-// Accumulator line `lane` (slots 0-2 in x, y, z).
-TACO_DEV uint4 ws_history_lanes(const Workspace* ws) {
+// History read before the call index is known: record line `lane` of every
+// bank (used where no bank is written yet when the read is issued).
+TACO_DEV uint3 ws_history_all(const Workspace* ws) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint4 h = make_uint4(0, 0, 0, 0);
-  if (lane < kAccLines) h = *reinterpret_cast<const uint4*>(&ws->acc[lane]);
+  uint3 h = make_uint3(0, 0, 0);
+  if (lane < kAccLines) h = make_uint3(ws->bank[0][lane].amax, ws->bank[1][lane].amax, ws->bank[2][lane].amax);
   return h;
 }
-
-// Abs-max recorded by call t - 1, from the lanes of ws_history_lanes (the
-// result is wave-uniform).
-TACO_DEV float ws_prev_amax(uint4 h, uint32_t t) {
-  const uint32_t slot = (t + 2) % 3;
-  const float v = __uint_as_float(slot == 0 ? h.x : (slot == 1 ? h.y : h.z));
+// The previous call's abs-max (wave-uniform) from ws_history_all's lanes.
+TACO_DEV float ws_prev_from(uint3 h, uint32_t e) {
+  const uint32_t pb = e == 0 ? 2u : e - 1u;
+  const float v = __uint_as_float(pb == 0 ? h.x : (pb == 1 ? h.y : h.z));
   return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(v))));
 }
-
-// Fold this wave's max (any value per lane) into call t's slot; the first wave
-// of workgroup 0 also clears the next slot. Called by every lane of a wave.
-TACO_DEV void ws_record_wave(Workspace* ws, uint32_t t, float lane_max) {
+// The previous call's abs-max read once the call index is known.
+TACO_DEV float ws_prev_amax(const Workspace* ws, uint32_t e) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = wave_in_group();
-  const float m = wave_max(lane_max);
-  const uint32_t line = (blockIdx.x * (kBlockThreads / kWave) + wave) % kAccLines;
-  if (lane == 0) TACO_AT_MAX(&ws->acc[line].slot[t % 3], __float_as_uint(m));
-  if (blockIdx.x == 0 && wave == 0) {
-    if (lane < kAccLines) TACO_AT_STORE(&ws->acc[lane].slot[(t + 1) % 3], 0u);
-    if (lane == 0) TACO_AT_STORE(&ws->grid, gridDim.x);
-  }
+  const uint32_t pb = e == 0 ? 2u : e - 1u;
+  float v = 0.0f;
+  if (lane < kAccLines) v = __uint_as_float(ws->bank[pb][lane].amax);
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(v))));
 }
-
-// Start of a call (first wave only, all its lanes): the ticket and, when
-// `history`, the accumulator lines are requested; the caller issues its first
-// loads before it uses them, so those stay in flight while the ticket returns.
-struct WsStart {
-  uint32_t ticket;
-  uint4 hist;
-};
-TACO_DEV WsStart ws_begin(Workspace* ws, bool history) {
-  WsStart s{0u, make_uint4(0, 0, 0, 0)};
-  if ((threadIdx.x & (kWave - 1)) == 0) s.ticket = ws_ticket(ws);
-  if (history) s.hist = ws_history_lanes(ws);
-  return s;
+// Zero the next call's bank (first wave of workgroup 0, all lanes).
+TACO_DEV void ws_clear_next(Workspace* ws, uint32_t e) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t nb = e == 2 ? 0u : e + 1u;
+  if (lane < kAccLines) ws->bank[nb][lane].amax = 0u;
 }
 
 // Workgroup barrier that orders LDS only: unlike __syncthreads it does not
@@ -303,5 +305,21 @@ TACO_DEV void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Fold the workgroup's max (any value per lane) into its record line of bank
+// e: every thread of the workgroup calls it; one atomic per workgroup. `lds`
+// holds one float per wave.
+TACO_DEV void ws_record_group(Workspace* ws, uint32_t e, float lane_max, float* lds) {
+  const float m = wave_max(lane_max);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_in_group();
+  if (lane == 0) lds[wave] = m;
+  lds_barrier();
+  if (wave == 0 && lane == 0) {
+    float g = lds[0];
+#pragma unroll
+    for (int w = 1; w < kBlockThreads / kWave; ++w) g = fmaxf(g, lds[w]);
+    TACO_AT_MAX(&ws->bank[e][blockIdx.x % kAccLines].amax, __float_as_uint(g));
+  }
+}
 
 }  // namespace taco

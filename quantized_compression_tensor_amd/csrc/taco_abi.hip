@@ -10,7 +10,9 @@ namespace {
 
 using namespace taco;
 
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// Largest tensor (rows * cols) a call accepts: 2^35 elements keeps every
+// one-wave-per-tile grid under 2^32 threads.
+constexpr int64_t kMaxElems = int64_t(1) << 35;
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 

@@ -97,6 +97,7 @@ def test_compress_validation():
     assert _st(comp, FP8, A + 2, 2, 128, 1.0, B_) == T.TACO_ERR_ALIGN
     assert _st(comp, FP8, A, 2, 128, 1.0, B_ + 8) == T.TACO_ERR_ALIGN
     assert _st(comp, FP8, A, -1, 128, 1.0, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 1 << 22, 1 << 14, 1.0, B_) == T.TACO_ERR_INVALID_ARG   # 2^36 elements: too large
     assert _st(comp, FP8, A, 2, 100, 1.0, B_) == T.TACO_ERR_SHAPE
     assert _st(comp, FP8, A, 2, 128, 0.0, B_) == T.TACO_ERR_WORKSPACE          # auto needs a workspace
     assert _st(comp, FP8, A, 2, 128, -1.0, B_) == T.TACO_ERR_WORKSPACE         # delayed needs one too

@@ -90,12 +90,11 @@ def test_compress_auto_scale_and_workspace(oc):
     buf, _ = gpu_compress(oc, bits, scale=T.TACO_SCALE_AUTO, ws=ws)
     assert_same(parse(buf, oc, *shape), ref, cid(oc))
     y = cd.transform(oc, bits)
-    calls, amax, slot = T.workspace_history(ws)
+    calls, amax, bank = T.workspace_history(ws)
     assert calls == 2                                     # pre-pass and compress both recorded
     assert np.float32(amax) == np.max(np.abs(y))          # recorded abs-max
     w = ws.cpu().numpy().view(np.uint32)
-    nxt = (slot + 1) % 3
-    assert (T.acc_lines(w)[:, nxt] == 0).all()                         # next call's slot is clear
+    assert (T.bank_lines(w)[(bank + 1) % 3] == 0).all()   # next call's bank is clear
 
 
 def test_compress_delayed_scale_uses_previous_call():
@@ -110,6 +109,39 @@ def test_compress_delayed_scale_uses_previous_call():
     g_prev = cd.auto_tensor_scale(cd.transform(oc, a))
     assert_same(parse(buf2, oc, *shape), oracle.compress(oc, b, tensor_scale=g_prev), "second: g from a")
     assert np.float32(T.workspace_history(ws)[1]) == np.max(np.abs(cd.transform(oc, b)))
+
+
+def _amax_of_transform(oc, bits, rows_per_step=2048):
+    """max |y| of the oracle's transform, a row slab at a time (the transform
+    acts on blocks inside a row, so slabs give the same maximum)."""
+    m = np.float32(0.0)
+    for r0 in range(0, bits.shape[0], rows_per_step):
+        m = max(m, np.max(np.abs(cd.transform(oc, bits[r0:r0 + rows_per_step]))))
+    return np.float32(m)
+
+
+def test_workspace_history_across_grid_sizes():
+    """One workspace in delayed-scale mode, calls whose grids differ: fewer
+    workgroups than ticket counters (37 x 1024), the persistent grid of small
+    tensors (64 x 4096) and the one-chunk-per-wave grid of large tensors
+    (32768 x 4096, the first size past 2^16 chunks of 2048). Every call's
+    tensor scale must come from the previous call's abs-max."""
+    oc = cd.Codec.fp8()
+    ws = new_workspace()
+    shapes = [(37, 1024), (32768, 4096), (64, 4096), (37, 1024)]
+    prev = np.float32(0.0)
+    for i, shape in enumerate(shapes):
+        print(f"[ws history] call {i}: {shape}", flush=True)
+        bits = bits_for(shape, seed=900 + i, sigma=0.02 * (i + 1))
+        g = cd.auto_tensor_scale(np.array([prev], dtype=np.float32))
+        buf, _ = gpu_compress(oc, bits, scale=T.TACO_SCALE_DELAYED, ws=ws)
+        got = parse(buf, oc, *shape)
+        assert np.float32(got["g"]) == g, f"call {i} {shape}: g {got['g']} != {g}"
+        if shape[0] * shape[1] <= 64 * 4096:
+            assert_same(got, oracle.compress(oc, bits, tensor_scale=g), f"call {i} {shape}")
+        prev = _amax_of_transform(oc, bits)
+        calls, amax, _ = T.workspace_history(ws)
+        assert calls == i + 1 and np.float32(amax) == prev, f"call {i}: history ({calls}, {amax}) != {prev}"
 
 
 @pytest.mark.parametrize("oc", ALL, ids=cid)
