@@ -110,7 +110,7 @@ typedef struct taco_layout_t {
 #define TACO_SCALE_AUTO 0.0f
 #define TACO_SCALE_DELAYED (-1.0f)
 #define TACO_MAX_SHARDS 16
-#define TACO_WORKSPACE_BYTES 16384
+#define TACO_WORKSPACE_BYTES 32768
 
 /* Layout of a compressed [rows, cols] tensor. Host only. */
 int taco_layout(taco_codec c, int64_t rows, int64_t cols, taco_layout_t* out);

@@ -30,7 +30,7 @@ TACO_FMT_INT8_ASYM = 4
 TACO_SCALE_AUTO = 0.0
 TACO_SCALE_DELAYED = -1.0
 TACO_MAX_SHARDS = 16
-TACO_WORKSPACE_BYTES = 16384
+TACO_WORKSPACE_BYTES = 32768
 
 # Entry points declared in include/taco.h (checked by the ABI tests).
 EXPORTS = (
@@ -218,7 +218,7 @@ def regions(buf, c, rows, cols):
     return codes, sc, aux, ten
 
 
-WS_TICKET_GROUPS = 16   # workspace ticket counters (kernel-side constants)
+WS_TICKET_GROUPS = 64   # workspace ticket counters (kernel-side constants)
 WS_BANK_LINES = 32      # workspace record lines per bank (three banks)
 WS_LINE = 32            # uint32 words per 128-byte line
 WS_SHARE_SHIFT = 24     # each call adds 2^24 to every ticket counter
@@ -228,8 +228,8 @@ def workspace_history(ws):
     """Read an FP8 tensor-scale workspace (a device tensor of
     TACO_WORKSPACE_BYTES) between calls: returns (calls made, abs-max recorded
     by the most recent call, that call's bank). Layout (uint32 words, 32 per
-    line): line 0 unused; line 1 + g, words 0-1: ticket counter g (16, uint64);
-    line 17 + 32 b + l, word 0: record line l of bank b (3 banks of 32).
+    line): line 0 unused; line 1 + g, words 0-1: ticket counter g (64, uint64);
+    line 65 + 32 b + l, word 0: record line l of bank b (3 banks of 32).
     Inspection only."""
     import numpy as np
     w = ws.detach().cpu().numpy().view(np.uint32).reshape(-1)

@@ -198,10 +198,10 @@ TACO_DEV float wave_max(float a) {
 // zero-filled once. Calls on one workspace are ordered (one stream), and any
 // call may run any grid.
 //
-// Call index. The workspace has 16 ticket counters; workgroup b adds to
-// counter b % 16, and the members of each counter add shares that total
+// Call index. The workspace has 64 ticket counters; workgroup b adds to
+// counter b % 64, and the members of each counter add shares that total
 // exactly 2^24 per call (2^24 / members each, the first member the
-// remainder; with fewer than 16 workgroups some take several counters). A counter therefore holds t * 2^24 when call t
+// remainder; with fewer than 64 workgroups some take several counters). A counter therefore holds t * 2^24 when call t
 // starts, and every workgroup's ticket (the value before its add) gives the
 // same t = ticket >> 24, whatever the grid.
 //
@@ -215,7 +215,7 @@ TACO_DEV float wave_max(float a) {
 // counter and record line is a 128-byte line of its own. Only the first wave of
 // a workgroup takes the ticket and reads the history; it hands t % 3 (and the
 // tensor scale) to the others through LDS.
-constexpr int kTicketGroups = 16;
+constexpr int kTicketGroups = 64;
 constexpr int kAccLines = 32;
 constexpr int kLineWords = 32;
 constexpr int kShareShift = 24;
@@ -241,8 +241,8 @@ static_assert(sizeof(Workspace) <= TACO_WORKSPACE_BYTES, "workspace size");
 
 // This workgroup's ticket (first wave, all lanes; lane 0 issues the add and
 // holds the result). The caller issues its data loads next and reads the
-// result only when it needs the call index. With fewer than 16 workgroups,
-// workgroup b also adds the whole 2^24 to every counter b + k * grid < 16
+// result only when it needs the call index. With fewer than 64 workgroups,
+// workgroup b also adds the whole 2^24 to every counter b + k * grid < 64
 // (k >= 1, lane k, not awaited), so every counter still advances by exactly
 // 2^24 per call.
 TACO_DEV unsigned long long ws_ticket(Workspace* ws) {

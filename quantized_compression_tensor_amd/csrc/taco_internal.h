@@ -131,7 +131,7 @@ constexpr int kReduceGroupsPerCU = TACO_REDUCE_GROUPS_PER_CU;
 static_assert(kReduceGroupsPerCU > 0, "reduce workgroups per CU");
 // Tiles per wave of the memory-bound reduce (one workgroup per 4 * this many).
 #ifndef TACO_REDUCE_TILES_PER_WAVE
-#define TACO_REDUCE_TILES_PER_WAVE 2
+#define TACO_REDUCE_TILES_PER_WAVE 1
 #endif
 constexpr int kReduceTilesPerWave = TACO_REDUCE_TILES_PER_WAVE;
 static_assert(kReduceTilesPerWave > 0, "tiles per wave");
