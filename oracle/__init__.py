@@ -24,7 +24,8 @@ Sources, cited by page title and the section / figure / equation on it:
   takes codes, zero point and scale), free parameters (group size 128; INT4
   reduce stage, INT8 gather stage).
 * [FP8] "FP8 Formats for Deep Learning" (cited in TACO's reference list) for
-  the E4M3 bit layout: bias 7, no infinities, S.1111.111 is NaN, max 448.
+  the E4M3 bit layout (bias 7, no infinities, S.1111.111 is NaN, max 448) and
+  the E5M2 one (bias 15, IEEE infinities and NaNs, max 57344).
 
 Precision. Every floating-point step is IEEE-754 binary32 with one
 round-to-nearest-even per operation and no fused multiply-add, in the stated
@@ -42,8 +43,9 @@ asymmetric codecs are pinned by closed forms, brute force and library
 cross-checks in ``tests/``. TACO's reshaping, ASH transform and dual-scale quantization are
 never defined on the pages (the referee on the TACO page says the reshaping
 and adaptive scales are "not quantified"), so ``compress_fp8_dual`` and its
-inverse are pinned only to the readings they implement: parity unpinned
-against the paper itself.
+inverse (with E4M3 or E5M2 codes) are pinned only to the readings they
+implement: parity unpinned against the paper itself. The E5M2 format itself
+is pinned like E4M3.
 """
 
 from .formats import (  # noqa: F401
@@ -51,12 +53,16 @@ from .formats import (  # noqa: F401
     f32_to_bf16_bits,
     decode_e4m3,
     encode_e4m3,
+    decode_e5m2,
+    encode_e5m2,
     pack_int4,
     unpack_int4,
 )
 from .hadamard import fwht, fwht_f64  # noqa: F401
 from .codecs import (  # noqa: F401
     FP8_DUAL,
+    FP8E5_DUAL,
+    FP8_FORMATS,
     INT8_SYM,
     INT4_ASYM,
     INT8_ASYM,

@@ -16,9 +16,12 @@ import numpy as np
 
 from .formats import (
     E4M3_MAX,
+    E5M2_MAX,
     bf16_bits_to_f32,
     decode_e4m3,
+    decode_e5m2,
     encode_e4m3,
+    encode_e5m2,
     f32_to_bf16_bits,
     pack_int4,
     unpack_int4,
@@ -31,6 +34,14 @@ FP8_DUAL = 1    # TACO: Hadamard blocks + tensor scale g + per-block power-of-tw
 INT8_SYM = 2    # EQuARX: symmetric abs-max int8, one float32 scale per 64 entries
 INT4_ASYM = 3   # FlashComm: asymmetric min/max, group 128, 4-bit codes packed two per byte
 INT8_ASYM = 4   # FlashComm: the same scheme at 8 bits, used for the gather stage
+FP8E5_DUAL = 5  # TACO's dual-scale scheme with E5M2 codes (the other FP8 format of Fig. 3)
+
+FP8_FORMATS = (FP8_DUAL, FP8E5_DUAL)
+# largest finite code value of each FP8 format, written 0.875 * 2^P
+FP8_MAX = {FP8_DUAL: E4M3_MAX, FP8E5_DUAL: E5M2_MAX}
+_FP8_P = {FP8_DUAL: 9, FP8E5_DUAL: 16}
+_FP8_ENC = {FP8_DUAL: encode_e4m3, FP8E5_DUAL: encode_e5m2}
+_FP8_DEC = {FP8_DUAL: decode_e4m3, FP8E5_DUAL: decode_e5m2}
 
 # Reading: the tensor scale g is kept within [2^-60, 2^60] so that g * 2^-k and
 # (1/g) * 2^k stay normal float32 numbers for every block exponent k.
@@ -56,6 +67,10 @@ class Codec:
     @staticmethod
     def fp8(block=128, hadamard=True):
         return Codec(FP8_DUAL, block, bool(hadamard))
+
+    @staticmethod
+    def fp8e5(block=128, hadamard=True):
+        return Codec(FP8E5_DUAL, block, bool(hadamard))
 
     @staticmethod
     def int8_sym(block=64):
@@ -91,7 +106,7 @@ class Compressed:
 
 # ---------------------------------------------------------------- TACO FP8 --
 
-def block_exponent(m):
+def block_exponent(m, fmt=FP8_DUAL):
     """Per-block power-of-two exponent k of the dual-scale reading.
 
     Reading of [TACO]'s Dual-Scale Quantization (named in the abstract and
@@ -101,30 +116,33 @@ def block_exponent(m):
     [-64, 63]; k = 0 for an all-zero block; an infinite m has no such k and
     gets the lower clamp. With m = f * 2^E (f in [0.5, 1)) the largest k is
     9 - E if f <= 0.875 (448 = 0.875 * 2^9) and 8 - E otherwise, which puts
-    the block maximum in (224, 448].
+    the block maximum in (224, 448]. For E5M2 the same rule holds with
+    57344 = 0.875 * 2^16: k = 16 - E or 15 - E, the maximum in (28672, 57344].
     """
+    P = _FP8_P[fmt]
     m = np.asarray(m, dtype=np.float32).astype(np.float64)
     fin = np.isfinite(m) & (m > 0)
     f, E = np.frexp(np.where(fin, m, 1.0))
-    k = np.where(f <= 0.875, 9, 8) - E.astype(np.int64)
+    k = np.where(f <= 0.875, P, P - 1) - E.astype(np.int64)
     k = np.clip(k, K_MIN, K_MAX)
     k = np.where(m == 0, 0, k)
     k = np.where(np.isinf(m), K_MIN, k)
     return k.astype(np.int64)
 
 
-def auto_tensor_scale(y):
+def auto_tensor_scale(y, fmt=FP8_DUAL):
     """Tensor scale g from the data (reading of [TACO] Fig. 7 "adaptive rescaling").
 
-    g = RN(A / 448) with A = max |y| over the whole tensor in the transformed
-    domain, so the tensor maximum maps onto the largest E4M3 value; g = 1 for
-    an all-zero tensor; g is clamped to [2^-60, 2^60].
+    g = RN(A / M) with A = max |y| over the whole tensor in the transformed
+    domain and M the format's largest value (448 for E4M3, 57344 for E5M2), so
+    the tensor maximum maps onto the largest code; g = 1 for an all-zero
+    tensor; g is clamped to [2^-60, 2^60].
     """
     y = np.asarray(y, dtype=np.float32)
     A = np.max(np.abs(y)) if y.size else F32(0)
     if A == 0:
         return F32(1.0)
-    g = F32(A) / F32(E4M3_MAX)
+    g = F32(A) / F32(FP8_MAX[fmt])
     return F32(min(max(g, G_MIN), G_MAX))
 
 
@@ -132,8 +150,8 @@ def sum_tensor_scales(gs):
     """Tensor scale of a sum of shards: g' = g_0 + g_1 + ... in order, clamped.
 
     Reading: the pages do not say how the gather-stage FP8 tensor is scaled.
-    Since every |dequantized value| <= 448 * 2^-k * g_r, the sum of the g_r
-    bounds the sum without a second pass over it.
+    Since every |dequantized value| <= M * 2^-k * g_r (M = 448 or 57344), the
+    sum of the g_r bounds the sum without a second pass over it.
     """
     acc = F32(0)
     for g in gs:
@@ -141,12 +159,12 @@ def sum_tensor_scales(gs):
     return F32(min(max(acc, G_MIN), G_MAX))
 
 
-def _quantize_fp8_dual(y, g, B):
-    """Dual-scale E4M3 quantization of transformed values y (float32, flat).
+def _quantize_fp8_dual(y, g, B, fmt=FP8_DUAL):
+    """Dual-scale FP8 quantization of transformed values y (float32, flat).
 
     w = RN(y * RN(1/g)); a w that is exactly zero is +0 (reading: the sign of
     an exact zero carries nothing); m = max |w| per block; k from
-    ``block_exponent``; v = w * 2^k; q = E4M3 code of v.
+    ``block_exponent``; v = w * 2^k; q = E4M3 (or E5M2) code of v.
     """
     g = F32(g)
     inv_g = F32(F32(1.0) / g)
@@ -154,15 +172,15 @@ def _quantize_fp8_dual(y, g, B):
     w = yb * inv_g
     w = np.where(yb == 0, F32(0.0), w).astype(np.float32)
     m = np.max(np.abs(w), axis=1) if w.size else np.zeros(0, np.float32)
-    k = block_exponent(m)
+    k = block_exponent(m, fmt)
     v = np.ldexp(w, k[:, None]).astype(np.float32)
-    q = encode_e4m3(v)
+    q = _FP8_ENC[fmt](v)
     return q.reshape(-1), k.astype(np.int8), v.reshape(-1)
 
 
-def _dequantize_fp8_dual(codes, k, g, B):
+def _dequantize_fp8_dual(codes, k, g, B, fmt=FP8_DUAL):
     """x' = RN(dec(q) * 2^-k * g): dec(q) * 2^-k is exact, one rounding for g."""
-    d = decode_e4m3(codes).reshape(-1, B)
+    d = _FP8_DEC[fmt](codes).reshape(-1, B)
     t = np.ldexp(d, -k.astype(np.int64)[:, None]).astype(np.float32)
     return (t * F32(g)).astype(np.float32).reshape(-1)
 
@@ -241,7 +259,7 @@ def _dequantize_asym(q, s, z, B):
 
 def _check(codec, cols):
     B = codec.block
-    if codec.format == FP8_DUAL:
+    if codec.format in FP8_FORMATS:
         assert B in (16, 32, 64, 128), "FP8 block must be 16, 32, 64 or 128"
     elif codec.format == INT8_SYM:
         assert B == 64, "INT8_SYM block is 64"
@@ -266,9 +284,9 @@ def quantize_values(codec, y, rows, cols, tensor_scale=None):
     _check(codec, cols)
     y = np.ascontiguousarray(y, dtype=np.float32).reshape(-1)
     B = codec.block
-    if codec.format == FP8_DUAL:
-        g = auto_tensor_scale(y) if tensor_scale is None else F32(tensor_scale)
-        q, k, v = _quantize_fp8_dual(y, g, B)
+    if codec.format in FP8_FORMATS:
+        g = auto_tensor_scale(y, codec.format) if tensor_scale is None else F32(tensor_scale)
+        q, k, v = _quantize_fp8_dual(y, g, B, codec.format)
         return _pack(codec, rows, cols, q, k, None, g, v)
     if codec.format == INT8_SYM:
         q, s, t = _quantize_int8_sym(y, B)
@@ -284,7 +302,7 @@ def transform(codec, x_bits):
     viewed as [n / B, B] blocks along the hidden dimension (no data movement).
     """
     u = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16)).reshape(-1)
-    if codec.format == FP8_DUAL and codec.hadamard:
+    if codec.format in FP8_FORMATS and codec.hadamard:
         return fwht(u, codec.block)
     return u
 
@@ -306,8 +324,8 @@ def compress(codec, x_bits, tensor_scale=None):
 def dequantize(c: Compressed):
     """Dequantize one shard to float32 (FP8_DUAL: still in the transformed domain)."""
     B = c.codec.block
-    if c.codec.format == FP8_DUAL:
-        return _dequantize_fp8_dual(c.codes, c.scale, c.tensor_scale, B)
+    if c.codec.format in FP8_FORMATS:
+        return _dequantize_fp8_dual(c.codes, c.scale, c.tensor_scale, B, c.codec.format)
     if c.codec.format == INT8_SYM:
         return _dequantize_int8_sym(c.codes.view(np.int8), c.scale, B)
     q = unpack_int4(c.codes) if c.codec.format == INT4_ASYM else c.codes
@@ -316,6 +334,7 @@ def dequantize(c: Compressed):
 
 ALLOWED_PAIRS = {
     (FP8_DUAL, FP8_DUAL),
+    (FP8E5_DUAL, FP8E5_DUAL),
     (INT8_SYM, INT8_SYM),
     (INT4_ASYM, INT8_ASYM),
     (INT8_ASYM, INT8_ASYM),
@@ -324,7 +343,7 @@ ALLOWED_PAIRS = {
 
 def check_pair(cin: Codec, cout: Codec):
     assert (cin.format, cout.format) in ALLOWED_PAIRS, "unsupported format pair"
-    if cin.format == FP8_DUAL:
+    if cin.format in FP8_FORMATS:
         assert cin.block == cout.block and cin.hadamard == cout.hadamard
     else:
         assert cin.block == cout.block
@@ -355,7 +374,7 @@ def decompress_reduce(shards: List[Compressed], out_codec: Optional[Codec] = Non
     if out_codec is not None:
         check_pair(c0.codec, out_codec)
         g = None
-        if out_codec.format == FP8_DUAL:
+        if out_codec.format in FP8_FORMATS:
             g = sum_tensor_scales([s.tensor_scale for s in shards])
         rq = quantize_values(out_codec, acc, c0.rows, c0.cols, g)
     return acc.reshape(c0.rows, c0.cols), rq
@@ -407,7 +426,7 @@ def decode(c: Compressed, out_dtype="f32"):
     Returns float32 [rows, cols], or bf16 bit patterns if out_dtype == "bf16".
     """
     y = dequantize(c)
-    if c.codec.format == FP8_DUAL and c.codec.hadamard:
+    if c.codec.format in FP8_FORMATS and c.codec.hadamard:
         B = c.codec.block
         t = fwht(y, B)
         x = np.ldexp(t, -int(np.log2(B))).astype(np.float32)

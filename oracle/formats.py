@@ -1,4 +1,4 @@
-"""Number formats used on the wire: bf16 input, FP8 E4M3 codes, packed INT4.
+"""Number formats used on the wire: bf16 input, FP8 E4M3 / E5M2 codes, packed INT4.
 
 Test infrastructure only (see the package docstring).
 """
@@ -81,6 +81,65 @@ def encode_e4m3(v):
 
     code = np.where(a < E4M3_MIN_NORMAL, m_sub, code_norm) | sign
     code = np.where(nan, E4M3_NAN, code)
+    return code.astype(np.uint8)
+
+
+# E5M2 constants from the format definition ([FP8]; [TACO] Fig. 3 sets E5M2
+# beside E4M3): 5 exponent bits with bias 15, 2 mantissa bits, IEEE-style
+# infinities and NaNs in the top exponent.
+E5M2_BIAS = 15
+E5M2_MAX = 57344.0        # S.11110.11
+E5M2_MIN_NORMAL = 2.0 ** -14
+E5M2_MIN_SUBNORMAL = 2.0 ** -16
+E5M2_INF = 0x7C           # S.11111.00
+E5M2_NAN = 0x7F           # S.11111.11; the encoder below emits the positive one
+
+
+def decode_e5m2(codes):
+    """Value of each E5M2 code, written out from the bit fields ([FP8]).
+
+    sign s, exponent field e (5 bits, bias 15), mantissa m (2 bits):
+    e == 0 -> (-1)^s * m * 2^-16 (subnormal); e == 31 -> +-inf (m == 0) or NaN;
+    otherwise (-1)^s * (1 + m/4) * 2^(e-15).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 2) & 0x1F
+    m = c & 3
+    mag = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.exp2(np.minimum(e, 30) - E5M2_BIAS))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    val = np.where(s == 1, -mag, mag)
+    return val.astype(np.float32)
+
+
+def encode_e5m2(v):
+    """Round float32 values to E5M2 codes: nearest, ties to even, saturating.
+
+    The same reading as ``encode_e4m3`` (the pages fix neither rounding nor
+    overflow): ties go to the even mantissa; finite magnitudes above 57344 and
+    infinities saturate to +-57344 (no infinity is produced); NaN encodes as
+    0x7F; the sign bit is kept for values that round to zero.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    nan = np.isnan(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    a = np.minimum(np.abs(v.astype(np.float64)), E5M2_MAX)
+    a = np.where(nan, 0.0, a)
+
+    # subnormal range: a < 2^-14, step 2^-16; m == 4 lands on the smallest normal
+    m_sub = np.rint(a * 65536.0).astype(np.int64)
+
+    # normal range: a = f * 2^E with f in [0.5, 1); exponent e = E - 1
+    _, E = np.frexp(np.where(a > 0, a, 1.0))
+    e = E.astype(np.int64) - 1
+    m = np.rint(np.ldexp(a, (2 - e))).astype(np.int64) - 4      # in [0, 4]
+    carry = m == 4
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    code_norm = ((e + E5M2_BIAS) << 2) | m
+
+    code = np.where(a < E5M2_MIN_NORMAL, m_sub, code_norm) | sign
+    code = np.where(nan, E5M2_NAN, code)
     return code.astype(np.uint8)
 
 

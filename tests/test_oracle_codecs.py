@@ -12,7 +12,7 @@ from oracle import formats as fm
 from oracle.hadamard import fwht
 import workloads as W
 from tests.conftest import read_golden
-from tests.test_oracle_formats import nearest_code_bruteforce
+from tests.test_oracle_formats import nearest_code_bruteforce, nearest_e5m2_bruteforce
 
 F32 = np.float32
 
@@ -165,6 +165,97 @@ def test_fp8_saturates_when_block_exponent_clamps():
     c = oracle.compress(cd.Codec.fp8(128, False), bits_of(x), tensor_scale=F32(2.0 ** -60))
     assert c.scale[0] == -64
     assert (c.codes == 0x7E).all()
+
+
+# ------------------------------------------------------- FP8 dual, E5M2 --
+
+def k_bruteforce_e5(m):
+    """Largest k in [-64, 63] with m * 2^k <= 57344 (exact in float64); -64 if none."""
+    m = float(m)
+    if m == 0.0:
+        return 0
+    best = -64
+    for k in range(-64, 64):
+        if m * 2.0 ** k <= 57344.0:
+            best = k
+    return best
+
+
+def test_block_exponent_e5m2_bruteforce_and_range():
+    m = np.concatenate([k_probe_values(), np.array([57344.0, 28672.0, 57345.0, 28671.0], np.float32)])
+    got = cd.block_exponent(m, cd.FP8E5_DUAL)
+    want = np.array([k_bruteforce_e5(v) for v in m])
+    assert (got == want).all(), m[got != want]
+    v = m.astype(np.float64) * np.exp2(got.astype(np.float64))
+    live = (m > 0) & (got > -64) & (got < 63)
+    assert np.all(v[live] <= 57344.0) and np.all(v[live] > 28672.0)
+
+
+@pytest.mark.parametrize("B", [16, 128])
+@pytest.mark.parametrize("gexp", [0, 4])
+def test_fp8e5_dual_bruteforce_small_integers(B, gexp):
+    """As for E4M3: exact FWHT and power-of-two scalings, so every code must be
+    the brute-force nearest E5M2 code of y * 2^(k - gexp)."""
+    rng = np.random.default_rng(B + 11 * (gexp + 3))
+    x = rng.integers(-9, 10, size=(3, 2 * B)).astype(np.float32)
+    x[0, :B] = 0.0
+    x[1, :B] = 0.0
+    x[1, 3] = 5.0
+    codec = cd.Codec.fp8e5(B, True)
+    c = oracle.compress(codec, bits_of(x), tensor_scale=F32(2.0 ** gexp))
+    y = fwht(x.reshape(-1), B).astype(np.float64).reshape(-1, B)
+    w = y * 2.0 ** -gexp
+    kk = np.array([k_bruteforce_e5(F32(np.max(np.abs(b)))) for b in w])
+    v = (w * np.exp2(kk)[:, None]).reshape(-1)
+    v = np.where(y.reshape(-1) == 0, 0.0, v)
+    assert (c.scale.astype(int) == kk).all()
+    assert (c.codes == nearest_e5m2_bruteforce(v.astype(np.float32))).all()
+
+
+def test_fp8e5_dual_auto_scale_and_error_bound():
+    """g = RN(A / 57344); TACO Eq. (3) with m = 2 at the scaled value, carried
+    back through the exact power-of-two and g scalings."""
+    x = W.random_bits((128, 512), seed=19, sigma=0.02)
+    codec = cd.Codec.fp8e5()
+    c = oracle.compress(codec, x)
+    y = cd.transform(codec, x).astype(np.float64)
+    assert c.tensor_scale == F32(F32(np.max(np.abs(y))) / F32(57344.0))
+    dq = oracle.dequantize(c).astype(np.float64)
+    av = np.abs(c.prequant.astype(np.float64))
+    ulp = np.where(av >= 2.0 ** -14, np.exp2(np.floor(np.log2(np.maximum(av, 1e-300))) - 2), 2.0 ** -16)
+    k = np.repeat(c.scale.astype(np.float64), 128)
+    g = float(c.tensor_scale)
+    bound = (ulp / 2) * 2.0 ** -k * g + 2 * 2.0 ** -24 * np.abs(y) + 2.0 ** -24 * np.abs(dq)
+    assert np.all(np.abs(dq - y) <= bound * (1 + 1e-9))
+    vmax = np.max(av.reshape(-1, 128), axis=1)
+    assert np.all(vmax <= 57344.0) and np.all(vmax > 28672.0)
+
+
+def test_fp8e5_dual_rel_mse_statistics():
+    """Two mantissa bits: about 2^-4 / 12 * E[(2^e / x)^2] ~ 2.8e-3, four times
+    the E4M3 figure."""
+    x = W.random_bits((256, 1024), seed=21, sigma=0.02)
+    r5 = oracle.rel_mse(oracle.decode(oracle.compress(cd.Codec.fp8e5(), x)), fm.bf16_bits_to_f32(x))
+    r4 = oracle.rel_mse(oracle.decode(oracle.compress(cd.Codec.fp8(), x)), fm.bf16_bits_to_f32(x))
+    assert 1.6e-3 < r5 < 4.4e-3, r5
+    assert 3.0 < r5 / r4 < 5.0, (r5, r4)
+
+
+def test_fp8e5_saturates_when_block_exponent_clamps():
+    x = np.full((1, 128), 1.0e12, np.float32)
+    c = oracle.compress(cd.Codec.fp8e5(128, False), bits_of(x), tensor_scale=F32(2.0 ** -60))
+    assert c.scale[0] == -64
+    assert (c.codes == 0x7B).all()
+
+
+def test_fp8e5_reduce_requant_pair_and_sum_scale():
+    xs = [W.random_bits((16, 256), seed=40 + r, sigma=0.02) for r in range(3)]
+    codec = cd.Codec.fp8e5()
+    shards = [oracle.compress(codec, x) for x in xs]
+    acc, rq = oracle.decompress_reduce(shards, codec)
+    assert rq.tensor_scale == cd.sum_tensor_scales([s.tensor_scale for s in shards])
+    with pytest.raises(AssertionError):
+        oracle.decompress_reduce(shards, cd.Codec.fp8())        # E5M2 -> E4M3 is not a pair
 
 
 # ---------------------------------------------------------- INT formats --

@@ -72,9 +72,10 @@ def test_skipped_butterfly_stage_is_caught(monkeypatch):
 
 def test_exponent_threshold_and_offset_errors_are_caught(monkeypatch):
     real = cd.block_exponent
-    monkeypatch.setattr(cd, "block_exponent", lambda m: real(m) + 1)
+    monkeypatch.setattr(cd, "block_exponent", lambda m, *f: real(m, *f) + 1)
     assert _fails(TC.test_block_exponent_bruteforce)
-    monkeypatch.setattr(cd, "block_exponent", lambda m: np.where(np.asarray(m) > 0, real(np.asarray(m) * np.float32(0.99)), 0))
+    monkeypatch.setattr(cd, "block_exponent",
+                        lambda m, *f: np.where(np.asarray(m) > 0, real(np.asarray(m) * np.float32(0.99), *f), 0))
     assert _fails(TC.test_block_exponent_bruteforce)
 
 
@@ -100,7 +101,7 @@ def test_asym_zero_point_sign_error_is_caught(monkeypatch):
 
 
 def test_dequant_dropping_tensor_scale_is_caught(monkeypatch):
-    def bad(codes, k, g, B):
+    def bad(codes, k, g, B, fmt=cd.FP8_DUAL):
         d = fm.decode_e4m3(codes).reshape(-1, B)
         return np.ldexp(d, -k.astype(np.int64)[:, None]).astype(np.float32).reshape(-1)
     monkeypatch.setattr(cd, "_dequantize_fp8_dual", bad)
@@ -143,3 +144,32 @@ def test_ring_hop_mistakes_are_caught(monkeypatch, sign, keep):
     monkeypatch.setattr(oracle, "ring_hop", _bad_ring_hop(sign, keep))
     assert _fails(TR.test_hop_sum_is_exact_when_every_term_is_representable)
     assert _fails(TR.test_ring_mse_matches_the_reported_values)
+
+
+def test_e5m2_encoder_mistakes_are_caught(monkeypatch):
+    real = fm.encode_e5m2
+
+    def ties_away(v):
+        v = np.asarray(v, np.float32)
+        return real(np.where(np.isfinite(v), v * np.float32(1 + 2 ** -22), v))
+    monkeypatch.setattr(fm, "encode_e5m2", ties_away)
+    assert _fails(TF.test_e5m2_rounding_golden)
+
+    def no_saturation(v):
+        c = real(v)
+        big = np.abs(np.asarray(v, np.float32)) > 57344
+        return np.where(big, np.uint8(0x7C) | (c & 0x80), c).astype(np.uint8)
+    monkeypatch.setattr(fm, "encode_e5m2", no_saturation)
+    assert _fails(TF.test_e5m2_special_values)
+
+
+def test_e5m2_decoder_bias_error_is_caught(monkeypatch):
+    real = fm.decode_e5m2
+    monkeypatch.setattr(fm, "decode_e5m2", lambda c: (real(c) * np.float32(2.0)).astype(np.float32))
+    assert _fails(TF.test_e5m2_landmarks_golden)
+
+
+def test_e5m2_exponent_with_the_e4m3_limit_is_caught(monkeypatch):
+    real = cd.block_exponent
+    monkeypatch.setattr(cd, "block_exponent", lambda m, *f: real(m))
+    assert _fails(TC.test_block_exponent_e5m2_bruteforce_and_range)
