@@ -72,11 +72,18 @@ extern "C" {
  *                    low nibble), float32 scale s and uint8 zero point z per
  *                    group of 128 (value = (q - z) * s).
  * TACO_FMT_INT8_ASYM [FlashComm] the same at 8 bits (gather stage).
+ * TACO_FMT_FP8E5_DUAL the TACO dual-scale scheme with E5M2 codes instead of
+ *                    E4M3 ([TACO] Fig. 3 sets E5M2 beside E4M3; bit layout of
+ *                    "FP8 Formats for Deep Learning", in TACO's reference list):
+ *                    the block exponent k brings each block maximum into
+ *                    (28672, 57344], AUTO g = abs-max / 57344; block, hadamard,
+ *                    layout, workspace and scale modes as TACO_FMT_FP8_DUAL.
  */
 #define TACO_FMT_FP8_DUAL 1
 #define TACO_FMT_INT8_SYM 2
 #define TACO_FMT_INT4_ASYM 3
 #define TACO_FMT_INT8_ASYM 4
+#define TACO_FMT_FP8E5_DUAL 5
 
 typedef struct taco_codec {
   int32_t format;   /* TACO_FMT_* */
@@ -99,11 +106,11 @@ typedef struct taco_layout_t {
   int64_t total_bytes;
 } taco_layout_t;
 
-/* tensor_scale values for taco_compress / taco_requantize (FP8 only):
+/* tensor_scale values for taco_compress / taco_requantize (FP8 formats only):
  *   > 0   use this g; it must lie in [2^-60, 2^60]
  *   AUTO  g from this tensor: an abs-max pass over the transformed values
- *         first, g = absmax / 448 (1 for an all-zero tensor), clamped to
- *         [2^-60, 2^60]. Needs a workspace.
+ *         first, g = absmax / 448 (E5M2: / 57344; 1 for an all-zero tensor),
+ *         clamped to [2^-60, 2^60]. Needs a workspace.
  *   DELAYED  g from the abs-max the workspace recorded in its previous call
  *         (1 if none): one pass; the history lives in the caller's workspace.
  * Every FP8 call given a workspace records its own abs-max there.          */
@@ -146,7 +153,7 @@ int taco_compress_debug(taco_codec c, const void* x_bf16, int64_t rows, int64_t 
  * chunks). Then, optionally,
  *   sum_fp32     device float32 [rows, cols] receives acc (nullable)
  *   requant_out  device buffer in c_out's layout receives acc re-quantized for
- *                the gather stage (nullable): FP8 -> FP8 with tensor scale
+ *                the gather stage (nullable): FP8 -> FP8 (same code format) with tensor scale
  *                g' = g_0 + ... + g_{n-1} and no second transform (the
  *                transform is linear and shared by all shards); INT8_SYM ->
  *                INT8_SYM; INT4_ASYM -> INT8_ASYM; INT8_ASYM -> INT8_ASYM. FP8
@@ -189,9 +196,11 @@ int taco_requantize(taco_codec c_out, const float* x_fp32, int64_t rows, int64_t
 int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
                     hipStream_t stream);
 
-/* Test hook: the device's E4M3 encoder (the one every FP8 kernel uses) on n
- * float32 values; codes are 1 byte each. Same argument rules as above. */
+/* Test hooks: the device's E4M3 / E5M2 encoder (the one every FP8 kernel of
+ * that format uses) on n float32 values; codes are 1 byte each. Same argument
+ * rules as above. */
 int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
+int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
 /* Name of a status code. Host only; never returns NULL. */
 const char* taco_status_string(int status);

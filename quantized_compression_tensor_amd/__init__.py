@@ -26,6 +26,8 @@ TACO_FMT_FP8_DUAL = 1
 TACO_FMT_INT8_SYM = 2
 TACO_FMT_INT4_ASYM = 3
 TACO_FMT_INT8_ASYM = 4
+TACO_FMT_FP8E5_DUAL = 5
+FP8_FORMATS = (TACO_FMT_FP8_DUAL, TACO_FMT_FP8E5_DUAL)
 
 TACO_SCALE_AUTO = 0.0
 TACO_SCALE_DELAYED = -1.0
@@ -36,7 +38,7 @@ TACO_WORKSPACE_BYTES = 32768
 EXPORTS = (
     "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
     "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
-    "taco_e4m3_encode", "taco_status_string",
+    "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string",
 )
 
 
@@ -89,6 +91,7 @@ def _load():
         "taco_requantize": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
         "taco_decompress": (ctypes.c_int, [C, P, I64, I64, P, I32, P]),
         "taco_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
+        "taco_e5m2_encode": (ctypes.c_int, [P, P, I64, P]),
         "taco_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -196,6 +199,10 @@ def taco_e4m3_encode(x, codes, n, stream=None):
     return _check(_lib.taco_e4m3_encode(_ptr(x), _ptr(codes), n, _stream(stream)), "taco_e4m3_encode")
 
 
+def taco_e5m2_encode(x, codes, n, stream=None):
+    return _check(_lib.taco_e5m2_encode(_ptr(x), _ptr(codes), n, _stream(stream)), "taco_e5m2_encode")
+
+
 # ------------------------------------------------- buffer plumbing (torch) --
 
 def empty_compressed(c, rows, cols, device="cuda"):
@@ -212,7 +219,7 @@ def regions(buf, c, rows, cols):
     L = taco_layout(c, rows, cols)
     codes = buf[L.codes_off:L.codes_off + L.codes_bytes]
     sc = buf[L.scale_off:L.scale_off + L.scale_bytes]
-    sc = sc.view(torch.int8) if c.format == TACO_FMT_FP8_DUAL else sc.view(torch.float32)
+    sc = sc.view(torch.int8) if c.format in FP8_FORMATS else sc.view(torch.float32)
     aux = buf[L.aux_off:L.aux_off + L.aux_bytes]
     ten = buf[L.tensor_off:L.tensor_off + L.tensor_bytes].view(torch.float32)
     return codes, sc, aux, ten

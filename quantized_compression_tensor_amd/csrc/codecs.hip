@@ -86,28 +86,29 @@ struct LaneCodes {
 // FP8 dual-scale on values already in the codec's domain. m = max|a| / g,
 // k = block exponent, each value scaled by the exact (1/g) * 2^k; an exact
 // zero becomes +0 through the +0 addend of the fused multiply-add.
-template <int B>
+template <int B, bool E5>
 TACO_DEV LaneCodes quant_fp8(float* a, float inv_g, float* pre) {
+  using F = Fp8Code<E5>;
   constexpr int G = B / kLaneElems;
   LaneCodes r;
   const float M = group_max<G>(absmax16(a));
   const float m = M * inv_g;
-  r.k = block_exponent(m);
+  r.k = block_exponent<E5>(m);
   const float c = inv_g * pow2f(r.k);
 #pragma unroll
   for (int i = 0; i < 16; ++i) a[i] = fmaf(a[i], c, 0.0f);
-  if (__builtin_expect(m * pow2f(r.k) > kE4M3Max, 0)) {
+  if (__builtin_expect(m * pow2f(r.k) > F::kMax, 0)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = sat448(a[i]);
+    for (int i = 0; i < 16; ++i) a[i] = sat_fp8<E5>(a[i]);
   }
   if (pre) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pre[i] = a[i];
   }
-  r.q.x = e4m3_pack4(a[0], a[1], a[2], a[3]);
-  r.q.y = e4m3_pack4(a[4], a[5], a[6], a[7]);
-  r.q.z = e4m3_pack4(a[8], a[9], a[10], a[11]);
-  r.q.w = e4m3_pack4(a[12], a[13], a[14], a[15]);
+  r.q.x = F::pack4(a[0], a[1], a[2], a[3]);
+  r.q.y = F::pack4(a[4], a[5], a[6], a[7]);
+  r.q.z = F::pack4(a[8], a[9], a[10], a[11]);
+  r.q.w = F::pack4(a[12], a[13], a[14], a[15]);
   r.s = 0.0f; r.z = 0;
   return r;
 }
@@ -174,7 +175,7 @@ TACO_DEV LaneCodes quant_asym(const float* a, float* pre) {
 
 template <int FMT, int B>
 TACO_DEV LaneCodes quant_lane(float* a, float inv_g, float* pre) {
-  if constexpr (FMT == kFP8) return quant_fp8<B>(a, inv_g, pre);
+  if constexpr (is_fp8(FMT)) return quant_fp8<B, FMT == kFP8E5>(a, inv_g, pre);
   else if constexpr (FMT == kINT8S) return quant_int8_sym(a, pre);
   else if constexpr (FMT == kINT4A) return quant_asym<4>(a, pre);
   else return quant_asym<8>(a, pre);
@@ -201,7 +202,7 @@ TACO_DEV LaneIn<FMT, B> load_in(const uint8_t* codes, const void* scale, const u
     r.q = *reinterpret_cast<const uint4*>(codes + e0);
   }
   r.z = 0;
-  if constexpr (FMT == kFP8) {
+  if constexpr (is_fp8(FMT)) {
     const int k = static_cast<const int8_t*>(scale)[blk];
     r.s = (*g_hdr) * pow2f(-k);
   } else {
@@ -228,9 +229,10 @@ TACO_DEV float sbyte(uint32_t w, int b) { return (float)(int)(int8_t)(uint8_t)(w
 //  INT8 asymmetric: (q - z) * s with q - z formed in float (exact).
 template <int FMT, int B>
 TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
-  if constexpr (FMT == kFP8) {
-    e4m3_unpack4(in.q.x, d); e4m3_unpack4(in.q.y, d + 4);
-    e4m3_unpack4(in.q.z, d + 8); e4m3_unpack4(in.q.w, d + 12);
+  if constexpr (is_fp8(FMT)) {
+    using F = Fp8Code<FMT == kFP8E5>;
+    F::unpack4(in.q.x, d); F::unpack4(in.q.y, d + 4);
+    F::unpack4(in.q.z, d + 8); F::unpack4(in.q.w, d + 12);
 #pragma unroll
     for (int i = 0; i < 16; ++i) d[i] = d[i] * in.s;
   } else if constexpr (FMT == kINT8S) {
@@ -293,7 +295,7 @@ TACO_DEV void store_lane(const LaneCodes& r, int64_t e0, uint8_t* codes, void* s
   }
   if (((threadIdx.x & (kWave - 1)) & (G - 1)) == 0) {
     const int64_t blk = e0 / B;
-    if constexpr (FMT == kFP8) {
+    if constexpr (is_fp8(FMT)) {
       static_cast<int8_t*>(scale)[blk] = (int8_t)r.k;
     } else {
       static_cast<float*>(scale)[blk] = r.s;
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float inv_g = 0.0f;
   uint32_t e = 0;
-  if constexpr (FMT == kFP8) {
+  if constexpr (is_fp8(FMT)) {
     __shared__ uint32_t lds_e;
     __shared__ float lds_g;
     float g = a.g;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
       if (wave_in_group() == 0) {
         const uint32_t ee = ws_bank_of(ws_ticket(a.ws));
         float gg = a.g;
-        if (a.g_from_ws) gg = tensor_scale_from_amax(ws_prev_amax(a.ws, ee));
+        if (a.g_from_ws) gg = tensor_scale_from_amax<FMT == kFP8E5>(ws_prev_amax(a.ws, ee));
         if (blockIdx.x == 0) ws_clear_next(a.ws, ee);
         if (lane == 0) { lds_e = ee; lds_g = gg; }
       }
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
-    if constexpr (FMT == kFP8) run_max = fmaxf(run_max, absmax16(v));
+    if constexpr (is_fp8(FMT)) run_max = fmaxf(run_max, absmax16(v));
     float pre[16];
     LaneCodes r = quant_lane<FMT, B>(v, inv_g, DEBUG ? pre : nullptr);
     if (valid) {
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
       }
     }
   }
-  if constexpr (FMT == kFP8) {
+  if constexpr (is_fp8(FMT)) {
     if (a.ws != nullptr) {
       __shared__ float lds_m[kBlockThreads / kWave];
       ws_record_group(a.ws, e, run_max, lds_m);
@@ -452,7 +454,7 @@ TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int n) {
   constexpr bool ASYM = FMT == kINT4A || FMT == kINT8A;
   ShardRsrc<FMT, B> s;
   s.codes = make_rsrc32(a.in.codes[r], live ? (FMT == kINT4A ? n / 2 : n) : 0);
-  s.meta = make_rsrc32(a.in.scale[r], live ? (FMT == kFP8 ? (nb + 3) & ~3 : (ASYM ? a.zero_rel + nb : 4 * nb)) : 0);
+  s.meta = make_rsrc32(a.in.scale[r], live ? (is_fp8(FMT) ? (nb + 3) & ~3 : (ASYM ? a.zero_rel + nb : 4 * nb)) : 0);
   return s;
 }
 
@@ -469,7 +471,7 @@ TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, float g,
     r.q = bload128<kNT>(s.codes, e0, 0);
   }
   r.z = 0;
-  if constexpr (FMT == kFP8) {
+  if constexpr (is_fp8(FMT)) {
     // the aligned dword holding the exponent byte (the resource is rounded up
     // to whole dwords, inside the region's padding)
     const uint32_t w = bload32(s.meta, blk & ~3, 0);
@@ -486,7 +488,7 @@ template <int FIN, int BIN, int NMAX>
 struct ReduceGroup {
   // shards per step: four for FP8 from eight shards on (more bytes per step
   // measured faster), two otherwise (fewer registers, more resident waves)
-  static constexpr int GRP = NMAX == 2 ? 1 : (FIN == kFP8 && NMAX >= 8 ? 4 : 2);
+  static constexpr int GRP = NMAX == 2 ? 1 : (is_fp8(FIN) && NMAX >= 8 ? 4 : 2);
   static constexpr int NG = NMAX / GRP;                 // steps per tile (>= 2)
   LaneIn<FIN, BIN> in[GRP];
 
@@ -501,7 +503,7 @@ struct ReduceGroup {
     for (int u = 0; u < GRP; ++u) {
       const int r = grp * GRP + u;
       float g = 0.0f;
-      if constexpr (FIN == kFP8) g = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), r));
+      if constexpr (is_fp8(FIN)) g = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), r));
       in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r, n), e0, g, a.zero_rel);
     }
   }
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   const int stride = (int)gridDim.x * (kBlockThreads / kWave);
   const bool rq = a.rq_codes != nullptr;
   float glane = 0.0f;
-  if constexpr (FIN == kFP8) {
+  if constexpr (is_fp8(FIN)) {
 #pragma unroll
     for (int r = 0; r < NMAX; ++r)
       if (r < a.nshards) {
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
       }
   }
   float inv_g = 0.0f;
-  if constexpr (FOUT == kFP8) {
+  if constexpr (is_fp8(FOUT)) {
     if (rq) {
       float gs = 0.0f;
       for (int r = 0; r < a.nshards; ++r) gs = gs + *a.in.g[r];
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   const int nb_out = n / BOUT;
   const rsrc_t r_sum = make_rsrc32(a.sum, a.sum ? 4 * n : 0);
   const rsrc_t r_qc = make_rsrc32(a.rq_codes, rq ? n : 0);
-  const rsrc_t r_qs = make_rsrc32(a.rq_scale, rq ? (FOUT == kFP8 ? nb_out : 4 * nb_out) : 0);
+  const rsrc_t r_qs = make_rsrc32(a.rq_scale, rq ? (is_fp8(FOUT) ? nb_out : 4 * nb_out) : 0);
   const rsrc_t r_qz = make_rsrc32(a.rq_zero, rq && FOUT == kINT8A ? nb_out : 0);
 
   // the finished sum of a tile: store it and/or re-quantize it
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
       LaneCodes q = quant_lane<FOUT, BOUT>(acc, inv_g, nullptr);
       const int blk = e0 / BOUT;
       bstore128(q.q, r_qc, e0, 0);
-      if constexpr (FOUT == kFP8) {
+      if constexpr (is_fp8(FOUT)) {
         bstore8((uint32_t)q.k, r_qs, blk, 0);
       } else {
         bstore32(__float_as_uint(q.s), r_qs, blk * 4, 0);
@@ -646,13 +648,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_ring_hop(HopArgs a) {
   }
 }
 
-// Test hook: the device E4M3 encoder alone (four values per lane).
-__global__ __launch_bounds__(kBlockThreads) void k_e4m3_encode(const float* x, uint8_t* out, int64_t n) {
+// Test hook: the device FP8 encoder alone (four values per lane).
+template <bool E5>
+__global__ __launch_bounds__(kBlockThreads) void k_fp8_encode(const float* x, uint8_t* out, int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) * 4;
   if (i >= n) return;
   float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = 0; j < 4 && i + j < n; ++j) v[j] = x[i + j];
-  const uint32_t w = e4m3_pack4(v[0], v[1], v[2], v[3]);
+  const uint32_t w = Fp8Code<E5>::pack4(v[0], v[1], v[2], v[3]);
   for (int j = 0; j < 4 && i + j < n; ++j) out[i + j] = (uint8_t)(w >> (8 * j));
 }
 
@@ -684,7 +687,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   QuantK k{a.x, a.n, a.codes, a.scale, a.zero, a.g_hdr, a.g, a.g_from_ws ? 1 : 0,
            static_cast<Workspace*>(a.ws), a.dbg};
-  if (a.fmt == kFP8 && a.auto_prepass) {
+  if (is_fp8(a.fmt) && a.auto_prepass) {
     dim3 grid = quant_grid(a), block(kBlockThreads);
     if (a.f32_in) hipLaunchKernelGGL((k_amax<true>), grid, block, 0, s, a.x, a.n, k.ws);
     else hipLaunchKernelGGL((k_amax<false>), grid, block, 0, s, a.x, a.n, k.ws);
@@ -696,6 +699,15 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
         case 32: launch_q<kFP8, 32>(a, k, s); break;
         case 64: launch_q<kFP8, 64>(a, k, s); break;
         case 128: launch_q<kFP8, 128>(a, k, s); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    case kFP8E5:
+      switch (a.block) {
+        case 16: launch_q<kFP8E5, 16>(a, k, s); break;
+        case 32: launch_q<kFP8E5, 32>(a, k, s); break;
+        case 64: launch_q<kFP8E5, 64>(a, k, s); break;
+        case 128: launch_q<kFP8E5, 128>(a, k, s); break;
         default: return hipErrorInvalidValue;
       }
       break;
@@ -724,6 +736,15 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
         case 32: launch_dq<kFP8, 32>(a, s); break;
         case 64: launch_dq<kFP8, 64>(a, s); break;
         case 128: launch_dq<kFP8, 128>(a, s); break;
+        default: return hipErrorInvalidValue;
+      }
+      break;
+    case kFP8E5:
+      switch (a.block) {
+        case 16: launch_dq<kFP8E5, 16>(a, s); break;
+        case 32: launch_dq<kFP8E5, 32>(a, s); break;
+        case 64: launch_dq<kFP8E5, 64>(a, s); break;
+        case 128: launch_dq<kFP8E5, 128>(a, s); break;
         default: return hipErrorInvalidValue;
       }
       break;
@@ -769,6 +790,14 @@ static hipError_t launch_reduce_piece(const ReduceArgs& a, hipStream_t s) {
       case 128: launch_rn<kFP8, 128, kFP8, 128>(a, s); break;
       default: return hipErrorInvalidValue;
     }
+  } else if (a.fin == kFP8E5) {
+    switch (a.bin) {
+      case 16: launch_rn<kFP8E5, 16, kFP8E5, 16>(a, s); break;
+      case 32: launch_rn<kFP8E5, 32, kFP8E5, 32>(a, s); break;
+      case 64: launch_rn<kFP8E5, 64, kFP8E5, 64>(a, s); break;
+      case 128: launch_rn<kFP8E5, 128, kFP8E5, 128>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
   } else if (a.fin == kINT8S) {
     launch_rn<kINT8S, 64, kINT8S, 64>(a, s);
   } else if (a.fin == kINT4A) {
@@ -782,7 +811,7 @@ static hipError_t launch_reduce_piece(const ReduceArgs& a, hipStream_t s) {
 }
 
 static int64_t code_bytes(int fmt, int64_t elems) { return fmt == kINT4A ? elems / 2 : elems; }
-static int64_t scale_bytes(int fmt, int64_t blocks) { return fmt == kFP8 ? blocks : 4 * blocks; }
+static int64_t scale_bytes(int fmt, int64_t blocks) { return is_fp8(fmt) ? blocks : 4 * blocks; }
 
 // Split the tensor into pieces of at most kReducePiece elements; each piece is
 // one launch over offset pointers (blocks never straddle pieces).
@@ -835,10 +864,11 @@ hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s) {
+hipError_t launch_fp8_encode(bool e5, const float* x, uint8_t* out, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int64_t groups = (n + 4LL * kBlockThreads - 1) / (4LL * kBlockThreads);
-  hipLaunchKernelGGL(k_e4m3_encode, dim3((unsigned)groups), dim3(kBlockThreads), 0, s, x, out, n);
+  if (e5) hipLaunchKernelGGL(k_fp8_encode<true>, dim3((unsigned)groups), dim3(kBlockThreads), 0, s, x, out, n);
+  else hipLaunchKernelGGL(k_fp8_encode<false>, dim3((unsigned)groups), dim3(kBlockThreads), 0, s, x, out, n);
   return hipGetLastError();
 }
 

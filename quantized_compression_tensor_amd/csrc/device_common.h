@@ -22,7 +22,6 @@ constexpr int kBlockThreads = 256;
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.
 TACO_DEV int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) / kWave; }
 
-constexpr float kE4M3Max = 448.0f;
 // Blocks whose abs-max (symmetric) or range (asymmetric) is below this are
 // stored as zero codes with a zero scale, so 127/A and qmax/r stay finite.
 constexpr float kTiny = 0x1p-100f;
@@ -112,31 +111,70 @@ TACO_DEV void e4m3_unpack4(uint32_t w, float* o) {
   o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
 }
 
-// Saturate to +-448 keeping NaN (only reached when a block exponent is
-// clamped, i.e. the block maximum cannot be brought down to 448).
-TACO_DEV float sat448(float v) {
-  return (fabsf(v) > kE4M3Max) ? copysignf(kE4M3Max, v) : v;
+// ------------------------------------------------------------------- E5M2 --
+// Hardware OCP E5M2 ("bf8") conversions of gfx950 (nearest-even), same
+// packing as the E4M3 pair.
+TACO_DEV uint32_t e5m2_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+TACO_DEV void e5m2_unpack4(uint32_t w, float* o) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+
+// The two FP8 code formats of the dual-scale codec. kMax is the largest finite
+// value, 1.75 * 2^kTop; the block exponent puts each block maximum in
+// (kMax / 2, kMax].
+template <bool E5>
+struct Fp8Code {
+  static constexpr float kMax = 448.0f;          // E4M3: 1.75 * 2^8
+  static constexpr int kTop = 8;
+  static TACO_DEV uint32_t pack4(float a, float b, float c, float d) { return e4m3_pack4(a, b, c, d); }
+  static TACO_DEV void unpack4(uint32_t w, float* o) { e4m3_unpack4(w, o); }
+};
+template <>
+struct Fp8Code<true> {
+  static constexpr float kMax = 57344.0f;        // E5M2: 1.75 * 2^15
+  static constexpr int kTop = 15;
+  static TACO_DEV uint32_t pack4(float a, float b, float c, float d) { return e5m2_pack4(a, b, c, d); }
+  static TACO_DEV void unpack4(uint32_t w, float* o) { e5m2_unpack4(w, o); }
+};
+
+// Saturate to +-kMax keeping NaN (only reached when a block exponent is
+// clamped, i.e. the block maximum cannot be brought down to kMax).
+template <bool E5>
+TACO_DEV float sat_fp8(float v) {
+  constexpr float M = Fp8Code<E5>::kMax;
+  return (fabsf(v) > M) ? copysignf(M, v) : v;
 }
 
 // ------------------------------------------------------- scales, exponents --
 // 2^k as a float for k in [-126, 127].
 TACO_DEV float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
 
-// Block exponent: largest k in [-64, 63] with m * 2^k <= 448 (m >= 0), 0 for
-// m == 0. From the float bits: with m = 1.f * 2^(e-127), the frexp fraction
-// is <= 0.875 exactly when the stored mantissa is <= 0x600000, giving
-// k = 135 - e or 134 - e; subnormal m clamps to 63 and infinity to -64.
+// Block exponent: largest k in [-64, 63] with m * 2^k <= kMax = 1.75 * 2^T
+// (m >= 0), 0 for m == 0. From the float bits: with m = 1.f * 2^(e-127),
+// 1.f <= 1.75 exactly when the stored mantissa is <= 0x600000, giving
+// k = T + 127 - e or T + 126 - e (E4M3: 135 / 134; E5M2: 142 / 141); subnormal
+// m clamps to 63 and infinity to -64.
+template <bool E5>
 TACO_DEV int block_exponent(float m) {
+  constexpr int T = Fp8Code<E5>::kTop + 127;
   uint32_t b = __float_as_uint(m);
-  int k = ((b & 0x7FFFFFu) <= 0x600000u ? 135 : 134) - (int)(b >> 23);
+  int k = ((b & 0x7FFFFFu) <= 0x600000u ? T : T - 1) - (int)(b >> 23);
   k = k < -64 ? -64 : (k > 63 ? 63 : k);
   return b == 0 ? 0 : k;
 }
 
 // Data-driven tensor scale from an abs-max A (FP8 dual-scale).
+template <bool E5>
 TACO_DEV float tensor_scale_from_amax(float A) {
   if (A == 0.0f) return 1.0f;
-  float g = A / kE4M3Max;
+  float g = A / Fp8Code<E5>::kMax;
   return fminf(fmaxf(g, kGMin), kGMax);
 }
 

@@ -177,22 +177,23 @@ TACO_DEV float had_transform_tile(uint4 raw, const LaneSigns<LOGB>& ls, float* v
 
 // Scale, encode and store tile i of chunk c from its transformed values v and
 // block abs-max M.
-template <int LOGB, int T, bool DEBUG>
+template <int LOGB, int T, bool E5, bool DEBUG>
 TACO_DEV void had_encode_tile(float* v, float M, int i, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
                               float inv_g, rsrc_t rc, rsrc_t rk, float* dbg) {
   using Gm = HadGeom<LOGB>;
+  using F = Fp8Code<E5>;
   const float m = M * inv_g;
-  const int k = block_exponent(m);
+  const int k = block_exponent<E5>(m);
   const float cs = inv_g * pow2f(k) * ls.parity;
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], cs, 0.0f);
-  if (__builtin_expect(m * pow2f(k) > kE4M3Max, 0)) {
+  if (__builtin_expect(m * pow2f(k) > F::kMax, 0)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = sat448(v[e]);
+    for (int e = 0; e < 8; ++e) v[e] = sat_fp8<E5>(v[e]);
   }
   uint2 q;
-  q.x = e4m3_pack4(v[0], v[1], v[2], v[3]);
-  q.y = e4m3_pack4(v[4], v[5], v[6], v[7]);
+  q.x = F::pack4(v[0], v[1], v[2], v[3]);
+  q.y = F::pack4(v[4], v[5], v[6], v[7]);
   bstore64(q, rc, ls.elem_off, i * kTileElems);
   // every lane of the block writes the same exponent byte
   bstore8((uint32_t)k, rk, row, i * Gm::BPT);
@@ -218,7 +219,7 @@ struct ChunkOut {
 };
 
 // Transform, scale, encode and store one chunk.
-template <int LOGB, int T, bool DEBUG>
+template <int LOGB, int T, bool E5, bool DEBUG>
 TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, const LaneSigns<LOGB>& ls, int row,
                                  float inv_g, uint8_t* codes, int8_t* kexp, float* dbg, float& run_max) {
   const ChunkOut<LOGB, T> o(codes, kexp, c, elems);
@@ -227,11 +228,11 @@ TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, con
     float v[8];
     const float M = had_transform_tile<LOGB>(raw[i], ls, v);
     run_max = fmaxf(run_max, M);
-    had_encode_tile<LOGB, T, DEBUG>(v, M, i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
+    had_encode_tile<LOGB, T, E5, DEBUG>(v, M, i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
   }
 }
 
-template <int LOGB, int T, bool GFROM_WS, bool DEBUG, bool PERSIST>
+template <int LOGB, int T, bool E5, bool GFROM_WS, bool DEBUG, bool PERSIST>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
     float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     if (wave0) {
       const uint32_t ee = ws_bank_of(tk);
       float gg = g_arg;
-      if constexpr (GFROM_WS) gg = tensor_scale_from_amax(PERSIST ? ws_prev_from(hist, ee) : ws_prev_amax(ws, ee));
+      if constexpr (GFROM_WS) gg = tensor_scale_from_amax<E5>(PERSIST ? ws_prev_from(hist, ee) : ws_prev_amax(ws, ee));
       if (blockIdx.x == 0) ws_clear_next(ws, ee);
       if (lane == 0) { lds_e = ee; lds_g = gg; }
     }
@@ -303,18 +304,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     if (PERSIST && ws != nullptr) {
       const ChunkOut<LOGB, T> o(codes, kexp, c, elems);
 #pragma unroll
-      for (int i = 0; i < T; ++i) had_encode_tile<LOGB, T, DEBUG>(v0[i], M0[i], i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
+      for (int i = 0; i < T; ++i) had_encode_tile<LOGB, T, E5, DEBUG>(v0[i], M0[i], i, c, elems, ls, row, inv_g, o.rc, o.rk, dbg);
     } else {
-      had_compress_chunk<LOGB, T, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+      had_compress_chunk<LOGB, T, E5, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
     }
     CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
     c += stride;
     while (c < nchunks) {
-      had_compress_chunk<LOGB, T, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+      had_compress_chunk<LOGB, T, E5, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
       CH::load(x, c + 2 * stride, elems, ls.elem_off, rb);
       c += stride;
       if (c >= nchunks) break;
-      had_compress_chunk<LOGB, T, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
+      had_compress_chunk<LOGB, T, E5, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
       CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
       c += stride;
     }
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
 // Consumer side: dequantize (dec(q) * g * 2^-k, the combined scale is exact),
 // inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
 // factor, then float32 or bf16 output.
-template <int LOGB, bool BF16OUT, int T>
+template <int LOGB, bool E5, bool BF16OUT, int T>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
     int64_t nblocks, void* __restrict__ out) {
@@ -391,8 +392,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const int64_t blk = (tile0 + i) * Gm::BPT + row;
     const float d = g * pow2f(-kk[i]);
     float v[8];
-    e4m3_unpack4(raw[i].x, v);
-    e4m3_unpack4(raw[i].y, v + 4);
+    Fp8Code<E5>::unpack4(raw[i].x, v);
+    Fp8Code<E5>::unpack4(raw[i].y, v + 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * d;
     fwht_in_lane(v);
@@ -425,17 +426,17 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
   return (tiles + 4 * T - 1) / (4 * T);
 }
 
-template <int LOGB, int T, bool DEBUG, bool PERSIST>
+template <int LOGB, int T, bool E5, bool DEBUG, bool PERSIST>
 static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s) {
   dim3 block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
   if (a.g_from_ws)
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, true, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes, a.kexp,
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes, a.kexp,
                        a.g_hdr, a.nblocks, a.g, ws, a.dbg);
   else
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, false, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes, a.kexp,
-                       a.g_hdr, a.nblocks, a.g, ws, a.dbg);
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes,
+                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg);
 }
 
 // Grid. Tensors of fewer than 2^16 large chunks take the small chunks on a
@@ -443,8 +444,8 @@ static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s) {
 // a few chunks; the workspace history is read up front and the first chunk is
 // transformed while the ticket returns). Larger tensors give every wave one
 // large chunk (the uncapped grid described above).
-template <int LOGB>
-static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
+template <int LOGB, bool E5>
+static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
   const int64_t elems = a.nblocks << LOGB;
   if (elems == 0) return hipSuccess;
   const int64_t chunks = (elems + kChunkTiles * kTileElems - 1) / (kChunkTiles * kTileElems);
@@ -458,13 +459,18 @@ static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
   if (small) {
     const int64_t need = had_groups(LOGB, a.nblocks, kSmallChunkTiles);
     const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
-    launch_compress_t<LOGB, kSmallChunkTiles, false, true>(a, dim3((unsigned)(need < cap ? need : cap)), s);
+    launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, dim3((unsigned)(need < cap ? need : cap)), s);
   } else {
     const dim3 grid((unsigned)had_groups(LOGB, a.nblocks, kChunkTiles));
-    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, true, false>(a, grid, s);   // test hook: the large chunks
-    else launch_compress_t<LOGB, kChunkTiles, false, false>(a, grid, s);
+    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, grid, s);   // test hook: the large chunks
+    else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, grid, s);
   }
   return hipGetLastError();
+}
+
+template <int LOGB>
+static hipError_t launch_compress_logb(const FP8HadArgs& a, hipStream_t s) {
+  return a.e5 ? launch_compress_fmt<LOGB, true>(a, s) : launch_compress_fmt<LOGB, false>(a, s);
 }
 
 hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s) {
@@ -477,18 +483,25 @@ hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int LOGB>
-static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
+template <int LOGB, bool E5>
+static void launch_decode_fmt(const FP8HadDecodeArgs& a, dim3 grid, hipStream_t s) {
   constexpr int T = 2;
-  const int64_t groups = had_groups(LOGB, a.nblocks, T);
-  if (groups == 0) return hipSuccess;
-  dim3 grid((unsigned)groups), block(kBlockThreads);
+  dim3 block(kBlockThreads);
   if (a.bf16_out)
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, true, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, true, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
                        a.out);
   else
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, false, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
-                       a.out);
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, false, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr,
+                       a.nblocks, a.out);
+}
+
+template <int LOGB>
+static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
+  const int64_t groups = had_groups(LOGB, a.nblocks, 2);
+  if (groups == 0) return hipSuccess;
+  const dim3 grid((unsigned)groups);
+  if (a.e5) launch_decode_fmt<LOGB, true>(a, grid, s);
+  else launch_decode_fmt<LOGB, false>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_fp8_format(int32_t f) { return f == TACO_FMT_FP8_DUAL || f == TACO_FMT_FP8E5_DUAL; }
+
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
@@ -27,6 +29,7 @@ int check_codec(const taco_codec& c) {
   if (c.reserved != 0) return TACO_ERR_INVALID_ARG;
   switch (c.format) {
     case TACO_FMT_FP8_DUAL:
+    case TACO_FMT_FP8E5_DUAL:
       if (c.hadamard != 0 && c.hadamard != 1) return TACO_ERR_FORMAT;
       if (c.block != 16 && c.block != 32 && c.block != 64 && c.block != 128) return TACO_ERR_SHAPE;
       return TACO_OK;
@@ -56,11 +59,11 @@ void layout_of(const taco_codec& c, int64_t n, taco_layout_t* L) {
   L->codes_off = 0;
   L->codes_bytes = c.format == TACO_FMT_INT4_ASYM ? n / 2 : n;
   L->scale_off = align256(L->codes_bytes);
-  L->scale_bytes = c.format == TACO_FMT_FP8_DUAL ? nb : 4 * nb;
+  L->scale_bytes = is_fp8_format(c.format) ? nb : 4 * nb;
   L->aux_off = align256(L->scale_off + L->scale_bytes);
   L->aux_bytes = (c.format == TACO_FMT_INT4_ASYM || c.format == TACO_FMT_INT8_ASYM) ? nb : 0;
   L->tensor_off = align256(L->aux_off + L->aux_bytes);
-  L->tensor_bytes = c.format == TACO_FMT_FP8_DUAL ? 16 : 0;
+  L->tensor_bytes = is_fp8_format(c.format) ? 16 : 0;
   L->total_bytes = align256(L->tensor_off + L->tensor_bytes);
 }
 
@@ -69,7 +72,7 @@ int log2_block(int b) { return b == 16 ? 4 : b == 32 ? 5 : b == 64 ? 6 : 7; }
 // FP8 tensor-scale mode: 0 = given g, 1 = auto (pre-pass), 2 = delayed.
 int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, int* mode) {
   *mode = 0;
-  if (c.format != TACO_FMT_FP8_DUAL) return TACO_OK;
+  if (!is_fp8_format(c.format)) return TACO_OK;
   if (isnan(ts) || isinf(ts)) return TACO_ERR_INVALID_ARG;
   if (ts > 0.0f) {
     if (ts < kGMin || ts > kGMax) return TACO_ERR_INVALID_ARG;
@@ -117,10 +120,10 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   if (dbg && (overlaps(dbg, 4 * n, x, in_bytes) || overlaps(dbg, 4 * n, out, L.total_bytes)))
     return TACO_ERR_INVALID_ARG;
   Regions R = regions_of(out, L);
-  if (c.format == TACO_FMT_FP8_DUAL && c.hadamard == 1 && !f32_in) {
+  if (is_fp8_format(c.format) && c.hadamard == 1 && !f32_in) {
     FP8HadArgs a;
     a.x = x; a.codes = R.codes; a.kexp = static_cast<int8_t*>(R.scale); a.g_hdr = R.tensor;
-    a.nblocks = n / c.block; a.logb = log2_block(c.block);
+    a.nblocks = n / c.block; a.logb = log2_block(c.block); a.e5 = c.format == TACO_FMT_FP8E5_DUAL;
     a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
     a.ws = ws; a.dbg = dbg;
     clear_stale_error();
@@ -130,7 +133,7 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   a.fmt = c.format; a.block = c.block; a.f32_in = f32_in; a.x = x; a.n = n;
   a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
   a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
-  a.ws = c.format == TACO_FMT_FP8_DUAL ? ws : nullptr; a.dbg = dbg;
+  a.ws = is_fp8_format(c.format) ? ws : nullptr; a.dbg = dbg;
   clear_stale_error();
   return hip_status(launch_quantize(a, stream));
 }
@@ -156,8 +159,8 @@ int device_cu_count() {
 namespace {
 
 bool pair_allowed(const taco_codec& i, const taco_codec& o) {
-  if (i.format == TACO_FMT_FP8_DUAL)
-    return o.format == TACO_FMT_FP8_DUAL && o.block == i.block && o.hadamard == i.hadamard;
+  if (is_fp8_format(i.format))
+    return o.format == i.format && o.block == i.block && o.hadamard == i.hadamard;
   if (i.format == TACO_FMT_INT8_SYM) return o.format == TACO_FMT_INT8_SYM;
   if (i.format == TACO_FMT_INT4_ASYM) return o.format == TACO_FMT_INT8_ASYM;
   if (i.format == TACO_FMT_INT8_ASYM) return o.format == TACO_FMT_INT8_ASYM;
@@ -185,7 +188,7 @@ int64_t taco_compressed_bytes(taco_codec c, int64_t rows, int64_t cols) {
 size_t taco_workspace_bytes(taco_codec c, int64_t rows, int64_t cols) {
   (void)rows;
   (void)cols;
-  return c.format == TACO_FMT_FP8_DUAL ? TACO_WORKSPACE_BYTES : 0;
+  return is_fp8_format(c.format) ? TACO_WORKSPACE_BYTES : 0;
 }
 
 int taco_compress(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
@@ -253,7 +256,7 @@ int taco_ring_hop(taco_codec c_in, const void* incoming, const void* local_bf16,
                   float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream) {
   int st = check_shape(c_in, rows, cols);
   if (st != TACO_OK) return st;
-  if (c_in.format == TACO_FMT_FP8_DUAL) return TACO_ERR_FORMAT;
+  if (is_fp8_format(c_in.format)) return TACO_ERR_FORMAT;
   if (requant_out != nullptr) {
     st = check_shape(c_out, rows, cols);
     if (st != TACO_OK) return st;
@@ -309,10 +312,11 @@ int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, vo
   layout_of(c, n, &L);
   if (overlaps(in, L.total_bytes, out, n * (out_dtype ? 2 : 4))) return TACO_ERR_INVALID_ARG;
   Regions R = regions_of(const_cast<void*>(in), L);
-  if (c.format == TACO_FMT_FP8_DUAL && c.hadamard == 1) {
+  if (is_fp8_format(c.format) && c.hadamard == 1) {
     FP8HadDecodeArgs a;
     a.codes = R.codes; a.kexp = static_cast<const int8_t*>(R.scale); a.g_hdr = R.tensor;
-    a.nblocks = n / c.block; a.logb = log2_block(c.block); a.bf16_out = out_dtype == 1; a.out = out;
+    a.nblocks = n / c.block; a.logb = log2_block(c.block); a.e5 = c.format == TACO_FMT_FP8E5_DUAL;
+    a.bf16_out = out_dtype == 1; a.out = out;
     clear_stale_error();
     return hip_status(launch_fp8_had_decode(a, stream));
   }
@@ -323,14 +327,24 @@ int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, vo
     return hip_status(launch_dequantize(a, stream));
 }
 
-int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+namespace {
+int fp8_encode(bool e5, const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
   if (n < 0 || n > kMaxElems) return TACO_ERR_INVALID_ARG;
   if (n == 0) return TACO_OK;
   if (x == nullptr || codes == nullptr) return TACO_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes)) return TACO_ERR_ALIGN;
   if (overlaps(x, 4 * n, codes, n)) return TACO_ERR_INVALID_ARG;
   clear_stale_error();
-    return hip_status(launch_e4m3_encode(x, codes, n, stream));
+  return hip_status(launch_fp8_encode(e5, x, codes, n, stream));
+}
+}  // namespace
+
+int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+  return fp8_encode(false, x, codes, n, stream);
+}
+
+int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+  return fp8_encode(true, x, codes, n, stream);
 }
 
 const char* taco_status_string(int status) {

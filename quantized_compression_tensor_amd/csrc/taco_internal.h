@@ -8,7 +8,10 @@
 
 namespace taco {
 
-enum Format : int { kFP8 = 1, kINT8S = 2, kINT4A = 3, kINT8A = 4 };
+enum Format : int { kFP8 = 1, kINT8S = 2, kINT4A = 3, kINT8A = 4, kFP8E5 = 5 };
+
+// The dual-scale FP8 formats (E4M3 and E5M2 codes).
+constexpr bool is_fp8(int f) { return f == kFP8 || f == kFP8E5; }
 
 // Range of the per-tensor scale g (FP8 dual-scale): both g * 2^-k and
 // (1/g) * 2^k stay normal float32 numbers for every block exponent k in
@@ -24,6 +27,7 @@ struct FP8HadArgs {
   float* g_hdr;
   int64_t nblocks;
   int logb;
+  bool e5;              // E5M2 codes (else E4M3)
   float g;              // used when !g_from_ws
   bool g_from_ws;       // tensor scale from the workspace's recorded abs-max
   bool auto_prepass;    // run the abs-max pass first (data-driven g of this tensor)
@@ -37,6 +41,7 @@ struct FP8HadDecodeArgs {
   const float* g_hdr;
   int64_t nblocks;
   int logb;
+  bool e5;              // E5M2 codes (else E4M3)
   bool bf16_out;
   void* out;
 };
@@ -142,6 +147,6 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s);
-hipError_t launch_e4m3_encode(const float* x, uint8_t* out, int64_t n, hipStream_t s);
+hipError_t launch_fp8_encode(bool e5, const float* x, uint8_t* out, int64_t n, hipStream_t s);
 
 }  // namespace taco

@@ -59,9 +59,13 @@ def assert_same(gpu, ref: oracle.Compressed, where=""):
     bad = gc != rc
     if ref.codec.format == cd.FP8_DUAL:
         bad &= ~(((gc & 0x7F) == 0x7F) & ((rc & 0x7F) == 0x7F))
+    if ref.codec.format == cd.FP8E5_DUAL:
+        def e5_nan(c):
+            return ((c & 0x7C) == 0x7C) & ((c & 0x03) != 0)
+        bad &= ~(e5_nan(gc) & e5_nan(rc))
     nbad = int(bad.sum())
     assert nbad == 0, f"{where}: {nbad} of {gc.size} codes differ; first at {np.flatnonzero(bad)[:8]}"
-    if ref.codec.format == cd.FP8_DUAL:
+    if ref.codec.format in cd.FP8_FORMATS:
         assert (gpu["scale"].astype(np.int8) == ref.scale.astype(np.int8)).all(), f"{where}: block exponents differ"
         assert gpu["g"].view(np.uint32) == np.float32(ref.tensor_scale).view(np.uint32), \
             f"{where}: g {gpu['g']!r} vs {ref.tensor_scale!r}"

@@ -41,6 +41,7 @@ FP8 = T.codec(T.TACO_FMT_FP8_DUAL, 128, 1)
 I8S = T.codec(T.TACO_FMT_INT8_SYM, 64)
 I4A = T.codec(T.TACO_FMT_INT4_ASYM, 128)
 I8A = T.codec(T.TACO_FMT_INT8_ASYM, 128)
+E5 = T.codec(T.TACO_FMT_FP8E5_DUAL, 128, 1)
 
 
 def test_layouts_by_hand():
@@ -58,13 +59,17 @@ def test_layouts_by_hand():
     assert L["total_bytes"] == 512
     assert T.taco_compressed_bytes(I8A, 0, 128) == 0
     assert T.taco_workspace_bytes(FP8, 1, 128) == T.TACO_WORKSPACE_BYTES
+    assert T.taco_workspace_bytes(E5, 1, 128) == T.TACO_WORKSPACE_BYTES
     assert T.taco_workspace_bytes(I8S, 1, 64) == 0
+    assert T.taco_layout(E5, 4096, 4096).as_dict() == T.taco_layout(FP8, 4096, 4096).as_dict()
 
 
 @pytest.mark.parametrize("c,cols,err", [
     (T.codec(T.TACO_FMT_FP8_DUAL, 128, 1), 100, T.TACO_ERR_SHAPE),
     (T.codec(T.TACO_FMT_FP8_DUAL, 96, 1), 96, T.TACO_ERR_SHAPE),
     (T.codec(T.TACO_FMT_FP8_DUAL, 128, 2), 128, T.TACO_ERR_FORMAT),
+    (T.codec(T.TACO_FMT_FP8E5_DUAL, 96, 0), 96, T.TACO_ERR_SHAPE),
+    (T.codec(T.TACO_FMT_FP8E5_DUAL, 128, 3), 128, T.TACO_ERR_FORMAT),
     (T.codec(T.TACO_FMT_INT8_SYM, 128), 128, T.TACO_ERR_SHAPE),
     (T.codec(T.TACO_FMT_INT8_SYM, 64, 1), 64, T.TACO_ERR_FORMAT),
     (T.codec(T.TACO_FMT_INT4_ASYM, 64), 128, T.TACO_ERR_SHAPE),
@@ -124,6 +129,8 @@ def test_reduce_validation():
     assert _st(red, I4A, shards, 4, 128, None, I4A, B_) == T.TACO_ERR_FORMAT
     assert _st(red, FP8, shards, 4, 128, None, T.codec(T.TACO_FMT_FP8_DUAL, 64, 1), B_) == T.TACO_ERR_FORMAT
     assert _st(red, FP8, shards, 4, 128, None, T.codec(T.TACO_FMT_FP8_DUAL, 128, 0), B_) == T.TACO_ERR_FORMAT
+    assert _st(red, FP8, shards, 4, 128, None, E5, B_) == T.TACO_ERR_FORMAT            # E4M3 -> E5M2 is no pair
+    assert _st(red, E5, shards, 4, 128, None, FP8, B_) == T.TACO_ERR_FORMAT
     assert _st(red, I8S, shards, 4, 64, A) == T.TACO_ERR_INVALID_ARG               # sum overlaps a shard
     assert _st(red, I8S, shards, 0, 64, B_) == 0
 
@@ -134,6 +141,7 @@ def test_ring_hop_validation():
     assert _st(hop, I8S, A, None, 4, 64, B_) == T.TACO_ERR_INVALID_ARG             # no local shard
     assert _st(hop, I8S, A, L, 4, 64, None, None, None) == T.TACO_ERR_INVALID_ARG  # no output
     assert _st(hop, FP8, A, L, 4, 128, B_) == T.TACO_ERR_FORMAT                    # FP8 is not a ring codec
+    assert _st(hop, E5, A, L, 4, 128, B_) == T.TACO_ERR_FORMAT
     assert _st(hop, I8S, A, L, 4, 64, None, FP8, B_) == T.TACO_ERR_SHAPE           # 64 cols: no 128 block
     assert _st(hop, I8S, A, L, 4, 128, None, FP8, B_) == T.TACO_ERR_FORMAT
     assert _st(hop, I4A, A, L, 4, 128, None, I4A, B_) == T.TACO_ERR_FORMAT         # the gather stage is INT8
@@ -155,6 +163,9 @@ def test_other_entry_points_validation():
     assert _st(T.taco_e4m3_encode, A, B_, -1) == T.TACO_ERR_INVALID_ARG
     assert _st(T.taco_e4m3_encode, A, A + 16, 64) == T.TACO_ERR_INVALID_ARG       # overlap
     assert _st(T.taco_e4m3_encode, A, B_, 0) == 0
+    assert _st(T.taco_e5m2_encode, A, None, 16) == T.TACO_ERR_INVALID_ARG
+    assert _st(T.taco_e5m2_encode, A, A + 16, 64) == T.TACO_ERR_INVALID_ARG       # overlap
+    assert _st(T.taco_e5m2_encode, A, B_, 0) == 0
 
 
 def test_one_hip_runtime_in_the_process():

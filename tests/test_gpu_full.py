@@ -12,6 +12,8 @@ import oracle
 from oracle import codecs as cd
 from oracle.formats import bf16_bits_to_f32
 import quantized_compression_tensor_amd as T
+import dataclasses
+
 import workloads as W
 from tests.gpu_util import DEV, ccodec, new_workspace, same_f32_bits
 
@@ -33,7 +35,7 @@ def rows_of(buf, oc, rows, cols, idx):
 
 def check_rows(got, ref, where):
     assert (got["codes"] == ref.codes).all(), f"{where}: {(got['codes'] != ref.codes).sum()} codes differ"
-    if ref.codec.format == cd.FP8_DUAL:
+    if ref.codec.format in cd.FP8_FORMATS:
         assert (got["scale"].astype(np.int8) == ref.scale.astype(np.int8)).all(), f"{where}: exponents differ"
         assert got["g"] == ref.tensor_scale, f"{where}: g {got['g']} vs {ref.tensor_scale}"
     else:
@@ -42,12 +44,19 @@ def check_rows(got, ref, where):
         assert (got["zero"] == ref.zero).all(), f"{where}: zero points differ"
 
 
-@pytest.mark.parametrize("name", ["gpt-tp", "equarx", "flashcomm", "qwen-tp"])
+def _workload(name):
+    if name == "gpt-tp-e5m2":   # the gpt-tp tensors through the E5M2 variant of the FP8 codec
+        return dataclasses.replace(W.WORKLOADS["gpt-tp"], name=name, in_format=cd.FP8E5_DUAL,
+                                   out_format=cd.FP8E5_DUAL)
+    return W.WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", ["gpt-tp", "equarx", "flashcomm", "qwen-tp", "gpt-tp-e5m2"])
 def test_full_size_workload(name):
-    w = W.WORKLOADS[name]
+    w = _workload(name)
     cin = cd.Codec(w.in_format, w.in_block, w.hadamard)
     cout = cd.Codec(w.out_format, w.out_block, w.hadamard)
-    fp8 = cin.format == cd.FP8_DUAL
+    fp8 = cin.format in cd.FP8_FORMATS
     chunks = W.sample_chunks(w, 2, seed=11)
     idx = W.chunk_rows(chunks, w.rows)
     print(f"[{name}] {w.shards} x {w.rows}x{w.cols}, sampled rows {len(idx)}", flush=True)
@@ -94,7 +103,7 @@ def test_full_size_workload(name):
     worst = float((num / den).max())
     total = float(num.sum() / den.sum())
     # per-row sanity bounds: FP8 ~7e-4 per quantization, INT8 ~5e-5, INT4 ~1e-2
-    limit = {cd.FP8_DUAL: 1e-2, cd.INT8_SYM: 1e-3, cd.INT8_ASYM: 1e-1}[cout.format]
+    limit = {cd.FP8_DUAL: 1e-2, cd.FP8E5_DUAL: 4e-2, cd.INT8_SYM: 1e-3, cd.INT8_ASYM: 1e-1}[cout.format]
     print(f"[{name}] requantized sum rel-MSE {total:.3e} (worst row {worst:.3e})", flush=True)
     assert worst < limit and np.isfinite(worst)
     if fp8:

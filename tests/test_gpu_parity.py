@@ -18,7 +18,8 @@ from tests.gpu_util import (DEV, assert_same, ccodec, gpu_compress, new_workspac
 
 pytestmark = pytest.mark.gpu
 
-FP8_CODECS = [cd.Codec.fp8(b, h) for b in (16, 32, 64, 128) for h in (True, False)]
+FP8_CODECS = ([cd.Codec.fp8(b, h) for b in (16, 32, 64, 128) for h in (True, False)]
+              + [cd.Codec.fp8e5(b, h) for b in (16, 128) for h in (True, False)])
 INT_CODECS = [cd.Codec.int8_sym(), cd.Codec.int4_asym(), cd.Codec.int8_asym()]
 ALL = FP8_CODECS + INT_CODECS
 SHAPES = [(1, 128), (3, 384), (37, 1024), (5, 2560), (64, 4096)]
@@ -64,6 +65,39 @@ def test_e4m3_encoder_nan_is_a_nan_code():
     torch.cuda.synchronize()
     got = out[:4].cpu().numpy()
     assert (got[[0, 1, 3]] & 0x7F == 0x7F).all() and got[2] == 0x38
+
+
+def test_e5m2_encoder_matches_oracle():
+    x = fm.bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    x = x[np.isfinite(x)]
+    parts = []
+    for s in (0, -8, 8, -20, 12):
+        with np.errstate(over="ignore"):
+            y = (x * np.float32(2.0 ** s)).astype(np.float32)
+        parts.append(y[np.abs(y) <= 57344])
+    vals = fm.decode_e5m2(np.arange(0, 0x7C, dtype=np.uint8)).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    parts += [mids, np.nextafter(mids, np.float32(1e9)), np.nextafter(mids, np.float32(-1e9)), -mids,
+              np.array([0.0, -0.0, 57344.0, -57344.0, 1e-45, -1e-45], np.float32)]
+    v = np.concatenate(parts).astype(np.float32)
+    n = v.size
+    out = torch.empty(n + 16, dtype=torch.uint8, device=DEV)
+    T.taco_e5m2_encode(upload_f32(v), out, n)
+    torch.cuda.synchronize()
+    got = out[:n].cpu().numpy()
+    want = fm.encode_e5m2(v)
+    bad = got != want
+    assert not bad.any(), list(zip(v[bad][:10], got[bad][:10], want[bad][:10]))
+
+
+def test_e5m2_encoder_nan_is_a_nan_code():
+    v = np.array([np.nan, -np.nan, 1.0, np.nan], np.float32)
+    out = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    T.taco_e5m2_encode(upload_f32(v), out, 4)
+    torch.cuda.synchronize()
+    got = out[:4].cpu().numpy()
+    nan = ((got & 0x7C) == 0x7C) & ((got & 0x03) != 0)
+    assert nan[[0, 1, 3]].all() and got[2] == 0x3C
 
 
 # ----------------------------------------------------------- compress ----
@@ -221,6 +255,7 @@ def test_empty_tensor_is_a_no_op():
 
 PAIRS = [(cd.Codec.fp8(), cd.Codec.fp8()), (cd.Codec.fp8(64, True), cd.Codec.fp8(64, True)),
          (cd.Codec.fp8(32, False), cd.Codec.fp8(32, False)),
+         (cd.Codec.fp8e5(), cd.Codec.fp8e5()), (cd.Codec.fp8e5(32, False), cd.Codec.fp8e5(32, False)),
          (cd.Codec.int8_sym(), cd.Codec.int8_sym()), (cd.Codec.int4_asym(), cd.Codec.int8_asym()),
          (cd.Codec.int8_asym(), cd.Codec.int8_asym())]
 
@@ -312,7 +347,7 @@ def test_requantize(oc):
     T.taco_requantize(c, xd, rows, cols, 0.125, out)
     torch.cuda.synchronize()
     assert_same(parse(out, oc, rows, cols), oracle.requantize(oc, x, tensor_scale=np.float32(0.125)))
-    if oc.format == cd.FP8_DUAL:
+    if oc.format in cd.FP8_FORMATS:
         ws = new_workspace()
         out2 = T.empty_compressed(c, rows, cols)
         T.taco_requantize(c, xd, rows, cols, T.TACO_SCALE_AUTO, out2, workspace=ws)
@@ -394,7 +429,7 @@ def test_codec_overlapped_with_gemm_is_unchanged():
 
 # ------------------------------------------------- graph capture and replay ---
 
-@pytest.mark.parametrize("oc", [cd.Codec.fp8(), cd.Codec.int8_sym(), cd.Codec.int4_asym()], ids=cid)
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(), cd.Codec.fp8e5(), cd.Codec.int8_sym(), cd.Codec.int4_asym()], ids=cid)
 def test_graph_replays_match_eager_steps(oc):
     """A step (two compresses, FP8 with the delayed tensor scale, then the
     decompress-reduce) captured once in a HIP graph and replayed four times,
@@ -404,7 +439,7 @@ def test_graph_replays_match_eager_steps(oc):
     rows, cols, n, steps = 64, 4096, 2, 4
     c = ccodec(oc)
     cout = ccodec(cd.Codec.int8_asym() if oc.format == cd.INT4_ASYM else oc)
-    fp8 = oc.format == cd.FP8_DUAL
+    fp8 = oc.format in cd.FP8_FORMATS
     scale = T.TACO_SCALE_DELAYED if fp8 else 1.0
     data = [[bits_for((rows, cols), seed=900 + 10 * s + r, sigma=0.02 * (1 + s)) for r in range(n)]
             for s in range(steps)]
