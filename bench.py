@@ -18,6 +18,7 @@ Prints one JSON line. --gpus above 1 is refused: this build measures one GPU.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -42,6 +43,9 @@ def parse():
                     help="FP8 tensor scale: delayed (abs-max of the previous step, one pass), "
                          "auto (abs-max pre-pass of this tensor) or given (a fixed g, no workspace)")
     ap.add_argument("--launch", choices=["graph", "eager"], default="eager")
+    ap.add_argument("--fp8-codes", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="FP8 workloads: the code format of the dual-scale codec (E5M2 is the variant "
+                         "format 5)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--ring", action="store_true",
@@ -63,8 +67,8 @@ def parse():
 def algorithmic_bytes(w):
     """Bytes each kernel must move, from the formats' definitions."""
     n = w.n
-    if w.in_format == 1:
-        cbytes, meta_in = n, n // w.in_block          # E4M3 codes + int8 exponent per block
+    if w.in_format in (1, 5):
+        cbytes, meta_in = n, n // w.in_block          # FP8 codes + int8 exponent per block
         hdr = 16
     elif w.in_format == 2:
         cbytes, meta_in, hdr = n, 4 * (n // 64), 0
@@ -75,7 +79,7 @@ def algorithmic_bytes(w):
     shard = cbytes + meta_in + hdr
     if w.out_format is None:
         out = 4 * n
-    elif w.out_format == 1:
+    elif w.out_format in (1, 5):
         out = n + n // w.out_block + 16
     elif w.out_format == 2:
         out = n + 4 * (n // 64)
@@ -136,7 +140,7 @@ def measure_ring(w, xs, stream, K):
 def decode_bytes(w):
     """Bytes the consumer-side decode of the gather-stage output to bf16 moves."""
     n = w.n
-    if w.out_format == 1:
+    if w.out_format in (1, 5):
         src = n + n // w.out_block + 16
     elif w.out_format == 2:
         src = n + 4 * (n // 64)
@@ -399,11 +403,14 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.fp8_codes == "e5m2" and w.in_format == T.TACO_FMT_FP8_DUAL:
+        w = dataclasses.replace(w, in_format=T.TACO_FMT_FP8E5_DUAL,
+                                out_format=T.TACO_FMT_FP8E5_DUAL if w.out_format else None)
     torch.cuda.set_device(0)
     dev = "cuda"
     c_in = T.codec(w.in_format, w.in_block, 1 if w.hadamard else 0)
     c_out = T.codec(w.out_format, w.out_block, 1 if w.hadamard else 0) if w.out_format else None
-    fp8 = w.in_format == T.TACO_FMT_FP8_DUAL
+    fp8 = w.in_format in T.FP8_FORMATS
     scale = {"delayed": T.TACO_SCALE_DELAYED, "auto": T.TACO_SCALE_AUTO, "given": 0.01}[args.scale_mode] \
         if fp8 else 1.0
     use_ws = fp8 and args.scale_mode != "given"
@@ -538,7 +545,7 @@ def main():
 
     ring = None
     if args.ring:
-        if w.in_format == T.TACO_FMT_FP8_DUAL:
+        if w.in_format in T.FP8_FORMATS:
             sys.exit("--ring applies to the INT workloads (the FP8 codec is not a ring codec)")
         ring = measure_ring(w, xs[0], stream, K=max(10, K // 4))
 
@@ -572,9 +579,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.shards} bf16 shards of {w.rows}x{w.cols}; "
-                        f"compress {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym'][w.in_format]} "
+                        f"compress {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym', 'FP8 E5M2 dual-scale'][w.in_format]} "
                         f"block {w.in_block}{' + Hadamard' if w.hadamard else ''}; decompress-reduce "
-                        + (f"-> {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym'][w.out_format]}"
+                        + (f"-> {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym', 'FP8 E5M2 dual-scale'][w.out_format]}"
                            if w.out_format else "-> FP32 sum"),
             "shards": w.shards, "rows": w.rows, "cols": w.cols,
             "tensor_scale": args.scale_mode if fp8 else "n/a",
