@@ -187,7 +187,8 @@ template <int FMT, int B>
 struct LaneIn {
   uint4 q;
   float s;      // INT scale, FP8 combined scale g * 2^-k
-  uint32_t z;   // asymmetric zero point
+  uint32_t z;   // asymmetric zero point; in the reduce, FP8: the dword holding k
+  uint32_t sh;  // in the reduce, FP8: bit offset of k in z
 };
 
 template <int FMT, int B>
@@ -202,6 +203,7 @@ TACO_DEV LaneIn<FMT, B> load_in(const uint8_t* codes, const void* scale, const u
     r.q = *reinterpret_cast<const uint4*>(codes + e0);
   }
   r.z = 0;
+  r.sh = 0;
   if constexpr (is_fp8(FMT)) {
     const int k = static_cast<const int8_t*>(scale)[blk];
     r.s = (*g_hdr) * pow2f(-k);
@@ -461,7 +463,10 @@ TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int n) {
 // One lane's codes and block metadata of one shard. FP8: g is the shard's
 // tensor scale (0 for an empty slot).
 template <int FMT, int B>
-TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, float g, int zero_rel) {
+// FP8 leaves the exponent dword in z and its bit offset in sh: the scale is
+// formed when the lane is added (fp8_reduce_scale), so nothing here waits for
+// the loads.
+TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, int zero_rel) {
   LaneIn<FMT, B> r;
   const int blk = e0 / B;
   if constexpr (FMT == kINT4A) {
@@ -471,12 +476,13 @@ TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, float g,
     r.q = bload128<kNT>(s.codes, e0, 0);
   }
   r.z = 0;
+  r.sh = 0;
+  r.s = 0.0f;
   if constexpr (is_fp8(FMT)) {
     // the aligned dword holding the exponent byte (the resource is rounded up
     // to whole dwords, inside the region's padding)
-    const uint32_t w = bload32(s.meta, blk & ~3, 0);
-    const int k = (int)(int8_t)(uint8_t)(w >> (8 * (blk & 3)));
-    r.s = g * pow2f(-k);
+    r.z = bload32(s.meta, blk & ~3, 0);
+    r.sh = 8 * (blk & 3);
   } else {
     r.s = __uint_as_float(bload32(s.meta, blk * 4, 0));
     if constexpr (FMT == kINT4A || FMT == kINT8A) r.z = bload8(s.meta, blk, zero_rel);
@@ -492,9 +498,9 @@ struct ReduceGroup {
   static constexpr int NG = NMAX / GRP;                 // steps per tile (>= 2)
   LaneIn<FIN, BIN> in[GRP];
 
-  // Issue the loads of shard group `grp` of the tile at element e0. glane:
-  // lane r holds shard r's FP8 tensor scale.
-  TACO_DEV void load(const ReduceArgs& a, int grp, int e0, int n, float glane) {
+  // Issue the loads of shard group `grp` of the tile at element e0 (FP8: the
+  // scale is formed when the step is added).
+  TACO_DEV void load(const ReduceArgs& a, int grp, int e0, int n) {
     // With more than two groups the compiler would hoist every shard's
     // resources out of the loop and spill them; an opaque group index keeps
     // each step building only its own group's.
@@ -502,17 +508,22 @@ struct ReduceGroup {
 #pragma unroll
     for (int u = 0; u < GRP; ++u) {
       const int r = grp * GRP + u;
-      float g = 0.0f;
-      if constexpr (is_fp8(FIN)) g = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), r));
-      in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r, n), e0, g, a.zero_rel);
+      in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r, n), e0, a.zero_rel);
     }
   }
 
-  TACO_DEV void add_to(float* acc) const {
+  // Dequantize and add group `grp` (a compile-time step index). glane: lane r
+  // holds shard r's FP8 tensor scale g_r; the FP8 scale is g_r * 2^-k (exact).
+  TACO_DEV void add_to(float* acc, int grp, float glane) const {
 #pragma unroll
     for (int u = 0; u < GRP; ++u) {
+      LaneIn<FIN, BIN> x = in[u];
+      if constexpr (is_fp8(FIN)) {
+        const int k = (int)(int8_t)(uint8_t)(x.z >> x.sh);
+        x.s = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), grp * GRP + u)) * pow2f(-k);
+      }
       float d[16];
-      dequant_lane<FIN, BIN>(in[u], d);
+      dequant_lane<FIN, BIN>(x, d);
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
     }
@@ -528,25 +539,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   const int ntiles = (n + kWaveElems - 1) / kWaveElems;
   const int stride = (int)gridDim.x * (kBlockThreads / kWave);
   const bool rq = a.rq_codes != nullptr;
-  float glane = 0.0f;
+  // FP8: lane r < nshards points at shard r's tensor scale, every other lane at
+  // shard 0's (always present; empty slots load zero codes, so the scale they
+  // pick up multiplies zeros). The scales come in with
+  // one gather load issued behind the first step's data loads: a chain of
+  // dependent scalar loads here would hold every wave's first loads back, and
+  // an unconditional load keeps the wait counts exact.
+  typedef __attribute__((address_space(1))) const float* gfloat_ptr;
+  gfloat_ptr gp = (gfloat_ptr)a.in.g[0];
   if constexpr (is_fp8(FIN)) {
 #pragma unroll
-    for (int r = 0; r < NMAX; ++r)
-      if (r < a.nshards) {
-        const float gr = *a.in.g[r];
-        if (lane == r) glane = gr;
-      }
-  }
-  float inv_g = 0.0f;
-  if constexpr (is_fp8(FOUT)) {
-    if (rq) {
-      float gs = 0.0f;
-      for (int r = 0; r < a.nshards; ++r) gs = gs + *a.in.g[r];
-      gs = fminf(fmaxf(gs, kGMin), kGMax);
-      inv_g = 1.0f / gs;
-      if (blockIdx.x == 0 && threadIdx.x == 0 && a.write_g) *a.rq_g_hdr = gs;
+    for (int r = 1; r < NMAX; ++r) {
+      // the opaque copy keeps the selection in registers (the compiler would
+      // otherwise turn it into a load of the pointer array from memory)
+      gfloat_ptr pr = (gfloat_ptr)a.in.g[r];
+      asm volatile("" : "+s"(pr));
+      gp = (lane == r && r < a.nshards) ? pr : gp;
     }
   }
+  float glane = 0.0f;
   const int nb_out = n / BOUT;
   const rsrc_t r_sum = make_rsrc32(a.sum, a.sum ? 4 * n : 0);
   const rsrc_t r_qc = make_rsrc32(a.rq_codes, rq ? n : 0);
@@ -564,6 +575,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
                   r_sum, e0 * 4 + 16 * q, 0);
     }
     if (rq) {
+      // FP8: g' = g_0 + ... + g_{N-1} in shard order, clamped
+      float inv_g = 0.0f;
+      if constexpr (is_fp8(FOUT)) {
+        float gs = 0.0f;
+        for (int r = 0; r < a.nshards; ++r)
+          gs = gs + __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), r));
+        gs = fminf(fmaxf(gs, kGMin), kGMax);
+        inv_g = 1.0f / gs;
+        if (blockIdx.x == 0 && threadIdx.x == 0 && a.write_g) *a.rq_g_hdr = gs;
+      }
       // lanes beyond the tensor quantize zeros; their stores fall outside the
       // resources and are dropped
       LaneCodes q = quant_lane<FOUT, BOUT>(acc, inv_g, nullptr);
@@ -591,15 +612,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   RG buf[2];
-  buf[0].load(a, 0, t * kWaveElems + lane * kLaneElems, n, glane);
+  buf[0].load(a, 0, t * kWaveElems + lane * kLaneElems, n);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (is_fp8(FIN)) glane = *gp;   // lanes >= nshards: shard 0's g, read by no live step
   for (; t < ntiles; t += stride) {
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
       const int tn = k + 1 < NG ? t : t + stride;   // tile and group of step k + 1
       const int gn = (k + 1) % NG;
-      buf[(k + 1) & 1].load(a, gn, tn * kWaveElems + lane * kLaneElems, n, glane);
+      buf[(k + 1) & 1].load(a, gn, tn * kWaveElems + lane * kLaneElems, n);
       __builtin_amdgcn_sched_barrier(0);
-      buf[k & 1].add_to(acc);
+      buf[k & 1].add_to(acc, k, glane);
     }
     finish(t, acc);
   }
