@@ -245,8 +245,8 @@ TACO_DEV float wave_max(float a) {
 //
 // Banks. Three banks of 32 record lines each; call t
 //   * reads the previous call's maxima from bank (t + 2) % 3,
-//   * folds each workgroup's maximum into bank t % 3 (atomic max, not
-//     awaited),
+//   * folds each wave's or workgroup's maximum into bank t % 3 (atomic max,
+//     not awaited),
 //   * zeroes bank (t + 1) % 3 for the next call (first wave of workgroup 0).
 // No bank is read and written by the same call, and the kernel boundary orders
 // calls, so there is no fence, no spin and no "last workgroup" chain. Every
@@ -341,6 +341,14 @@ TACO_DEV void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Fold this wave's max (any value per lane) into its record line of bank e
+// (one atomic per wave, no barrier). Every lane of the wave calls it.
+TACO_DEV void ws_record_wave(Workspace* ws, uint32_t e, float lane_max) {
+  const float m = wave_max(lane_max);
+  const uint32_t line = (blockIdx.x * (kBlockThreads / kWave) + wave_in_group()) % kAccLines;
+  if ((threadIdx.x & (kWave - 1)) == 0) TACO_AT_MAX(&ws->bank[e][line].amax, __float_as_uint(m));
 }
 
 // Fold the workgroup's max (any value per lane) into its record line of bank
