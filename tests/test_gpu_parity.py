@@ -178,6 +178,26 @@ def test_workspace_history_across_grid_sizes():
         assert calls == i + 1 and np.float32(amax) == prev, f"call {i}: history ({calls}, {amax}) != {prev}"
 
 
+def test_workspace_history_over_many_grid_sizes():
+    """Delayed-scale calls on one workspace whose grids take 1, 2, 3, 15-17,
+    63-65 and 100 workgroups (a [4 G, 1024] tensor runs G workgroups of the
+    persistent grid), alternating with the E5M2 codec: every call's tensor
+    scale comes from the previous call's abs-max, and the call count advances
+    by one per call."""
+    ws = new_workspace()
+    prev = np.float32(0.0)
+    for i, G in enumerate([1, 2, 3, 15, 16, 17, 63, 64, 65, 100, 1]):
+        oc = cd.Codec.fp8e5() if i % 3 == 2 else cd.Codec.fp8()
+        shape = (4 * G, 1024)
+        bits = bits_for(shape, seed=700 + i, sigma=0.01 * (1 + i % 4))
+        g = cd.auto_tensor_scale(np.array([prev], dtype=np.float32), oc.format)
+        buf, _ = gpu_compress(oc, bits, scale=T.TACO_SCALE_DELAYED, ws=ws)
+        assert_same(parse(buf, oc, *shape), oracle.compress(oc, bits, tensor_scale=g), f"call {i}: G = {G}")
+        prev = np.float32(np.max(np.abs(cd.transform(oc, bits))))
+        calls, amax, _ = T.workspace_history(ws)
+        assert calls == i + 1 and np.float32(amax) == prev, f"call {i}: history ({calls}, {amax}) != {prev}"
+
+
 @pytest.mark.parametrize("oc", ALL, ids=cid)
 def test_compress_debug_prequant(oc):
     shape = (5, 2560) if oc.block != 128 or oc.format != cd.INT8_SYM else (5, 2560)
