@@ -70,7 +70,9 @@ extern "C" {
  *                    per block of 64 (value = q * s).
  * TACO_FMT_INT4_ASYM [FlashComm] 4-bit codes, two per byte (element 2j in the
  *                    low nibble), float32 scale s and uint8 zero point z per
- *                    group of 128 (value = (q - z) * s).
+ *                    group of 128 (value = (q - z) * s). Compression writes
+ *                    z in [0, 15]; buffers read back must keep z <= 15
+ *                    (larger zero points give unspecified values).
  * TACO_FMT_INT8_ASYM [FlashComm] the same at 8 bits (gather stage).
  * TACO_FMT_FP8E5_DUAL the TACO dual-scale scheme with E5M2 codes instead of
  *                    E4M3 ([TACO] Fig. 3 sets E5M2 beside E4M3; bit layout of

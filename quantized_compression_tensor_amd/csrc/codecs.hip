@@ -49,33 +49,36 @@ TACO_DEV void load_lane(const void* x, int64_t e0, float* a) {
   }
 }
 
-TACO_DEV float absmax16(const float* a) { return fmaxf(absmax8(a), absmax8(a + 8)); }
+// max |a|, max a and min a over a lane's V = 8 or 16 values
+template <int V>
+TACO_DEV float absmax_v(const float* a) {
+  if constexpr (V == 8) return absmax8(a);
+  else return fmaxf(absmax8(a), absmax8(a + 8));
+}
 
-TACO_DEV float max16(const float* a) {
+template <int V>
+TACO_DEV float max_v(const float* a) {
   float m = a[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) m = fmaxf(m, a[i]);
+  for (int i = 1; i < V; ++i) m = fmaxf(m, a[i]);
   return m;
 }
 
-TACO_DEV float min16(const float* a) {
+template <int V>
+TACO_DEV float min_v(const float* a) {
   float m = a[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) m = fminf(m, a[i]);
+  for (int i = 1; i < V; ++i) m = fminf(m, a[i]);
   return m;
-}
-
-TACO_DEV uint32_t pack_u8x4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-         ((uint32_t)d << 24);
 }
 
 TACO_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // --------------------------------------------------------- quantization --
 //
-// Per-lane result of quantizing 16 values: code bytes (INT4: 8 bytes in
-// words x, y) and the block metadata, valid in every lane of the block.
+// Per-lane result of quantizing V = 8 or 16 consecutive values (a block of B
+// spans B / V lanes): code bytes in words x, y, z, w from the first (INT4:
+// V / 2 bytes) and the block metadata, valid in every lane of the block.
 struct LaneCodes {
   uint4 q;
   float s;      // INT scale, or unused
@@ -86,99 +89,168 @@ struct LaneCodes {
 // FP8 dual-scale on values already in the codec's domain. m = max|a| / g,
 // k = block exponent, each value scaled by the exact (1/g) * 2^k; an exact
 // zero becomes +0 through the +0 addend of the fused multiply-add.
-template <int B, bool E5>
+template <int B, bool E5, int V>
 TACO_DEV LaneCodes quant_fp8(float* a, float inv_g, float* pre) {
   using F = Fp8Code<E5>;
-  constexpr int G = B / kLaneElems;
+  constexpr int G = B / V;
   LaneCodes r;
-  const float M = group_max<G>(absmax16(a));
+  const float M = group_max<G>(absmax_v<V>(a));
   const float m = M * inv_g;
   r.k = block_exponent<E5>(m);
   const float c = inv_g * pow2f(r.k);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a[i] = fmaf(a[i], c, 0.0f);
+  for (int i = 0; i < V; ++i) a[i] = fmaf(a[i], c, 0.0f);
   if (__builtin_expect(m * pow2f(r.k) > F::kMax, 0)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = sat_fp8<E5>(a[i]);
+    for (int i = 0; i < V; ++i) a[i] = sat_fp8<E5>(a[i]);
   }
   if (pre) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pre[i] = a[i];
+    for (int i = 0; i < V; ++i) pre[i] = a[i];
   }
+  r.q = make_uint4(0, 0, 0, 0);
   r.q.x = F::pack4(a[0], a[1], a[2], a[3]);
   r.q.y = F::pack4(a[4], a[5], a[6], a[7]);
-  r.q.z = F::pack4(a[8], a[9], a[10], a[11]);
-  r.q.w = F::pack4(a[12], a[13], a[14], a[15]);
+  if constexpr (V == 16) {
+    r.q.z = F::pack4(a[8], a[9], a[10], a[11]);
+    r.q.w = F::pack4(a[12], a[13], a[14], a[15]);
+  }
   r.s = 0.0f; r.z = 0;
   return r;
 }
 
-// Symmetric INT8 over a block of 64: s = A/127, q = round(a * (127/A)).
-TACO_DEV LaneCodes quant_int8_sym(const float* a, float* pre) {
-  LaneCodes r;
-  const float A = group_max<4>(absmax16(a));
-  const bool live = A >= kTiny;
-  r.s = live ? A / 127.0f : 0.0f;
-  const float inv = live ? 127.0f / A : 0.0f;
-  int q[16];
+// Scale and reciprocal of a block from its statistic m (INT8 symmetric: the
+// abs-max; asymmetric: the range hi - lo): s = m / QMAX and inv = QMAX / m,
+// both 0 for a block with m < 2^-100 (which then quantizes to zeros).
+template <int QMAX>
+TACO_DEV void block_scales(float m, float& s, float& inv) {
+  const bool live = m >= kTiny;
+  s = live ? m / (float)QMAX : 0.0f;
+  inv = live ? (float)QMAX / m : 0.0f;
+}
+
+// The same for the two blocks a lane holds in the two-half tile layout, with
+// one division per quantity: the lanes with bit 2 set divide for the second
+// half, the others for the first, and each takes the other result from its
+// mirror lane (lane ^ 7 within its eight-lane half-row), which lies in the
+// same block of both halves when a block spans at least eight lanes.
+template <int QMAX>
+TACO_DEV void block_scales_pair(float m0, float m1, float* s, float* inv) {
+  const bool upper = (threadIdx.x & 4) != 0;
+  float sm, im;
+  block_scales<QMAX>(upper ? m1 : m0, sm, im);
+  constexpr int kMirror = 0x141;   // DPP row_half_mirror
+  const float so = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sm), kMirror, 0xF, 0xF, false));
+  const float io = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(im), kMirror, 0xF, 0xF, false));
+  s[0] = upper ? so : sm; s[1] = upper ? sm : so;
+  inv[0] = upper ? io : im; inv[1] = upper ? im : io;
+}
+
+// Four bytes (the low byte of each value) into one word.
+TACO_DEV uint32_t pack_bytes(int a, int b, int c, int d) {
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);   // a.b0, b.b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x04000c0cu);   // 0, 0, c.b0, d.b0
+  return lo | hi;
+}
+
+// Eight 4-bit values in [0, 15] into one word, element 0 in the low nibble:
+// one shift-or per value (a chain the compiler would otherwise rebalance into
+// separate shifts and three-way ors).
+TACO_DEV uint32_t pack_nibbles(const int* q) {
+  uint32_t w = (uint32_t)q[0];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int b = 1; b < 8; ++b)
+    asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(w) : "v"(q[b]), "i"(4 * b), "v"(w));
+  return w;
+}
+
+// Symmetric INT8 over a block of 64: q = round(a * inv), given the block's
+// s = A/127 and inv = 127/A.
+template <int V>
+TACO_DEV LaneCodes int8_sym_encode(const float* a, float s, float inv, float* pre) {
+  LaneCodes r;
+  r.s = s;
+  int q[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
     const float t = a[i] * inv;
     if (pre) pre[i] = t;
     q[i] = clampi(rne_int(t), -127, 127);
   }
-  r.q.x = pack_u8x4(q[0], q[1], q[2], q[3]);
-  r.q.y = pack_u8x4(q[4], q[5], q[6], q[7]);
-  r.q.z = pack_u8x4(q[8], q[9], q[10], q[11]);
-  r.q.w = pack_u8x4(q[12], q[13], q[14], q[15]);
+  r.q = make_uint4(0, 0, 0, 0);
+  r.q.x = pack_bytes(q[0], q[1], q[2], q[3]);
+  r.q.y = pack_bytes(q[4], q[5], q[6], q[7]);
+  if constexpr (V == 16) {
+    r.q.z = pack_bytes(q[8], q[9], q[10], q[11]);
+    r.q.w = pack_bytes(q[12], q[13], q[14], q[15]);
+  }
   r.k = 0; r.z = 0;
   return r;
 }
 
-// Asymmetric min/max over a group of 128, BITS = 4 or 8.
-template <int BITS>
-TACO_DEV LaneCodes quant_asym(const float* a, float* pre) {
+template <int V>
+TACO_DEV float int8_sym_stat(const float* a) { return group_max<64 / V>(absmax_v<V>(a)); }
+
+template <int V>
+TACO_DEV LaneCodes quant_int8_sym(const float* a, float* pre) {
+  float s, inv;
+  block_scales<127>(int8_sym_stat<V>(a), s, inv);
+  return int8_sym_encode<V>(a, s, inv, pre);
+}
+
+// Asymmetric min/max over a group of 128, BITS = 4 or 8: lo = min(min a, 0),
+// hi = max(max a, 0); the statistic is the range hi - lo.
+template <int V>
+TACO_DEV float asym_stat(const float* a, float& lo) {
+  constexpr int G = 128 / V;
+  lo = fminf(group_min<G>(min_v<V>(a)), 0.0f);
+  const float hi = fmaxf(group_max<G>(max_v<V>(a)), 0.0f);
+  return hi - lo;
+}
+
+// z = clamp(round(-lo * inv)), q = clamp(round(a * inv) + z).
+template <int BITS, int V>
+TACO_DEV LaneCodes asym_encode(const float* a, float lo, float s, float inv, float* pre) {
   constexpr int QMAX = (1 << BITS) - 1;
   LaneCodes r;
-  const float lo = fminf(group_min<8>(min16(a)), 0.0f);
-  const float hi = fmaxf(group_max<8>(max16(a)), 0.0f);
-  const float rg = hi - lo;
-  const bool live = rg >= kTiny;
-  r.s = live ? rg / (float)QMAX : 0.0f;
-  const float inv = live ? (float)QMAX / rg : 0.0f;
+  r.s = s;
   r.z = clampi(rne_int((-lo) * inv), 0, QMAX);
-  int q[16];
+  int q[V];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < V; ++i) {
     const float t = a[i] * inv;
     if (pre) pre[i] = t;
     q[i] = clampi(rne_int(t) + r.z, 0, QMAX);
   }
+  r.q = make_uint4(0, 0, 0, 0);
   if constexpr (BITS == 4) {
-    uint32_t w[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      w[j] = 0;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) w[j] |= (uint32_t)q[8 * j + b] << (4 * b);
-    }
-    r.q = make_uint4(w[0], w[1], 0, 0);
+    r.q.x = pack_nibbles(q);
+    if constexpr (V == 16) r.q.y = pack_nibbles(q + 8);
   } else {
-    r.q.x = pack_u8x4(q[0], q[1], q[2], q[3]);
-    r.q.y = pack_u8x4(q[4], q[5], q[6], q[7]);
-    r.q.z = pack_u8x4(q[8], q[9], q[10], q[11]);
-    r.q.w = pack_u8x4(q[12], q[13], q[14], q[15]);
+    r.q.x = pack_bytes(q[0], q[1], q[2], q[3]);
+    r.q.y = pack_bytes(q[4], q[5], q[6], q[7]);
+    if constexpr (V == 16) {
+      r.q.z = pack_bytes(q[8], q[9], q[10], q[11]);
+      r.q.w = pack_bytes(q[12], q[13], q[14], q[15]);
+    }
   }
   r.k = 0;
   return r;
 }
 
-template <int FMT, int B>
+template <int BITS, int V>
+TACO_DEV LaneCodes quant_asym(const float* a, float* pre) {
+  float lo, s, inv;
+  block_scales<(1 << BITS) - 1>(asym_stat<V>(a, lo), s, inv);
+  return asym_encode<BITS, V>(a, lo, s, inv, pre);
+}
+
+template <int FMT, int B, int V = kLaneElems>
 TACO_DEV LaneCodes quant_lane(float* a, float inv_g, float* pre) {
-  if constexpr (is_fp8(FMT)) return quant_fp8<B, FMT == kFP8E5>(a, inv_g, pre);
-  else if constexpr (FMT == kINT8S) return quant_int8_sym(a, pre);
-  else if constexpr (FMT == kINT4A) return quant_asym<4>(a, pre);
-  else return quant_asym<8>(a, pre);
+  if constexpr (is_fp8(FMT)) return quant_fp8<B, FMT == kFP8E5, V>(a, inv_g, pre);
+  else if constexpr (FMT == kINT8S) return quant_int8_sym<V>(a, pre);
+  else if constexpr (FMT == kINT4A) return quant_asym<4, V>(a, pre);
+  else return quant_asym<8, V>(a, pre);
 }
 
 // ------------------------------------------------------- dequantization --
@@ -268,6 +340,43 @@ TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
   }
 }
 
+// INT4 asymmetric, the reduce's form: the same values as dequant_lane, in
+// half the instructions. Two codes share one dword as 16-bit halves holding
+// c = q + 16 - z in [1, 31] (no half borrows from or carries into the other);
+// read as a half-precision subnormal, a half is c * 2^-24 (or, for the codes
+// left in bits 4-8 of their half, 16 c * 2^-24) exactly, and one mixed-
+// precision fused multiply-add per value forms (q - z) * s = c * s - 16 s
+// with a single rounding: c * 2^-24 * (s * 2^24) is the exact product and
+// 16 s is exact. Valid when every zero point is at most 15 and |s| < 2^100
+// (s * 2^24 finite); int4_fast_ok tells.
+TACO_DEV float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+TACO_DEV float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+template <int B>
+TACO_DEV bool int4_fast_ok(const LaneIn<kINT4A, B>& in) {
+  return fabsf(in.s) < 0x1p100f && in.z <= 15u;
+}
+
+template <int B>
+TACO_DEV void dequant_int4_fast(const LaneIn<kINT4A, B>& in, float* d) {
+  const uint32_t zr = 0x00100010u - in.z * 0x00010001u;   // 16 - z in each half
+  const uint32_t zr16 = zr << 4;
+  const float s24 = in.s * 0x1p24f, s20 = in.s * 0x1p20f, m16 = in.s * -16.0f;
+  const uint32_t w[2] = {in.q.x, in.q.y};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t a = (w[j] & 0x000F000Fu) + zr;            // elements 0 and 4 of the dword
+    const uint32_t b = (w[j] & 0x00F000F0u) + zr16;          // 1 and 5, times 16
+    const uint32_t c = ((w[j] >> 8) & 0x000F000Fu) + zr;     // 2 and 6
+    const uint32_t e = ((w[j] >> 8) & 0x00F000F0u) + zr16;   // 3 and 7, times 16
+    float* o = d + 8 * j;
+    o[0] = fmaf(half_lo(a), s24, m16); o[4] = fmaf(half_hi(a), s24, m16);
+    o[1] = fmaf(half_lo(b), s20, m16); o[5] = fmaf(half_hi(b), s20, m16);
+    o[2] = fmaf(half_lo(c), s24, m16); o[6] = fmaf(half_hi(c), s24, m16);
+    o[3] = fmaf(half_lo(e), s20, m16); o[7] = fmaf(half_hi(e), s20, m16);
+  }
+}
+
 // ---------------------------------------------------------------- kernels --
 
 struct QuantK {
@@ -306,15 +415,58 @@ TACO_DEV void store_lane(const LaneCodes& r, int64_t e0, uint8_t* codes, void* s
   }
 }
 
-// Quantization without a transform. Grid-stride over 1024-element wave tiles,
-// no explicit prefetch: the launch gives every wave one tile and relies on
-// full occupancy for the loads in flight (measured faster than a two-buffer
-// pipeline on a persistent grid).
+// Quantization of the two halves of a wave tile (lane layout of k_quantize):
+// the integer formats share one division per scale between the halves.
+template <int FMT, int B>
+TACO_DEV void quant_halves(float (*v)[8], float inv_g, float (*pre)[8], LaneCodes* r) {
+  constexpr int V = 8;
+  if constexpr (FMT == kINT8S) {
+    static_assert(64 / V >= 8, "a block spans the mirror pairs of block_scales_pair");
+    float s[2], inv[2];
+    block_scales_pair<127>(int8_sym_stat<V>(v[0]), int8_sym_stat<V>(v[1]), s, inv);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r[h] = int8_sym_encode<V>(v[h], s[h], inv[h], pre ? pre[h] : nullptr);
+  } else if constexpr (FMT == kINT4A || FMT == kINT8A) {
+    static_assert(128 / V >= 8, "a block spans the mirror pairs of block_scales_pair");
+    constexpr int BITS = FMT == kINT4A ? 4 : 8;
+    float lo[2], s[2], inv[2];
+    const float m0 = asym_stat<V>(v[0], lo[0]);
+    const float m1 = asym_stat<V>(v[1], lo[1]);
+    block_scales_pair<(1 << BITS) - 1>(m0, m1, s, inv);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r[h] = asym_encode<BITS, V>(v[h], lo[h], s[h], inv[h], pre ? pre[h] : nullptr);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r[h] = quant_lane<FMT, B, V>(v[h], inv_g, pre ? pre[h] : nullptr);
+  }
+}
+
+// Quantization without a transform. Each wave tile of 1024 elements is two
+// halves of 512, and a lane holds 8 consecutive elements of each half, so
+// every load instruction of a wave reads one contiguous run (1 KiB of bf16;
+// measured 7 % faster than 16 consecutive elements per lane, whose two loads
+// each touch every other 16 bytes). A block of B elements spans B / 8 lanes of
+// one half. Each tile's accesses go through buffer resources clipped at the
+// tensor's end (a ragged tail loads zeros and its stores are dropped). The
+// launch gives every wave one tile and relies on full occupancy for the loads
+// in flight; the loop only matters for grids smaller than that.
 template <int FMT, int B, bool F32IN, bool DEBUG>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
+  constexpr int V = 8;                      // elements per lane and half
+  constexpr int HALF = kWaveElems / 2;      // 512
+  constexpr int ES = F32IN ? 4 : 2;         // input bytes per element
+  constexpr int NQ = V * ES / 16;           // 16-byte loads per lane and half
+  constexpr int G = B / V;                  // lanes per block
+  constexpr int BPH = HALF / B;             // blocks per half
+  constexpr int CB = FMT == kINT4A ? 2 : 1; // elements per code byte
+  constexpr int MB = is_fp8(FMT) ? 1 : 4;   // bytes per block scale
+  constexpr bool ASYM = FMT == kINT4A || FMT == kINT8A;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t ntiles = (a.n + kWaveElems - 1) / kWaveElems;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  // elements of the last (possibly partial) tile; a multiple of B, so each
+  // lane's run lies wholly inside or outside the tensor
+  const int tail = (int)(a.n - (ntiles - 1) * kWaveElems);
   float inv_g = 0.0f;
   uint32_t e = 0;
   if constexpr (is_fp8(FMT)) {
@@ -337,25 +489,55 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.g_hdr = g;
   }
   float run_max = 0.0f;
-  for (int64_t tile = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); tile < ntiles;
-       tile += stride) {
-    const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
-    const bool valid = e0 < a.n;   // n is a multiple of B, B a multiple of 16
-    float v[16];
-    if (valid) load_lane<F32IN>(a.x, e0, v);
-    else {
+  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
+    const int64_t base = t * kWaveElems;
+    const int rt = t == ntiles - 1 ? tail : kWaveElems;   // elements of this tile
+    const rsrc_t rx = make_rsrc32(static_cast<const uint8_t*>(a.x) + base * ES, rt * ES);
+    uint4 raw[2][NQ];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) raw[h][q] = bload128<kNT>(rx, lane * V * ES + 16 * q, h * HALF * ES);
+    float v[2][V];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          v[h][4 * q + 0] = __uint_as_float(raw[h][q].x); v[h][4 * q + 1] = __uint_as_float(raw[h][q].y);
+          v[h][4 * q + 2] = __uint_as_float(raw[h][q].z); v[h][4 * q + 3] = __uint_as_float(raw[h][q].w);
+        }
+      } else {
+        const uint4 w = raw[h][0];
+        v[h][0] = bf16_lo(w.x); v[h][1] = bf16_hi(w.x); v[h][2] = bf16_lo(w.y); v[h][3] = bf16_hi(w.y);
+        v[h][4] = bf16_lo(w.z); v[h][5] = bf16_hi(w.z); v[h][6] = bf16_lo(w.w); v[h][7] = bf16_hi(w.w);
+      }
+      if constexpr (is_fp8(FMT)) run_max = fmaxf(run_max, absmax_v<V>(v[h]));
     }
-    if constexpr (is_fp8(FMT)) run_max = fmaxf(run_max, absmax16(v));
-    float pre[16];
-    LaneCodes r = quant_lane<FMT, B>(v, inv_g, DEBUG ? pre : nullptr);
-    if (valid) {
-      store_lane<FMT, B>(r, e0, a.codes, a.scale, a.zero);
-      if constexpr (DEBUG) {
-        float4* d = reinterpret_cast<float4*>(a.dbg + e0);
+    float pre[2][V];
+    LaneCodes r[2];
+    quant_halves<FMT, B>(v, inv_g, DEBUG ? pre : nullptr, r);
+    const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
+    const rsrc_t rs = make_rsrc32(static_cast<uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
+    const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
+    const int blk = lane / G;   // every lane of a block stores the same metadata
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d[q] = make_float4(pre[4 * q], pre[4 * q + 1], pre[4 * q + 2], pre[4 * q + 3]);
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (FMT == kINT4A) bstore32(r[h].q.x, rc, lane * (V / 2), h * HALF / 2);
+      else bstore64(make_uint2(r[h].q.x, r[h].q.y), rc, lane * V, h * HALF);
+      if constexpr (is_fp8(FMT)) {
+        bstore8((uint32_t)r[h].k, rs, blk, h * BPH);
+      } else {
+        bstore32(__float_as_uint(r[h].s), rs, 4 * blk, 4 * h * BPH);
+        if constexpr (ASYM) bstore8((uint32_t)r[h].z, rz, blk, h * BPH);
+      }
+      if constexpr (DEBUG) {
+        const rsrc_t rd = make_rsrc32(a.dbg + base, rt * 4);
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q)
+          bstore128(make_uint4(__float_as_uint(pre[h][4 * q]), __float_as_uint(pre[h][4 * q + 1]),
+                               __float_as_uint(pre[h][4 * q + 2]), __float_as_uint(pre[h][4 * q + 3])),
+                    rd, lane * V * 4 + 16 * q, h * HALF * 4);
       }
     }
   }
@@ -373,15 +555,26 @@ __global__ __launch_bounds__(kBlockThreads) void k_amax(const void* x, int64_t n
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t ntiles = (n + kWaveElems - 1) / kWaveElems;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  constexpr int ES = F32IN ? 4 : 2;
+  constexpr int NQ = kLaneElems * ES / 16;   // 16-byte loads per lane; load q reads bytes [1024 q, 1024 q + 1024)
   float m = 0.0f;
-  for (int64_t tile = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); tile < ntiles;
-       tile += stride) {
-    const int64_t e0 = tile * kWaveElems + (int64_t)lane * kLaneElems;
-    if (e0 < n) {
-      float v[16];
-      load_lane<F32IN>(x, e0, v);
-      m = fmaxf(m, absmax16(v));
+  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
+    const int64_t base = t * kWaveElems;
+    const rsrc_t rx = make_rsrc(static_cast<const uint8_t*>(x) + base * ES, (n - base) * ES);
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint4 w = bload128<kNT>(rx, lane * 16, q * 1024);
+      if constexpr (F32IN) {
+        v[4 * q + 0] = __uint_as_float(w.x); v[4 * q + 1] = __uint_as_float(w.y);
+        v[4 * q + 2] = __uint_as_float(w.z); v[4 * q + 3] = __uint_as_float(w.w);
+      } else {
+        v[8 * q + 0] = bf16_lo(w.x); v[8 * q + 1] = bf16_hi(w.x); v[8 * q + 2] = bf16_lo(w.y);
+        v[8 * q + 3] = bf16_hi(w.y); v[8 * q + 4] = bf16_lo(w.z); v[8 * q + 5] = bf16_hi(w.z);
+        v[8 * q + 6] = bf16_lo(w.w); v[8 * q + 7] = bf16_hi(w.w);
+      }
     }
+    m = fmaxf(m, absmax_v<16>(v));   // a ragged tail loads zeros
   }
   __shared__ float lds_m[kBlockThreads / kWave];
   __shared__ uint32_t lds_e;
@@ -523,9 +716,34 @@ struct ReduceGroup {
         x.s = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(glane), grp * GRP + u)) * pow2f(-k);
       }
       float d[16];
-      dequant_lane<FIN, BIN>(x, d);
+      if constexpr (FIN == kINT4A) {
+        // the fast form when the whole wave qualifies (always, for shards the
+        // compressor wrote); the first shard's values are the sum so far
+        // (0 + d = d: the fast form never yields -0).
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!int4_fast_ok<BIN>(x)) == 0, 1)) {
+          dequant_int4_fast<BIN>(x, d);
+          if (grp == 0 && u == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
+            for (int i = 0; i < 16; ++i) acc[i] = d[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
+          }
+        } else {
+          dequant_lane<FIN, BIN>(x, d);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            acc[i] = acc[i] + d[i];
+            // keeps the compiler from merging the two branches' adds after
+            // the branch, which would hold every step's values at once
+            asm volatile("" : "+v"(acc[i]));
+          }
+        }
+      } else {
+        dequant_lane<FIN, BIN>(x, d);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = acc[i] + d[i];
+      }
     }
   }
 };
@@ -691,7 +909,8 @@ static dim3 grid_for(int64_t n) {
 
 // One wave per tile and as many workgroups as that takes: the hardware keeps
 // every CU at full occupancy as waves retire (5-8 % faster than a grid capped
-// at 4 workgroups per CU on the INT8 and INT4 compress).
+// at 4 workgroups per CU on the INT8 and INT4 compress; two or four tiles per
+// wave with all their loads issued first measured 2-7 % slower).
 static dim3 quant_grid(const QuantArgs& a) { return grid_for(a.n); }
 
 template <int FMT, int B>

@@ -332,6 +332,62 @@ def test_reduce_with_zero_shards_and_repeats():
     assert_same(parse(out, cout, rows, cols), rq)
 
 
+def _upload_compressed(ref: oracle.Compressed):
+    """A device buffer in the library's layout holding the given shard."""
+    c = ccodec(ref.codec)
+    buf = T.empty_compressed(c, ref.rows, ref.cols)
+    buf.zero_()
+    codes, sc, aux, _ = T.regions(buf, c, ref.rows, ref.cols)
+    codes.copy_(torch.from_numpy(ref.codes))
+    sc.copy_(torch.from_numpy(ref.scale.astype(np.float32)))
+    if ref.zero is not None:
+        aux.copy_(torch.from_numpy(ref.zero))
+    return buf
+
+
+@pytest.mark.parametrize("nshards", [1, 3, 8])
+def test_reduce_int4_handmade_shards(nshards):
+    """INT4 shards written directly rather than by the compressor: arbitrary
+    codes and zero points in [0, 15], and scales from subnormal to beyond
+    2^100, infinite, NaN, zero of either sign and negative, placed so that
+    some 1024-element tiles hold only ordinary scales and others mix in the
+    extremes. The sum is compared bit for bit (NaN as a class); the INT8
+    re-quantization on every group whose sum is finite."""
+    cin, cout = cd.Codec.int4_asym(), cd.Codec.int8_asym()
+    rows, cols = 6, 2048   # 12 tiles of 1024, 96 groups
+    rng = np.random.default_rng(77 + nshards)
+    ngroups = rows * cols // 128
+    extremes = np.array([1e-40, 2.0 ** -149, 0.0, -0.0, -0.37, 2.0 ** 100, 2.0 ** 101, 3e38,
+                         np.inf, -np.inf, np.nan, 2.0 ** 99], np.float32)
+    refs, bufs = [], []
+    for r in range(nshards):
+        codes = rng.integers(0, 256, rows * cols // 2, dtype=np.uint8)
+        zero = rng.integers(0, 16, ngroups, dtype=np.uint8)
+        scale = (rng.random(ngroups, dtype=np.float32) * np.float32(0.01)).astype(np.float32)
+        # tiles 1, 4 and 9 (groups 8t .. 8t + 7) carry extreme scales, a
+        # different one per shard; tile 6 only subnormal and zero scales
+        for t in (1, 4, 9):
+            scale[8 * t + (r % 8)] = extremes[(3 * t + r) % len(extremes)]
+        scale[48:56] = np.array([1e-40, 0.0, -0.0, 2.0 ** -149, 3e-39, 1e-45, 0.0, 5e-39], np.float32)
+        ref = oracle.Compressed(cin, rows, cols, codes, scale, zero)
+        refs.append(ref)
+        bufs.append(_upload_compressed(ref))
+    acc, rq = oracle.decompress_reduce(refs, cout)
+    s = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+    out = T.empty_compressed(ccodec(cout), rows, cols)
+    T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, s, ccodec(cout), out)
+    torch.cuda.synchronize()
+    got = s.cpu().numpy()
+    assert same_f32_bits(got, acc).all()
+    g = parse(out, cout, rows, cols)
+    finite = np.isfinite(acc.reshape(-1, 128)).all(axis=1)
+    assert finite.sum() >= ngroups // 2
+    gq, rqc = g["codes"].reshape(-1, 128), rq.codes.reshape(-1, 128)
+    assert (gq[finite] == rqc[finite]).all()
+    assert (g["scale"][finite].view(np.uint32) == rq.scale[finite].view(np.uint32)).all()
+    assert (g["zero"][finite] == rq.zero[finite]).all()
+
+
 # ------------------------------------------------------------- decode ----
 
 @pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
