@@ -65,12 +65,13 @@ TACO_DEV uint2 bload64(rsrc_t r, int voff, int soff) {
 }
 TACO_DEV uint32_t bload32(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0); }
 TACO_DEV uint32_t bload8(rsrc_t r, int voff, int soff) { return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0); }
-// Stores of the codes and scales are streaming (non-temporal): the compressed
-// tensors are written once and consumed elsewhere, so they should not displace
-// other data in the caches.
+// Stores of the codes and scales are streaming (non-temporal) by default: the
+// compressed tensors are written once and consumed elsewhere, so they should
+// not displace other data in the caches.
+template <int AUX = kNT>
 TACO_DEV void bstore128(uint4 v, rsrc_t r, int voff, int soff) {
   u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kNT);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, AUX);
 }
 TACO_DEV void bstore64(uint2 v, rsrc_t r, int voff, int soff) {
   u32x2 w = {v.x, v.y};
