@@ -123,18 +123,13 @@ static_assert(4 * kReducePiece < (int64_t(1) << 31), "a piece's float32 sum must
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 // Workgroups per CU (4 waves each) of the persistent FP8 compress of small
-// tensors and of the persistent reduce of the asymmetric formats.
+// tensors.
 #ifndef TACO_GROUPS_PER_CU
 #define TACO_GROUPS_PER_CU 4
 #endif
 constexpr int kPersistentGroupsPerCU = TACO_GROUPS_PER_CU;
 static_assert(kPersistentGroupsPerCU > 0, "persistent kernels need at least one workgroup per CU");
-#ifndef TACO_REDUCE_GROUPS_PER_CU
-#define TACO_REDUCE_GROUPS_PER_CU 4
-#endif
-constexpr int kReduceGroupsPerCU = TACO_REDUCE_GROUPS_PER_CU;
-static_assert(kReduceGroupsPerCU > 0, "reduce workgroups per CU");
-// Tiles per wave of the memory-bound reduce (one workgroup per 4 * this many).
+// Tiles per wave of the reduce (one workgroup per 4 * this many).
 #ifndef TACO_REDUCE_TILES_PER_WAVE
 #define TACO_REDUCE_TILES_PER_WAVE 1
 #endif
