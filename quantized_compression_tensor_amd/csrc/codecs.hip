@@ -147,6 +147,24 @@ TACO_DEV void block_scales_pair(float m0, float m1, float* s, float* inv) {
   inv[0] = upper ? io : im; inv[1] = upper ? im : io;
 }
 
+// The same with one division per lane, for a block of G = 4 or 8 lanes that
+// all hold its statistic m and are all active: the lanes with bit G/2 set
+// divide for the reciprocal, the others for the scale, and each takes the
+// other result from its mirror lane (lane ^ (G - 1) inside the block: a quad
+// permute for 4 lanes, the half-row mirror for 8).
+template <int QMAX, int G>
+TACO_DEV void block_scales_split(float m, float& s, float& inv) {
+  static_assert(G == 4 || G == 8, "a block of 4 or 8 lanes");
+  constexpr int kMirror = G == 8 ? 0x141 : 0x1B;   // DPP row_half_mirror / quad_perm [3, 2, 1, 0]
+  const bool upper = (threadIdx.x & (G / 2)) != 0;
+  const bool live = m >= kTiny;
+  const float num = upper ? (float)QMAX : m, den = upper ? m : (float)QMAX;
+  const float mine = live ? num / den : 0.0f;
+  const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), kMirror, 0xF, 0xF, false));
+  s = upper ? other : mine;
+  inv = upper ? mine : other;
+}
+
 // Four bytes (the low byte of each value) into one word.
 TACO_DEV uint32_t pack_bytes(int a, int b, int c, int d) {
   const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);   // a.b0, b.b0, 0, 0
@@ -195,7 +213,8 @@ TACO_DEV float int8_sym_stat(const float* a) { return group_max<64 / V>(absmax_v
 template <int V>
 TACO_DEV LaneCodes quant_int8_sym(const float* a, float* pre) {
   float s, inv;
-  block_scales<127>(int8_sym_stat<V>(a), s, inv);
+  if constexpr (64 / V == 4 || 64 / V == 8) block_scales_split<127, 64 / V>(int8_sym_stat<V>(a), s, inv);
+  else block_scales<127>(int8_sym_stat<V>(a), s, inv);
   return int8_sym_encode<V>(a, s, inv, pre);
 }
 
@@ -216,6 +235,23 @@ TACO_DEV LaneCodes asym_encode(const float* a, float lo, float s, float inv, flo
   LaneCodes r;
   r.s = s;
   r.z = clampi(rne_int((-lo) * inv), 0, QMAX);
+  r.q = make_uint4(0, 0, 0, 0);
+  if constexpr (BITS == 8) {
+    // rne(t) + z is an exact integer in float; v_cvt_pk_u8_f32 clamps it to
+    // [0, 255] (it saturates, and rounds to nearest even, which leaves an
+    // integer unchanged) and writes it into its byte of the word
+    const float zf = (float)r.z;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float t = a[i] * inv;
+      if (pre) pre[i] = t;
+      w[i / 4] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(t) + zf, i % 4, w[i / 4]);
+    }
+    r.q = make_uint4(w[0], w[1], w[2], w[3]);
+    r.k = 0;
+    return r;
+  }
   int q[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -223,7 +259,6 @@ TACO_DEV LaneCodes asym_encode(const float* a, float lo, float s, float inv, flo
     if (pre) pre[i] = t;
     q[i] = clampi(rne_int(t) + r.z, 0, QMAX);
   }
-  r.q = make_uint4(0, 0, 0, 0);
   if constexpr (BITS == 4) {
     r.q.x = pack_nibbles(q);
     if constexpr (V == 16) r.q.y = pack_nibbles(q + 8);
@@ -242,7 +277,8 @@ TACO_DEV LaneCodes asym_encode(const float* a, float lo, float s, float inv, flo
 template <int BITS, int V>
 TACO_DEV LaneCodes quant_asym(const float* a, float* pre) {
   float lo, s, inv;
-  block_scales<(1 << BITS) - 1>(asym_stat<V>(a, lo), s, inv);
+  if constexpr (128 / V == 4 || 128 / V == 8) block_scales_split<(1 << BITS) - 1, 128 / V>(asym_stat<V>(a, lo), s, inv);
+  else block_scales<(1 << BITS) - 1>(asym_stat<V>(a, lo), s, inv);
   return asym_encode<BITS, V>(a, lo, s, inv, pre);
 }
 
@@ -669,52 +705,80 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
 // every N <= NMAX. Steps past the last tile load nothing (their offsets lie
 // outside every resource). A launch covers at most kReducePiece elements (the
 // host splits larger tensors), so every byte offset fits 32 bits.
-// Two resources per shard: the codes, and the block metadata -- the scales,
-// followed (asymmetric formats) by the zero points a.zero_rel bytes after the
-// first scale byte, the same distance in every shard.
+// Each shard's resources are rebased to the tile a step reads (scalar
+// arithmetic), so every lane's offsets are the same for every tile and step:
+// the codes, the block scales or exponents, and (asymmetric formats) the zero
+// points, each clipped at the tensor's end.
 template <int FMT, int B>
 struct ShardRsrc {
-  rsrc_t codes, meta;
+  rsrc_t codes, meta, zero;
 };
 
-// n <= kReducePiece, so every size below is under 2^31.
+// Byte offsets of a lane's codes and block metadata inside its tile.
+// FP8 exponents are read as the aligned dword that holds the lane's byte
+// (byte loads let the compiler sink them past the scheduling barrier); a
+// tile's first block index is a multiple of 8, so the rebased dwords stay
+// aligned.
 template <int FMT, int B>
-TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int n) {
-  const bool live = r < a.nshards;
-  const int nb = n / B;
+struct LaneOffs {
+  int code, meta, zero, sh;
+  TACO_DEV explicit LaneOffs(int lane) {
+    const int blk = lane * kLaneElems / B;
+    code = FMT == kINT4A ? lane * (kLaneElems / 2) : lane * kLaneElems;
+    meta = is_fp8(FMT) ? (blk & ~3) : 4 * blk;
+    sh = is_fp8(FMT) ? 8 * (blk & 3) : 0;
+    zero = blk;
+  }
+  // The offsets of the same lane inside the whole tensor, for tile t.
+  TACO_DEV LaneOffs at_tile(int t) const {
+    const unsigned e = (unsigned)t * kWaveElems, blk0 = e / B;
+    LaneOffs r = *this;
+    r.code += (int)(FMT == kINT4A ? e / 2 : e);
+    r.meta += (int)(is_fp8(FMT) ? blk0 : 4 * blk0);
+    r.zero += (int)blk0;
+    return r;
+  }
+};
+
+// n <= kReducePiece, and t is at most one grid stride past the last tile, so
+// every size below is under 2^31. A slot r >= nshards, or a tile at or past
+// the end, gets empty resources (its loads return zeros).
+template <int FMT, int B>
+TACO_DEV ShardRsrc<FMT, B> shard_rsrc(const ReduceArgs& a, int r, int n, int t) {
   constexpr bool ASYM = FMT == kINT4A || FMT == kINT8A;
+  const unsigned e = (unsigned)t * kWaveElems;                             // the tile's first element
+  const unsigned rem = (r < a.nshards && e < (unsigned)n) ? (unsigned)n - e : 0u;
+  const unsigned blk0 = e / B, nbr = rem / B;
+  const uint8_t* scale = static_cast<const uint8_t*>(a.in.scale[r]);
   ShardRsrc<FMT, B> s;
-  s.codes = make_rsrc32(a.in.codes[r], live ? (FMT == kINT4A ? n / 2 : n) : 0);
-  s.meta = make_rsrc32(a.in.scale[r], live ? (is_fp8(FMT) ? (nb + 3) & ~3 : (ASYM ? a.zero_rel + nb : 4 * nb)) : 0);
+  s.codes = make_rsrc32(a.in.codes[r] + (FMT == kINT4A ? e / 2 : e), (int)(FMT == kINT4A ? rem / 2 : rem));
+  if constexpr (is_fp8(FMT)) s.meta = make_rsrc32(scale + blk0, (int)((nbr + 3) & ~3u));
+  else s.meta = make_rsrc32(scale + 4 * blk0, (int)(4 * nbr));
+  s.zero = make_rsrc32(ASYM ? a.in.zero[r] + blk0 : a.in.codes[r], ASYM ? (int)nbr : 0);
   return s;
 }
 
-// One lane's codes and block metadata of one shard. FP8: g is the shard's
-// tensor scale (0 for an empty slot).
+// One lane's codes and block metadata of one shard. FP8 leaves the exponent
+// dword in z and its bit offset in sh: the scale is formed when the lane is
+// added, so nothing here waits for the loads.
 template <int FMT, int B>
-// FP8 leaves the exponent dword in z and its bit offset in sh: the scale is
-// formed when the lane is added (fp8_reduce_scale), so nothing here waits for
-// the loads.
-TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, int e0, int zero_rel) {
+TACO_DEV LaneIn<FMT, B> load_in_buf(const ShardRsrc<FMT, B>& s, const LaneOffs<FMT, B>& o) {
   LaneIn<FMT, B> r;
-  const int blk = e0 / B;
   if constexpr (FMT == kINT4A) {
-    uint2 w = bload64<kNT>(s.codes, e0 / 2, 0);
+    uint2 w = bload64<kNT>(s.codes, o.code, 0);
     r.q = make_uint4(w.x, w.y, 0, 0);
   } else {
-    r.q = bload128<kNT>(s.codes, e0, 0);
+    r.q = bload128<kNT>(s.codes, o.code, 0);
   }
   r.z = 0;
   r.sh = 0;
   r.s = 0.0f;
   if constexpr (is_fp8(FMT)) {
-    // the aligned dword holding the exponent byte (the resource is rounded up
-    // to whole dwords, inside the region's padding)
-    r.z = bload32(s.meta, blk & ~3, 0);
-    r.sh = 8 * (blk & 3);
+    r.z = bload32(s.meta, o.meta, 0);
+    r.sh = o.sh;
   } else {
-    r.s = __uint_as_float(bload32(s.meta, blk * 4, 0));
-    if constexpr (FMT == kINT4A || FMT == kINT8A) r.z = bload8(s.meta, blk, zero_rel);
+    r.s = __uint_as_float(bload32(s.meta, o.meta, 0));
+    if constexpr (FMT == kINT4A || FMT == kINT8A) r.z = bload8(s.zero, o.zero, 0);
   }
   return r;
 }
@@ -727,17 +791,28 @@ struct ReduceGroup {
   static constexpr int NG = NMAX / GRP;                 // steps per tile (>= 2)
   LaneIn<FIN, BIN> in[GRP];
 
-  // Issue the loads of shard group `grp` of the tile at element e0 (FP8: the
-  // scale is formed when the step is added).
-  TACO_DEV void load(const ReduceArgs& a, int grp, int e0, int n) {
-    // With more than two groups the compiler would hoist every shard's
-    // resources out of the loop and spill them; an opaque group index keeps
-    // each step building only its own group's.
-    if constexpr (NG > 2) asm volatile("" : "+s"(grp));
+  // Issue the loads of shard group `grp` of tile t (FP8: the scale is formed
+  // when the step is added).
+  // With more than two groups the compiler would hoist every shard's
+  // resources out of the loop and spill them; an opaque group index keeps
+  // each step building only its own group's, rebased to the tile, so the
+  // lane offsets need no per-step arithmetic (the instruction-bound
+  // asymmetric inputs gain 5 %). With two groups the resources of all NMAX
+  // shards cover the whole tensor and stay in scalar registers for the
+  // whole loop, and a step adds the tile's offset to the lane's (two or three
+  // adds): the loads then issue back to back, which the memory-bound FP8
+  // reduce needs (rebuilding its resources per step measured 4-7 % slower).
+  TACO_DEV void load(const ReduceArgs& a, int grp, int t, int n, const LaneOffs<FIN, BIN>& o) {
+    if constexpr (NG > 2) {
+      asm volatile("" : "+s"(grp));
 #pragma unroll
-    for (int u = 0; u < GRP; ++u) {
-      const int r = grp * GRP + u;
-      in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, r, n), e0, a.zero_rel);
+      for (int u = 0; u < GRP; ++u)
+        in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, grp * GRP + u, n, t), o);
+    } else {
+      const LaneOffs<FIN, BIN> ot = o.at_tile(t);
+#pragma unroll
+      for (int u = 0; u < GRP; ++u)
+        in[u] = load_in_buf<FIN, BIN>(shard_rsrc<FIN, BIN>(a, grp * GRP + u, n, 0), ot);
     }
   }
 
@@ -812,21 +887,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
     }
   }
   float glane = 0.0f;
+  // whole-tensor output resources (kept in scalar registers for the whole
+  // loop; out-of-range lanes are dropped)
   const int nb_out = n / BOUT;
   const rsrc_t r_sum = make_rsrc32(a.sum, a.sum ? 4 * n : 0);
   const rsrc_t r_qc = make_rsrc32(a.rq_codes, rq ? n : 0);
   const rsrc_t r_qs = make_rsrc32(a.rq_scale, rq ? (is_fp8(FOUT) ? nb_out : 4 * nb_out) : 0);
   const rsrc_t r_qz = make_rsrc32(a.rq_zero, rq && FOUT == kINT8A ? nb_out : 0);
 
-  // the finished sum of a tile: store it and/or re-quantize it
+  // the finished sum of tile t: store it and/or re-quantize it
   auto finish = [&](int t, float* acc) {
-    const int e0 = t * kWaveElems + lane * kLaneElems;
+    const unsigned e = (unsigned)t * kWaveElems;   // the tile's first element
     if (a.sum != nullptr) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         bstore128(make_uint4(__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
                              __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3])),
-                  r_sum, e0 * 4 + 16 * q, 0);
+                  r_sum, (int)(4 * e) + lane * (4 * kLaneElems) + 16 * q, 0);
     }
     if (rq) {
       // FP8: g' = g_0 + ... + g_{N-1} in shard order, clamped
@@ -842,8 +919,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
       // lanes beyond the tensor quantize zeros; their stores fall outside the
       // resources and are dropped
       LaneCodes q = quant_lane<FOUT, BOUT>(acc, inv_g, nullptr);
-      const int blk = e0 / BOUT;
-      bstore128(q.q, r_qc, e0, 0);
+      const int blk = (int)(e / BOUT) + lane * kLaneElems / BOUT;
+      bstore128(q.q, r_qc, (int)e + lane * kLaneElems, 0);
       if constexpr (is_fp8(FOUT)) {
         bstore8((uint32_t)q.k, r_qs, blk, 0);
       } else {
@@ -866,7 +943,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   RG buf[2];
-  buf[0].load(a, 0, t * kWaveElems + lane * kLaneElems, n);
+  const LaneOffs<FIN, BIN> offs(lane);
+  buf[0].load(a, 0, t, n, offs);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (is_fp8(FIN)) glane = *gp;   // lanes >= nshards: shard 0's g, read by no live step
   for (; t < ntiles; t += stride) {
@@ -874,7 +952,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
     for (int k = 0; k < NG; ++k) {
       const int tn = k + 1 < NG ? t : t + stride;   // tile and group of step k + 1
       const int gn = (k + 1) % NG;
-      buf[(k + 1) & 1].load(a, gn, tn * kWaveElems + lane * kLaneElems, n);
+      buf[(k + 1) & 1].load(a, gn, tn, n, offs);
       __builtin_amdgcn_sched_barrier(0);
       buf[k & 1].add_to(acc, k, glane);
     }
@@ -1098,18 +1176,10 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
     p.n = (a.n - e < kReducePiece) ? a.n - e : kReducePiece;
     p.write_g = (e == 0);
     const int64_t bi = e / a.bin, bo = e / a.bout;
-    p.zero_rel = 0;
     for (int r = 0; r < a.nshards; ++r) {
       p.in.codes[r] = a.in.codes[r] + code_bytes(a.fin, e);
       p.in.scale[r] = static_cast<const uint8_t*>(a.in.scale[r]) + scale_bytes(a.fin, bi);
       p.in.zero[r] = a.in.zero[r] + bi;
-      if (a.fin == kINT4A || a.fin == kINT8A) {
-        // the zero points follow the scales at one distance in every shard
-        const int64_t rel = p.in.zero[r] - static_cast<const uint8_t*>(p.in.scale[r]);
-        if (rel < 4 * (p.n / a.bin) || rel + p.n / a.bin > 0x7FFFFFF0 || (r > 0 && rel != p.zero_rel))
-          return hipErrorInvalidValue;
-        p.zero_rel = (int)rel;
-      }
     }
     if (a.sum) p.sum = a.sum + e;
     if (a.rq_codes) {

@@ -98,7 +98,6 @@ struct ReduceArgs {
   uint8_t* rq_zero;
   float* rq_g_hdr;
   bool write_g;         // this launch writes the requantized tensor scale
-  int zero_rel;         // asymmetric input: bytes from a shard's first scale to its first zero point
 };
 
 struct HopArgs {
