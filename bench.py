@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
                          "next activation, on a second stream, and report the overlap")
+    ap.add_argument("--rank-share", action="store_true",
+                    help="also time the decompress-reduce at one rank's share: (rows / N) x cols from N sources "
+                         "(kept out of the default run so the profiled runs hold only full-size launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (known bytes) for counter calibration")
     ap.add_argument("--summarize", nargs="+", metavar="PATH",
@@ -87,6 +90,61 @@ def algorithmic_bytes(w):
         out = n + 5 * (n // 128)
     reduce = w.shards * shard + out
     return compress, reduce
+
+
+def measure_rank_share(w, xs, stream, K):
+    """The decompress-reduce at one rank's share of the step: with N ranks a rank
+    reduces the (rows / N) x cols row chunk it owns, from N sources (one
+    compressed chunk per rank), and re-quantizes it for the gather stage. The
+    N source chunks are compressed here from row chunks of the workload's
+    shards; enough independent sets rotate that they exceed twice the
+    Infinity Cache, so the chunks come from HBM as the full-size kernels' do."""
+    import torch
+    import quantized_compression_tensor_amd as T
+    dev = "cuda"
+    rows = w.rows // w.shards
+    ws_ = dataclasses.replace(w, rows=rows)
+    c_in = T.codec(w.in_format, w.in_block, int(w.hadamard))
+    c_out = T.codec(w.out_format, w.out_block, int(w.hadamard)) if w.out_format else None
+    fp8 = w.in_format in T.FP8_FORMATS
+    per_set = w.shards * T.taco_compressed_bytes(c_in, rows, w.cols)
+    nsets = max(2, -(-2 * MALL_BYTES // per_set))
+    sh = stream.cuda_stream
+    sets, outs = [], []
+    with torch.cuda.stream(stream):
+        for j in range(nsets):
+            bufs = []
+            for r in range(w.shards):
+                x = xs[j % len(xs)][r].reshape(-1)[:rows * w.cols]
+                b = T.empty_compressed(c_in, rows, w.cols, dev)
+                wsb = torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) if fp8 else None
+                T.taco_compress(c_in, x, rows, w.cols, T.TACO_SCALE_AUTO if fp8 else 1.0, b, workspace=wsb, stream=sh)
+                bufs.append(b)
+            sets.append(bufs)
+            outs.append(T.empty_compressed(c_out, rows, w.cols, dev) if c_out is not None
+                        else torch.empty(rows * w.cols, dtype=torch.float32, device=dev))
+
+        def red(j):
+            if c_out is not None:
+                T.taco_decompress_reduce(c_in, sets[j], rows, w.cols, None, c_out, outs[j], stream=sh)
+            else:
+                T.taco_decompress_reduce(c_in, sets[j], rows, w.cols, outs[j], stream=sh)
+
+        for j in range(nsets):
+            red(j)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            red(i % nsets)
+        b.record(stream)
+        torch.cuda.synchronize()
+    t = a.elapsed_time(b) / K
+    _, b_red = algorithmic_bytes(ws_)
+    gbs = b_red / (t * 1e-3) / 1e9
+    return {"rows": rows, "cols": w.cols, "sources": w.shards, "input_sets": nsets, "reduce_ms": round(t, 5),
+            "reduce_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": b_red}
 
 
 def measure_ring(w, xs, stream, K):
@@ -550,6 +608,8 @@ def main():
         ach, bytes_launch, kname = red_gbs, b_red, "reduce"
     traffic = read_traffic(kname, w.name, src_hash)
 
+    rank_share = measure_rank_share(w, xs, stream, K=max(20, K // 2)) if args.rank_share else None
+
     ring = None
     if args.ring:
         if w.in_format in T.FP8_FORMATS:
@@ -615,6 +675,7 @@ def main():
             "host_ms_per_step": round(host * 1e3 / K, 5),
             "event_ms_per_step": round(gpu_ms_step, 5),
         },
+        **({"rank_share": rank_share} if rank_share else {}),
         "quality": q,
         "cpu_baseline": cpu,
         **({"overlap": overlap} if overlap else {}),
