@@ -143,6 +143,27 @@ size_t taco_workspace_bytes(taco_codec c, int64_t rows, int64_t cols);
 int taco_compress(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* taco_compress for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and outputs, with the FP8 tensor-scale workspace taken
+ * from a TACO_WORKSPACE_BYTES (32 KiB) array that the library holds in each
+ * GPU's memory until the process ends, instead of a workspace argument. The
+ * call allocates nothing and calls no allocating routine. The array is the
+ * same size for every tensor, so no size is too large for it (the 2^35
+ * element limit of every entry point applies).
+ *   - Every call on one GPU shares that GPU's array: TACO_SCALE_DELAYED takes
+ *     the abs-max recorded by the previous FP8 call on that GPU (any stream,
+ *     any caller), and every FP8 call records its own. Calls that overlap on
+ *     one GPU (concurrent streams or host threads) race on it: order them.
+ *   - The first call on a device clears the array with a fill kernel on
+ *     `stream`, ordered before its own work; a graph that captured that first
+ *     call clears it again on every replay.
+ *   - Non-FP8 formats use no workspace; this call then equals taco_compress.
+ * Errors as taco_compress; TACO_ERR_HIP also when the array's device address
+ * cannot be obtained. */
+int taco_compress_noalloc(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale,
+                          void* out, hipStream_t stream);
+
 /* taco_compress that also writes, for every element, the float32 value handed
  * to the final rounding step (FP8: the scaled value encoded to E4M3; INT:
  * value * (1/scale) before rounding) to `prequant` (device, n floats). */

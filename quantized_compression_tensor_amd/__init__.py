@@ -38,7 +38,7 @@ TACO_WORKSPACE_BYTES = 32768
 EXPORTS = (
     "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
     "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
-    "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string",
+    "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string", "taco_compress_noalloc",
 )
 
 
@@ -85,6 +85,7 @@ def _load():
         "taco_compressed_bytes": (I64, [C, I64, I64]),
         "taco_workspace_bytes": (SZ, [C, I64, I64]),
         "taco_compress": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P]),
+        "taco_compress_noalloc": (ctypes.c_int, [C, P, I64, I64, F32, P, P]),
         "taco_compress_debug": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P, P]),
         "taco_decompress_reduce": (ctypes.c_int, [C, ctypes.POINTER(P), I32, I64, I64, P, C, P, P]),
         "taco_ring_hop": (ctypes.c_int, [C, P, P, I64, I64, P, C, P, P]),
@@ -160,6 +161,11 @@ def taco_compress(c, x_bf16, rows, cols, tensor_scale, out, workspace=None, ws_b
     wsb = ws_bytes if ws_bytes is not None else (TACO_WORKSPACE_BYTES if workspace is not None else 0)
     return _check(_lib.taco_compress(c, _ptr(x_bf16), rows, cols, float(tensor_scale), _ptr(out),
                                      _ptr(workspace), wsb, _stream(stream)), "taco_compress")
+
+
+def taco_compress_noalloc(c, x_bf16, rows, cols, tensor_scale, out, stream=None):
+    return _check(_lib.taco_compress_noalloc(c, _ptr(x_bf16), rows, cols, float(tensor_scale), _ptr(out),
+                                             _stream(stream)), "taco_compress_noalloc")
 
 
 def taco_compress_debug(c, x_bf16, rows, cols, tensor_scale, out, prequant, workspace=None, ws_bytes=None,

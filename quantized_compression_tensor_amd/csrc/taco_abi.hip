@@ -1,7 +1,11 @@
-// The C ABI: validation, buffer layout and kernel dispatch. Everything here is
-// host code; all checks run before any work is enqueued.
+// The C ABI: validation, buffer layout and kernel dispatch; all checks run
+// before any work is enqueued. Apart from the allocation-free compress's
+// scratch array (and the fill kernel that clears it once per device),
+// everything here is host code.
 #include <math.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "taco.h"
 #include "taco_internal.h"
@@ -70,7 +74,9 @@ void layout_of(const taco_codec& c, int64_t n, taco_layout_t* L) {
 int log2_block(int b) { return b == 16 ? 4 : b == 32 ? 5 : b == 64 ? 6 : 7; }
 
 // FP8 tensor-scale mode: 0 = given g, 1 = auto (pre-pass), 2 = delayed.
-int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, int* mode) {
+// internal_ws: the workspace is the library's own scratch array (no
+// workspace argument to check).
+int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, bool internal_ws, int* mode) {
   *mode = 0;
   if (!is_fp8_format(c.format)) return TACO_OK;
   if (isnan(ts) || isinf(ts)) return TACO_ERR_INVALID_ARG;
@@ -78,9 +84,9 @@ int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, int* mo
     if (ts < kGMin || ts > kGMax) return TACO_ERR_INVALID_ARG;
   } else {
     *mode = (ts == 0.0f) ? 1 : 2;
-    if (ws == nullptr || ws_bytes < TACO_WORKSPACE_BYTES) return TACO_ERR_WORKSPACE;
+    if (!internal_ws && (ws == nullptr || ws_bytes < TACO_WORKSPACE_BYTES)) return TACO_ERR_WORKSPACE;
   }
-  if (ws != nullptr && (ws_bytes < TACO_WORKSPACE_BYTES || !aligned16(ws))) return TACO_ERR_WORKSPACE;
+  if (!internal_ws && ws != nullptr && (ws_bytes < TACO_WORKSPACE_BYTES || !aligned16(ws))) return TACO_ERR_WORKSPACE;
   return TACO_OK;
 }
 
@@ -102,12 +108,16 @@ Regions regions_of(void* buf, const taco_layout_t& L) {
   return Regions{b + L.codes_off, b + L.scale_off, b + L.aux_off, reinterpret_cast<float*>(b + L.tensor_off)};
 }
 
+int scratch_workspace(hipStream_t stream, void** ws);
+
+// internal_ws: the FP8 workspace is the device's scratch array (fetched, and
+// cleared on its first use, only after every argument has been checked).
 int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int64_t cols, float ts, void* out,
-                    void* ws, size_t ws_bytes, float* dbg, hipStream_t stream) {
+                    void* ws, size_t ws_bytes, float* dbg, hipStream_t stream, bool internal_ws = false) {
   int st = check_shape(c, rows, cols);
   if (st != TACO_OK) return st;
   int mode = 0;
-  st = scale_mode(c, ts, ws, ws_bytes, &mode);
+  st = scale_mode(c, ts, ws, ws_bytes, internal_ws, &mode);
   if (st != TACO_OK) return st;
   const int64_t n = rows * cols;
   if (n == 0) return TACO_OK;
@@ -119,6 +129,10 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   if (overlaps(x, in_bytes, out, L.total_bytes)) return TACO_ERR_INVALID_ARG;
   if (dbg && (overlaps(dbg, 4 * n, x, in_bytes) || overlaps(dbg, 4 * n, out, L.total_bytes)))
     return TACO_ERR_INVALID_ARG;
+  if (internal_ws && is_fp8_format(c.format)) {
+    st = scratch_workspace(stream, &ws);
+    if (st != TACO_OK) return st;
+  }
   Regions R = regions_of(out, L);
   if (is_fp8_format(c.format) && c.hadamard == 1 && !f32_in) {
     FP8HadArgs a;
@@ -136,6 +150,43 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   a.ws = is_fp8_format(c.format) ? ws : nullptr; a.dbg = dbg;
   clear_stale_error();
   return hip_status(launch_quantize(a, stream));
+}
+
+// ---------------------------------------------------------------- scratch --
+// The FP8 tensor-scale workspace of taco_compress_noalloc: one array per GPU,
+// in the library's own device memory, so that call allocates nothing. Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, and is kept per device.
+constexpr int kScratchWords = TACO_WORKSPACE_BYTES / 4;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+__global__ __launch_bounds__(256) void k_clear_words(uint32_t* p, int nwords) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < nwords) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch array. The first call on a device looks up its
+// address and clears it on `stream` (a fill kernel, ordered before the
+// compress that follows on the same stream); later calls reuse the address.
+int scratch_workspace(hipStream_t stream, void** ws) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TACO_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return TACO_ERR_HIP;
+    clear_stale_error();
+    hipLaunchKernelGGL(k_clear_words, dim3((kScratchWords + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ptr), kScratchWords);
+    if (hipGetLastError() != hipSuccess) return TACO_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *ws = g_scratch_ptr[dev];
+  return TACO_OK;
 }
 
 }  // namespace
@@ -194,6 +245,11 @@ size_t taco_workspace_bytes(taco_codec c, int64_t rows, int64_t cols) {
 int taco_compress(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,
                   void* workspace, size_t ws_bytes, hipStream_t stream) {
   return quantize_common(c, x_bf16, false, rows, cols, tensor_scale, out, workspace, ws_bytes, nullptr, stream);
+}
+
+int taco_compress_noalloc(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale,
+                          void* out, hipStream_t stream) {
+  return quantize_common(c, x_bf16, false, rows, cols, tensor_scale, out, nullptr, 0, nullptr, stream, true);
 }
 
 int taco_compress_debug(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale, void* out,

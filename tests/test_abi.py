@@ -116,6 +116,22 @@ def test_compress_validation():
     assert _st(T.taco_compress_debug, FP8, A, 2, 128, 1.0, B_, None) == T.TACO_ERR_INVALID_ARG
 
 
+def test_noalloc_compress_validation():
+    """The allocation-free compress checks its arguments as taco_compress does,
+    before it looks up (or clears) its scratch array; it takes no workspace."""
+    comp = T.taco_compress_noalloc
+    assert _st(comp, FP8, None, 2, 128, 0.0, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, -1.0, None) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A + 2, 2, 128, 0.0, B_) == T.TACO_ERR_ALIGN
+    assert _st(comp, FP8, A, 2, 100, 0.0, B_) == T.TACO_ERR_SHAPE
+    assert _st(comp, FP8, A, 1 << 22, 1 << 14, 0.0, B_) == T.TACO_ERR_INVALID_ARG   # 2^36 elements: too large
+    assert _st(comp, FP8, A, 2, 128, float("inf"), B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 2.0 ** 61, B_) == T.TACO_ERR_INVALID_ARG
+    assert _st(comp, FP8, A, 2, 128, 0.0, A) == T.TACO_ERR_INVALID_ARG          # output overlaps input
+    assert _st(comp, E5, A, 0, 128, -1.0, B_) == 0                             # empty: nothing to do
+    assert _st(comp, I4A, A, 2, 96, 1.0, B_) == T.TACO_ERR_SHAPE
+
+
 def test_reduce_validation():
     red = T.taco_decompress_reduce
     shards = [A, A + (1 << 16)]
