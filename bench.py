@@ -5,12 +5,25 @@ One step = every rank's compress of its shard (N bf16 shards already resident
 in HBM, one compress launch each) followed by the decompress-reduce of the N
 compressed shards with re-quantization for the gather stage -- all of the hot
 path. Shards rotate over several input sets so that the working set exceeds
-the 256 MB Infinity Cache. Kernels are launched eagerly on one stream; the
-timed region has one pair of HIP events per step. Each kernel's average launch
-duration (for the roofline) comes from the same launches repeated right after,
-each between its own pair of events on the launch stream. --launch graph
-replays the step from HIP graphs instead (slower here: the runtime leaves gaps
-between graph launches).
+the 256 MB Infinity Cache. Kernels are launched eagerly on one stream.
+
+The headline workload is qwen-tp (8 shards of 32768 x 5120 bf16, FP8
+dual-scale with the 128-point Hadamard transform, re-quantized to FP8), the
+largest configuration that fits one GPU; the other 8-shard workloads (equarx,
+flashcomm) are timed in the same run and reported under "workloads".
+
+Per workload:
+  * steps for 0.5 s of wall time (the GPU's clocks rise from idle), then the
+    W warm-up steps;
+  * timed region: K steps between one pair of HIP events, bracketed by
+    synchronizations (no event inside it) -> value, ms_per_step;
+  * K more steps with an event at every step boundary -> median, p10, p90;
+  * K more steps with events between the compress phase (N launches) and the
+    reduce -> each kernel's average launch duration in step context (the
+    roofline's denominator);
+  * the quality check: the compress and the reduce+requantize round trips on
+    a seeded sample of row chunks, GPU against the oracle at the same tensor
+    scale (the oracle computes it from the whole tensor itself).
 
 value = N * rows * cols * 2 bytes of bf16 input / step time (GB/s).
 
@@ -22,6 +35,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -31,14 +45,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+PREWARM_S = 0.5
+PEAK_CLOCK_GHZ = 2.4
+HEADLINE = "qwen-tp"
+EXTRA = "equarx,flashcomm"
+FORMAT_NAMES = ["", "FP8 dual-scale", "INT8 sym", "INT4 asym", "INT8 asym", "FP8 E5M2 dual-scale"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt-tp")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--extra", default=EXTRA,
+                    help="comma-separated workloads timed after the headline one in the same run "
+                         "(reported under 'workloads'); 'none' for the headline alone")
     ap.add_argument("--scale-mode", choices=["delayed", "auto", "given"], default="delayed",
                     help="FP8 tensor scale: delayed (abs-max of the previous step, one pass), "
                          "auto (abs-max pre-pass of this tensor) or given (a fixed g, no workspace)")
@@ -46,11 +68,14 @@ def parse():
     ap.add_argument("--fp8-codes", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 workloads: the code format of the dual-scale codec (E5M2 is the variant "
                          "format 5)")
+    ap.add_argument("--prewarm", type=float, default=PREWARM_S,
+                    help="seconds of steps before the warm-up steps (0 for profiler counter passes)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-quality", action="store_true", help="skip the GPU-vs-oracle quality check")
     ap.add_argument("--ring", action="store_true",
                     help="INT workloads: also time one quantized ring reduce-scatter hop (taco_ring_hop) at "
-                         "full size and run the whole full-loop ring over the shards for its MSE")
+                         "full size and run the full-loop and semi-loop rings over the shards for their MSE")
     ap.add_argument("--overlap", action="store_true",
                     help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
                          "next activation, on a second stream, and report the overlap")
@@ -63,6 +88,9 @@ def parse():
                     help="FETCH_DIR WRITE_DIR TRACE_DIR [TRACE_LOG]: turn rocprofv3 FETCH_SIZE / WRITE_SIZE / "
                          "kernel-trace output (and the bench line printed under the trace) into the "
                          "profiles/ summaries and exit")
+    ap.add_argument("--summarize-issue", metavar="DIR",
+                    help="turn a rocprofv3 --pmc run of instruction and busy counters (with --kernel-trace) into "
+                         "profiles/issue_<kernel>_<workload>.txt and exit")
     ap.add_argument("--command", default="", help="with --summarize: the profiled command, recorded")
     return ap.parse_args()
 
@@ -90,6 +118,621 @@ def algorithmic_bytes(w):
         out = n + 5 * (n // 128)
     reduce = w.shards * shard + out
     return compress, reduce
+
+
+def decode_bytes(w):
+    """Bytes the consumer-side decode of the gather-stage output to bf16 moves."""
+    n = w.n
+    if w.out_format in (1, 5):
+        src = n + n // w.out_block + 16
+    elif w.out_format == 2:
+        src = n + 4 * (n // 64)
+    else:
+        src = n + 5 * (n // 128)
+    return src + 2 * n
+
+
+def kernel_patterns(w):
+    """Name prefixes (as the profiler prints them) of the compress and reduce
+    kernels this workload launches."""
+    if w.in_format in (1, 5) and w.hadamard:
+        comp = f"k_fp8_had_compress<{7 if w.in_block == 128 else w.in_block.bit_length() - 1}, "
+    else:
+        comp = f"k_quantize<{w.in_format}, {w.in_block}, false, false>"
+    nmax = 2 if w.shards <= 2 else 4 if w.shards <= 4 else 8 if w.shards <= 8 else 16
+    fout = w.out_format if w.out_format else w.in_format
+    bout = w.out_block if w.out_format else w.in_block
+    red = f"k_reduce<{w.in_format}, {w.in_block}, {fout}, {bout}, {nmax}>"
+    return {"compress": comp, "reduce": red}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_compression_tensor_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, workload, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+COPY_BYTES = 256 << 20
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize(fetch_dir, write_dir, trace_dir, names, command, trace_log=None):
+    """Per-launch HBM bytes of each workload's compress and reduce kernels from
+    two counter passes, scaled by what the same counters read for a plain copy
+    of COPY_BYTES (read and write), plus the kernel-trace statistics and, when
+    the profiled run's output is given, the bench's own event timing in that
+    same run; written to profiles/<kernel>_<workload>_counters.txt and
+    profiles/kernels_<workload>_trace.txt."""
+    import numpy as np
+    import workloads as W
+    src_hash = kernel_source_hash()
+    bench_ms = {}
+    if trace_log:
+        lines = [l for l in open(trace_log) if l.startswith("{")]
+        if lines:
+            line = json.loads(lines[-1])
+            per = {line["config"]["name"]: line["kernels"]}
+            for k, v in (line.get("workloads") or {}).items():
+                per[k] = v["kernels"]
+            bench_ms = {k: {"compress": v.get("compress_ms"), "reduce": v.get("reduce_ms")} for k, v in per.items()}
+    per = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for row in _csv_rows(d, "counter_collection.csv"):
+            if row.get("Counter_Name") != cname:
+                continue
+            per.setdefault((cname, row.get("Kernel_Name", "")), []).append(float(row["Counter_Value"]))
+    # the calibration copies are the three largest copy dispatches of the run
+    copy_f = sorted((v for (c, k), vs in per.items() if c == "FETCH_SIZE" and "copy" in k.lower() for v in vs),
+                    reverse=True)[:3]
+    copy_w = sorted((v for (c, k), vs in per.items() if c == "WRITE_SIZE" and "copy" in k.lower() for v in vs),
+                    reverse=True)[:3]
+    f_fetch = COPY_BYTES / (np.median(copy_f) * 1024) if copy_f else None
+    f_write = COPY_BYTES / (np.median(copy_w) * 1024) if copy_w else None
+    trace = {row["Name"]: row for row in _csv_rows(trace_dir, "kernel_stats.csv")}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    written = []
+    for wname in names:
+        w = W.WORKLOADS[wname]
+        pats = kernel_patterns(w)
+        for key, pat in pats.items():
+            fk = [(k, vs) for (c, k), vs in per.items() if c == "FETCH_SIZE" and pat in k]
+            wk = [(k, vs) for (c, k), vs in per.items() if c == "WRITE_SIZE" and pat in k]
+            if not fk or not wk:
+                continue
+            fk.sort(key=lambda kv: -len(kv[1]))
+            wk.sort(key=lambda kv: -len(kv[1]))
+            kname = fk[0][0]
+            fetch_kib = float(np.median(fk[0][1]))
+            write_kib = float(np.median(wk[0][1]))
+            hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write if f_fetch and f_write else None
+            tr = trace.get(kname)
+            path = os.path.join(ROOT, "profiles", f"{key}_{wname}_counters.txt")
+            with open(path, "w") as fh:
+                fh.write(f"# rocprofv3 hardware counters for {kname}\n")
+                fh.write(f"# workload: {wname}\n# command: {command}\n")
+                fh.write("# FETCH_SIZE and WRITE_SIZE come from separate --pmc passes (KiB per dispatch,\n"
+                         "# median over dispatches); each is scaled by COPY_BYTES / counter of a plain\n"
+                         "# device-to-device copy of COPY_BYTES profiled in the same pass.\n")
+                fh.write(f"kernel: {kname}\n")
+                fh.write(f"source_hash: {src_hash}\n")
+                fh.write(f"fetch_kib_per_dispatch: {fetch_kib:.1f}\n")
+                fh.write(f"write_kib_per_dispatch: {write_kib:.1f}\n")
+                fh.write(f"copy_bytes: {COPY_BYTES}\n")
+                fh.write(f"copy_fetch_factor: {f_fetch}\n")
+                fh.write(f"copy_write_factor: {f_write}\n")
+                fh.write(f"hbm_bytes_per_launch: {hbm}\n")
+                fh.write(f"algorithmic_bytes_per_launch: {algorithmic_bytes(w)[0 if key == 'compress' else 1]}\n")
+                if tr is not None:
+                    fh.write(f"trace_calls: {tr.get('Calls')}\n")
+                    fh.write(f"trace_average_ns: {tr.get('AverageNs')}\n")
+                    fh.write(f"trace_min_ns: {tr.get('MinNs')}\n")
+                    fh.write(f"trace_max_ns: {tr.get('MaxNs')}\n")
+                b = bench_ms.get(wname, {}).get(key)
+                if b is not None:
+                    fh.write("# the bench's own HIP-event average in the profiled run (launches in step\n"
+                             "# context, including the gap before each launch, which the profiler widens)\n")
+                    fh.write(f"bench_event_average_ns_under_profiler: {b * 1e6:.0f}\n")
+            written.append(path)
+        if trace:
+            # this workload's kernels: its compress, reduce and the decode of its
+            # gather-stage format; the device copies are the run's shared reference
+            dec = {1: "k_fp8_had_decode", 5: "k_fp8_had_decode"}.get(w.out_format, f"k_dequantize<{w.out_format}, ")
+            mine = [n for n in trace if any(p in n for p in pats.values()) or
+                    (dec in n and (w.out_format not in (1, 5) or "<7, " + ("true" if w.out_format == 5 else "false") in n))]
+            if w.in_format in (1, 5) and w.hadamard:
+                mine += [n for n in trace if "k_fp8_had_amax" in n]
+            path = os.path.join(ROOT, "profiles", f"kernels_{wname}_trace.txt")
+            with open(path, "w") as fh:
+                fh.write(f"# rocprofv3 kernel-trace statistics: the kernels of workload {wname}\n"
+                         f"# command: {command}\n")
+                fh.write("# (kernel durations exclude dispatch gaps; the bench's phase events include them)\n")
+                fh.write(f"source_hash: {src_hash}\n")
+                fh.write(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
+                for name in sorted(set(mine), key=lambda n: -float(trace[n]["TotalDurationNs"])):
+                    row = trace[name]
+                    fh.write(f"{int(row['Calls']):>6} {float(row['AverageNs']) / 1e3:>9.2f} "
+                             f"{float(row['MinNs']) / 1e3:>9.2f} {float(row['MaxNs']) / 1e3:>9.2f}  {name[:160]}\n")
+            written.append(path)
+    print("\n".join(written))
+
+
+ISSUE_COUNTERS = ("SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "SQ_WAVES",
+                  "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+
+
+def summarize_issue(d, names, command):
+    """Instruction-issue profile of each workload's compress and reduce: per
+    dispatch medians of the SQ / GRBM counters (one --pmc pass with the kernel
+    trace, which gives each dispatch's duration), and what follows from them:
+    VALU instructions per wave, VALU busy (quad-cycles of VALU work per CU
+    over the active cycles of one XCD) and the VALU floor (the VALU
+    instructions at one wave64 instruction per 4 cycles on each of the 1024
+    SIMDs at the 2.4 GHz peak clock)."""
+    import numpy as np
+    import workloads as W
+    src_hash = kernel_source_hash()
+    ctr = {}
+    for row in _csv_rows(d, "counter_collection.csv"):
+        key = (row.get("Kernel_Name", ""), row.get("Dispatch_Id") or row.get("Correlation_Id"))
+        ctr.setdefault(key, {})[row["Counter_Name"]] = ctr.get(key, {}).get(row["Counter_Name"], 0.0) + \
+            float(row["Counter_Value"])
+    dur = {}
+    for row in _csv_rows(d, "kernel_trace.csv"):
+        key = (row.get("Kernel_Name", ""), row.get("Dispatch_Id") or row.get("Correlation_Id"))
+        dur[key] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    written = []
+    for wname in names:
+        w = W.WORKLOADS[wname]
+        for key, pat in kernel_patterns(w).items():
+            rows = [(k, v) for k, v in ctr.items() if pat in k[0]]
+            if not rows:
+                continue
+            kname = rows[0][0][0]
+            med = {c: float(np.median([v.get(c, np.nan) for _, v in rows])) for c in ISSUE_COUNTERS}
+            ds = [dur[k] for k, _ in rows if k in dur]
+            t_ns = float(np.median(ds)) if ds else None
+            xcds, cus, simds = 8, 256, 1024
+            gui = med["GRBM_GUI_ACTIVE"]
+            path = os.path.join(ROOT, "profiles", f"issue_{key}_{wname}.txt")
+            with open(path, "w") as fh:
+                fh.write(f"# rocprofv3 instruction and busy counters for {kname}\n")
+                fh.write(f"# workload: {wname}\n# command: {command}\n")
+                fh.write("# per-dispatch medians over the run's dispatches of this kernel; SQ counters are summed\n"
+                         "# over shader engines and XCDs, GRBM_GUI_ACTIVE over the 8 XCDs\n")
+                fh.write(f"kernel: {kname}\nsource_hash: {src_hash}\ndispatches: {len(rows)}\n")
+                for c in ISSUE_COUNTERS:
+                    fh.write(f"{c}: {med[c]:.0f}\n")
+                floor_ns = med["SQ_INSTS_VALU"] * 4 / simds / PEAK_CLOCK_GHZ
+                fh.write(f"valu_floor_ns (SQ_INSTS_VALU * 4 cycles / 1024 SIMDs / 2.4 GHz): {floor_ns:.0f}\n")
+                if t_ns:
+                    fh.write(f"duration_ns_median: {t_ns:.0f}\n")
+                    fh.write(f"duration_over_valu_floor: {t_ns / floor_ns:.3f}\n")
+                fh.write(f"valu_insts_per_wave: {med['SQ_INSTS_VALU'] / max(med['SQ_WAVES'], 1):.1f}\n")
+                fh.write(f"salu_insts_per_wave: {med['SQ_INSTS_SALU'] / max(med['SQ_WAVES'], 1):.1f}\n")
+                fh.write(f"vmem_insts_per_wave: {med['SQ_INSTS_VMEM'] / max(med['SQ_WAVES'], 1):.1f}\n")
+                fh.write(f"valu_busy (100 * SQ_ACTIVE_INST_VALU / 256 CUs / (GRBM_GUI_ACTIVE / 8)): "
+                         f"{100 * med['SQ_ACTIVE_INST_VALU'] / cus / (gui / xcds):.1f}\n")
+            written.append(path)
+    print("\n".join(written))
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, as written, on a bounded sample of the same workload: row
+    chunks of every shard, compressed and reduced (+ requantized), spread over
+    a thread pool (NumPy releases the GIL inside its loops)."""
+    import oracle
+    from oracle import codecs as cd
+    import workloads as W
+
+    cin = cd.Codec(w.in_format, w.in_block, w.hadamard)
+    cout = cd.Codec(w.out_format, w.out_block, w.hadamard) if w.out_format else None
+    nchunks = (w.rows + W.ROW_CHUNK - 1) // W.ROW_CHUNK
+    host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, host_cores))
+
+    inputs = {}
+
+    def one(chunk):
+        shards = [oracle.compress(cin, inputs[(chunk, r)]) for r in range(w.shards)]
+        oracle.decompress_reduce(shards, cout)
+        return chunk
+
+    # calibrate on one chunk, then size the sample to the time budget
+    for r in range(w.shards):
+        inputs[(0, r)] = W.make_shard(w, r, chunks=[0])
+    t = time.perf_counter()
+    one(0)
+    per_chunk = time.perf_counter() - t
+    want = max(1, int(seconds * threads / max(per_chunk, 1e-6)))
+    chunks = list(range(min(nchunks, max(threads, want))))
+    for c in chunks:
+        for r in range(w.shards):
+            if (c, r) not in inputs:
+                inputs[(c, r)] = W.make_shard(w, r, chunks=[c])
+    # whole passes over the sample until the time budget is spent (a workload
+    # smaller than the budget is run several times over)
+    passes = 0
+    t = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        while True:
+            list(ex.map(one, chunks))
+            passes += 1
+            dt = time.perf_counter() - t
+            if dt >= seconds:
+                break
+    rows = sum(min(W.ROW_CHUNK, w.rows - c * W.ROW_CHUNK) for c in chunks)
+    bytes_in = passes * w.shards * rows * w.cols * 2
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = host_cores
+    return {"value": round(bytes_in / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host_cores": host_cores, "host_cores_usable": affinity, "threads": threads,
+            "sample": f"{rows} of {w.rows} rows of each of the {w.shards} shards ({len(chunks)} chunks of "
+                      f"{W.ROW_CHUNK} rows): compress + decompress-reduce"
+                      + (" + requantize" if cout else "") + f"; {passes} pass(es), {dt:.1f} s; NumPy float32 "
+                      f"oracle over a pool of {threads} threads on a host with {host_cores} cores"}
+
+
+def oracle_tensor_scale(w, oc, bits):
+    """The oracle's data-driven FP8 tensor scale of one whole shard: the abs-max
+    of the transformed tensor is the max over row chunks (run in a thread pool),
+    and the oracle's own scale rule is applied to it."""
+    import numpy as np
+    from oracle import codecs as cd
+    import workloads as W
+    step = W.ROW_CHUNK
+
+    def amax(r0):
+        return float(np.max(np.abs(cd.transform(oc, bits[r0:r0 + step]))))
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        A = max(ex.map(amax, range(0, bits.shape[0], step)))
+    return cd.auto_tensor_scale(np.float32([A]), oc.format)
+
+
+def quality(w, ctx):
+    """rel-MSE of the compress round trip (shard 0) and of the reduce +
+    requantize round trip, GPU against the oracle at the same tensor scale, on
+    a seeded sample of row chunks. The GPU compresses the step's first input
+    set again with the data-driven tensor scale of each whole tensor (AUTO);
+    the oracle computes that scale from the whole tensor itself, so both sides
+    quantize the sample rows with the same g and their codes must agree bit for
+    bit. The delayed-scale figure (the scale the timed steps used: the previous
+    step's abs-max) is reported beside it."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import codecs as cd
+    from oracle.formats import bf16_bits_to_f32
+    import quantized_compression_tensor_amd as T
+    import workloads as W
+
+    dev = "cuda"
+    c_in, c_out = ctx["c_in"], ctx["c_out"]
+    oc = cd.Codec(w.in_format, w.in_block, w.hadamard)
+    ocout = cd.Codec(w.out_format, w.out_block, w.hadamard) if w.out_format else None
+    fp8 = w.in_format in T.FP8_FORMATS
+    ch = W.sample_chunks(w, 3, seed=7)
+    rows_idx = W.chunk_rows(ch, w.rows)
+    ridx = torch.from_numpy(rows_idx).to(dev)
+    bits0 = ctx["sets_bits"]
+    xs0 = ctx["xs"][0]
+
+    # GPU: AUTO compress of every shard of set 0, reduce + requantize, decodes
+    qb = [T.empty_compressed(c_in, w.rows, w.cols, dev) for _ in range(w.shards)]
+    for r in range(w.shards):
+        wsb = torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) if fp8 else None
+        T.taco_compress(c_in, xs0[r], w.rows, w.cols, T.TACO_SCALE_AUTO if fp8 else 1.0, qb[r], workspace=wsb)
+    d = torch.empty(w.n, dtype=torch.float32, device=dev)
+
+    def decoded_rows(c, buf):
+        T.taco_decompress(c, buf, w.rows, w.cols, d, 0)
+        return d.view(w.rows, w.cols)[ridx].cpu().numpy()
+
+    got_c = decoded_rows(c_in, qb[0])
+    got_delayed = decoded_rows(c_in, ctx["bufs"][0][0])
+    if c_out is not None:
+        rq = T.empty_compressed(c_out, w.rows, w.cols, dev)
+        T.taco_decompress_reduce(c_in, qb, w.rows, w.cols, None, c_out, rq)
+        got_r = decoded_rows(c_out, rq)
+    else:
+        T.taco_decompress_reduce(c_in, qb, w.rows, w.cols, d)
+        got_r = d.view(w.rows, w.cols)[ridx].cpu().numpy()
+    torch.cuda.synchronize()
+
+    def gpu_region_rows(c, buf):
+        """codes / block metadata / g of the sample rows, parsed by the layout."""
+        L = T.taco_layout(c, w.rows, w.cols)
+        h = buf.cpu().numpy()
+        cb = w.cols // 2 if c.format == T.TACO_FMT_INT4_ASYM else w.cols
+        nb = w.cols // c.block
+        mb = 1 if c.format in T.FP8_FORMATS else 4
+        codes = h[L.codes_off:L.codes_off + L.codes_bytes].reshape(w.rows, cb)[rows_idx]
+        meta = h[L.scale_off:L.scale_off + L.scale_bytes].reshape(w.rows, nb * mb)[rows_idx]
+        aux = h[L.aux_off:L.aux_off + L.aux_bytes].reshape(w.rows, nb)[rows_idx] if L.aux_bytes else None
+        g = h[L.tensor_off:L.tensor_off + 4].view(np.float32)[0] if L.tensor_bytes else None
+        return codes, meta, aux, g
+
+    def same(gpu, ref):
+        codes, meta, aux, g = gpu
+        ok = bool((codes.reshape(-1) == ref.codes.reshape(-1)).all())
+        ok &= bool((meta.reshape(-1) == np.ascontiguousarray(ref.scale).view(np.uint8).reshape(-1)).all())
+        if aux is not None:
+            ok &= bool((aux.reshape(-1) == ref.zero.reshape(-1)).all())
+        if g is not None:
+            ok &= bool(np.float32(g).view(np.uint32) == np.float32(ref.tensor_scale).view(np.uint32))
+        return ok
+
+    # oracle: each shard's scale from its whole tensor, then the sample rows
+    t0 = time.perf_counter()
+    gs = [oracle_tensor_scale(w, oc, bits0[r]) if fp8 else None for r in range(w.shards)]
+    ref_sh = [oracle.compress(oc, bits0[r][rows_idx], tensor_scale=gs[r]) for r in range(w.shards)]
+    acc, rq_ref = oracle.decompress_reduce(ref_sh, ocout)
+    ref_c = oracle.decode(ref_sh[0])
+    ref_r = oracle.decode(rq_ref) if rq_ref is not None else acc
+    t_oracle = time.perf_counter() - t0
+
+    x0 = bf16_bits_to_f32(bits0[0][rows_idx])
+    exact = np.zeros(x0.shape, np.float64)
+    for r in range(w.shards):
+        exact += bf16_bits_to_f32(bits0[r][rows_idx]).astype(np.float64)
+    rm = oracle.rel_mse
+    out = {
+        "sample_rows": int(len(rows_idx)),
+        "tensor_scale": "data-driven (AUTO) on both sides" if fp8 else "n/a",
+        "compress": {"rel_mse_gpu": rm(got_c, x0), "rel_mse_oracle": rm(ref_c, x0),
+                     "codes_bit_exact": same(gpu_region_rows(c_in, qb[0]), ref_sh[0])},
+        "reduce": {"rel_mse_gpu": rm(got_r, exact), "rel_mse_oracle": rm(ref_r, exact),
+                   "against": "exact float64 sum of the bf16 shards",
+                   "codes_bit_exact": same(gpu_region_rows(c_out, rq), rq_ref) if c_out is not None else
+                   bool((got_r.view(np.uint32) == acc.view(np.uint32)).all())},
+        "oracle_seconds": round(t_oracle, 2),
+    }
+    if fp8:
+        g_gpu = [np.float32(T.regions(qb[r], c_in, w.rows, w.cols)[3][0].item()) for r in range(w.shards)]
+        out["gpu_g_equals_oracle_g"] = all(g_gpu[r].view(np.uint32) == np.float32(gs[r]).view(np.uint32)
+                                           for r in range(w.shards))
+        out["delayed_scale"] = {
+            "rel_mse_gpu": rm(got_delayed, x0),
+            "vs_data_driven": round(rm(got_delayed, x0) / max(rm(got_c, x0), 1e-300), 4),
+            "note": "compress round trip of the timed steps' shard 0, whose g is the previous step's abs-max / 448"}
+    return out
+
+
+def setup(w, args):
+    """Seeded inputs on the device, compressed buffers and workspaces."""
+    import numpy as np
+    import torch
+    import quantized_compression_tensor_amd as T
+    import workloads as W
+    dev = "cuda"
+    c_in = T.codec(w.in_format, w.in_block, 1 if w.hadamard else 0)
+    c_out = T.codec(w.out_format, w.out_block, 1 if w.hadamard else 0) if w.out_format else None
+    fp8 = w.in_format in T.FP8_FORMATS
+    in_bytes = w.shards * w.n * 2
+    nsets = max(2, min(4, -(-2 * MALL_BYTES // in_bytes) + 1))
+    sets_bits, xs, bufs, outs = None, [], [], []
+    for s in range(nsets):
+        bits = [W.make_shard(w, r + 100 * s) for r in range(w.shards)]
+        if s == 0:
+            sets_bits = bits
+        xs.append([torch.from_numpy(b.view(np.int16)).to(dev) for b in bits])
+        bufs.append([T.empty_compressed(c_in, w.rows, w.cols, dev) for _ in range(w.shards)])
+        outs.append(T.empty_compressed(c_out, w.rows, w.cols, dev) if c_out is not None
+                    else torch.empty(w.n, dtype=torch.float32, device=dev))
+    wss = [torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(w.shards)]
+    scale = {"delayed": T.TACO_SCALE_DELAYED, "auto": T.TACO_SCALE_AUTO, "given": 0.01}[args.scale_mode] \
+        if fp8 else 1.0
+    torch.cuda.synchronize()
+    return dict(c_in=c_in, c_out=c_out, fp8=fp8, nsets=nsets, sets_bits=sets_bits, xs=xs, bufs=bufs, outs=outs,
+                wss=wss, scale=scale, use_ws=fp8 and args.scale_mode != "given", in_bytes=in_bytes)
+
+
+def pctl(v, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(v), q)), 5)
+
+
+def run_workload(w, args, headline):
+    """Time one workload: returns its summary dict (and the step function for
+    the optional overlap measurement)."""
+    import torch
+    import quantized_compression_tensor_amd as T
+
+    dev = "cuda"
+    ctx = setup(w, args)
+    c_in, c_out, nsets = ctx["c_in"], ctx["c_out"], ctx["nsets"]
+    xs, bufs, outs, wss = ctx["xs"], ctx["bufs"], ctx["outs"], ctx["wss"]
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    def compress(s):
+        for r in range(w.shards):
+            T.taco_compress(c_in, xs[s][r], w.rows, w.cols, ctx["scale"], bufs[s][r],
+                            workspace=wss[r] if ctx["use_ws"] else None, stream=sh)
+
+    def reduce(s):
+        if c_out is not None:
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, None, c_out, outs[s], stream=sh)
+        else:
+            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, outs[s], stream=sh)
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    with torch.cuda.stream(stream):
+        # first calls seed the delayed-scale history with this data
+        for s in range(nsets):
+            compress(s)
+            reduce(s)
+        torch.cuda.synchronize()
+        if args.launch == "graph":
+            g_step = []
+            for s in range(nsets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    compress(s)
+                    reduce(s)
+                g_step.append(g)
+
+        def step(s):
+            if args.launch == "graph":
+                g_step[s].replay()
+            else:
+                compress(s)
+                reduce(s)
+
+        # the first steps after the GPU sat idle (while the host generated the
+        # inputs) run slower until its clocks rise: before the W warm-up steps,
+        # steps run for at least --prewarm seconds of wall time
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < args.prewarm:
+            for _ in range(8):
+                step(i % nsets)
+                i += 1
+            torch.cuda.synchronize()
+        prewarm_steps = i
+        for i in range(args.warmup):
+            step(i % nsets)
+        torch.cuda.synchronize()
+
+        # timed region: K whole steps between one pair of events (an event
+        # record between kernels costs GPU time, so none inside the region)
+        ev0, ev1 = mk(), mk()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(K):
+            step(i % nsets)
+        ev1.record(stream)
+        host = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+        # step-time distribution: K more steps, an event at every step boundary
+        evs = [mk() for _ in range(K + 1)]
+        evs[0].record(stream)
+        for i in range(K):
+            step(i % nsets)
+            evs[i + 1].record(stream)
+        # per-kernel launch durations in step context: K more steps with an
+        # event before the N compress launches, one between them and the
+        # reduce, and one after it; each average includes the short gap
+        # before each launch, so it bounds the kernel's own duration from above
+        ph = [(mk(), mk(), mk()) for _ in range(K)]
+        for i in range(K):
+            ph[i][0].record(stream)
+            compress(i % nsets)
+            ph[i][1].record(stream)
+            reduce(i % nsets)
+            ph[i][2].record(stream)
+        # streaming reference: a plain device copy of one shard (2 B read +
+        # 2 B written per element), N per step, back to back. Left out of the
+        # counter passes, whose calibration copies must be the only large
+        # device copies of the run.
+        a_x, b_x = mk(), mk()
+        if not args.copy_calibration:
+            ref_out = torch.empty(w.n, dtype=torch.int16, device=dev)
+            a_x.record(stream)
+            for i in range(K):
+                for r in range(w.shards):
+                    ref_out.copy_(xs[i % nsets][r].reshape(-1))
+            b_x.record(stream)
+        # the consumer-side decode of the gather-stage output to bf16 (the next
+        # GEMM's input; FP8: with the inverse transform), outside the step
+        dec_out = torch.empty(w.n, dtype=torch.bfloat16, device=dev) if c_out is not None else None
+        a_d, b_d = mk(), mk()
+        if dec_out is not None:
+            a_d.record(stream)
+            for i in range(K):
+                T.taco_decompress(c_out, outs[i % nsets], w.rows, w.cols, dec_out, 1, stream=sh)
+            b_d.record(stream)
+        torch.cuda.synchronize()
+
+    steps_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    comp_launch = [ph[i][0].elapsed_time(ph[i][1]) / w.shards for i in range(K)]
+    red_launch = [ph[i][1].elapsed_time(ph[i][2]) for i in range(K)]
+    t_comp = sum(comp_launch) / K
+    t_red = sum(red_launch) / K
+    t_dec = a_d.elapsed_time(b_d) / K if dec_out is not None else None
+    t_ref = a_x.elapsed_time(b_x) / (K * w.shards) if not args.copy_calibration else None
+    ms_step = wall * 1e3 / K
+    b_comp, b_red = algorithmic_bytes(w)
+    comp_gbs = b_comp / (t_comp * 1e-3) / 1e9
+    red_gbs = b_red / (t_red * 1e-3) / 1e9
+    res = {
+        "name": w.name,
+        "workload": f"{w.name}: {w.shards} bf16 shards of {w.rows}x{w.cols}; compress {FORMAT_NAMES[w.in_format]} "
+                    f"block {w.in_block}{' + Hadamard' if w.hadamard else ''}; decompress-reduce "
+                    + (f"-> {FORMAT_NAMES[w.out_format]}" if w.out_format else "-> FP32 sum"),
+        "shards": w.shards, "rows": w.rows, "cols": w.cols,
+        "value": round(ctx["in_bytes"] / (ms_step * 1e-3) / 1e9, 2),
+        "ms_per_step": round(ms_step, 5),
+        "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_ms_distribution": {"median": pctl(steps_ms, 50), "p10": pctl(steps_ms, 10), "p90": pctl(steps_ms, 90),
+                                 "note": "K further steps with an event at each step boundary"},
+        "kernels": {
+            "compress_ms": round(t_comp, 5), "compress_GBs": round(comp_gbs, 1),
+            "compress_hbm_frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+            "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
+            "reduce_hbm_frac": round(red_gbs / HBM_PEAK_GBS, 4),
+            "compress_ms_p10_p90": [pctl(comp_launch, 10), pctl(comp_launch, 90)],
+            "reduce_ms_p10_p90": [pctl(red_launch, 10), pctl(red_launch, 90)],
+            **({"decode_bf16_ms": round(t_dec, 5),
+                "decode_bf16_GBs": round(decode_bytes(w) / (t_dec * 1e-3) / 1e9, 1)} if t_dec else {}),
+            "phases_hbm_frac": round((w.shards * b_comp + b_red) / ((w.shards * t_comp + t_red) * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 4),
+            "host_ms_per_step": round(host * 1e3 / K, 5),
+            "event_ms_per_step": round(ev0.elapsed_time(ev1) / K, 5),
+        },
+        "algorithmic_bytes": {"compress": b_comp, "reduce": b_red, "step": w.shards * b_comp + b_red},
+        "input_sets": nsets,
+        "prewarm_steps": prewarm_steps,
+        "tensor_scale": args.scale_mode if ctx["fp8"] else "n/a",
+    }
+    if t_ref:
+        res["copy_reference"] = {
+            "kernel": "device copy of one bf16 shard (2 B read + 2 B written per element), timed like the "
+                      "compress: the streaming rate this machine reaches at this size",
+            "ms": round(t_ref, 5), "GBs": round(4 * w.n / (t_ref * 1e-3) / 1e9, 1),
+            "compress_vs_copy": round(comp_gbs / (4 * w.n / (t_ref * 1e-3) / 1e9), 3)}
+    if not args.no_quality:
+        res["quality"] = quality(w, ctx)
+    extras = {"stream": stream, "step": lambda s: (compress(s), reduce(s)), "ctx": ctx, "t_comp": t_comp,
+              "t_red": t_red, "ms_step": ms_step}
+    return res, extras
 
 
 def measure_rank_share(w, xs, stream, K):
@@ -148,32 +791,58 @@ def measure_rank_share(w, xs, stream, K):
 
 
 def measure_ring(w, xs, stream, K):
-    """One hop of the full-loop ring (dequantize the incoming shard, add the
+    """One hop of the quantized ring (dequantize the incoming shard, add the
     local bf16 shard, quantize for the next hop) timed at full size, and the
-    whole ring over the workload's shards: its MSE against the exact sum, next
-    to the MSE of quantizing the exact sum once (the all-gather alone)."""
+    whole rings over the workload's shards: the full loop (N - 1 hops in one
+    direction, then the gather) and the semi-loop (each chunk gathered from both
+    ends towards the middle: two chains of about N/2 hops, joined by one more
+    hop), each decoded and compared with the exact sum, next to quantizing the
+    exact sum once (the all-gather alone)."""
     import torch
     import quantized_compression_tensor_amd as T
-    c_in = T.codec(w.in_format, w.in_block, 0)
     c_out = T.codec(w.out_format, w.out_block, 0)
     dev = "cuda"
     N = len(xs)
     sh = stream.cuda_stream
     bufs = [T.empty_compressed(c_out, w.rows, w.cols, dev) for _ in range(3)]
+
+    def decoded(buf):
+        o = torch.empty(w.n, dtype=torch.float32, device=dev)
+        T.taco_decompress(c_out, buf, w.rows, w.cols, o, 0, stream=sh)
+        return o
+
     with torch.cuda.stream(stream):
-        # the ring: the first rank quantizes its shard, every later rank adds its own
+        # full loop: the first rank quantizes its shard, every later rank adds its own
         T.taco_ring_hop(c_out, None, xs[0], w.rows, w.cols, None, c_out, bufs[0], stream=sh)
         for r in range(1, N):
             T.taco_ring_hop(c_out, bufs[(r - 1) % 2], xs[r], w.rows, w.cols, None, c_out, bufs[r % 2], stream=sh)
-        ring = torch.empty(w.n, dtype=torch.float32, device=dev)
-        T.taco_decompress(c_out, bufs[(N - 1) % 2], w.rows, w.cols, ring, 0, stream=sh)
+        ring = decoded(bufs[(N - 1) % 2])
+        # semi-loop: ranks 0 .. h-1 chain forwards, ranks N-1 .. h backwards,
+        # and the last rank of the backward chain adds the forward partial sum
+        h = N // 2
+        fwd = [T.empty_compressed(c_out, w.rows, w.cols, dev) for _ in range(2)]
+        bwd = [T.empty_compressed(c_out, w.rows, w.cols, dev) for _ in range(2)]
+        T.taco_ring_hop(c_out, None, xs[0], w.rows, w.cols, None, c_out, fwd[0], stream=sh)
+        for r in range(1, h):
+            T.taco_ring_hop(c_out, fwd[(r - 1) % 2], xs[r], w.rows, w.cols, None, c_out, fwd[r % 2], stream=sh)
+        f_last = fwd[(h - 1) % 2]
+        T.taco_ring_hop(c_out, None, xs[N - 1], w.rows, w.cols, None, c_out, bwd[0], stream=sh)
+        j = 0
+        for r in range(N - 2, h - 1, -1):
+            T.taco_ring_hop(c_out, bwd[j % 2], xs[r], w.rows, w.cols, None, c_out, bwd[(j + 1) % 2], stream=sh)
+            j += 1
+        b_last = bwd[j % 2]
+        # join: dequantize both partial sums and requantize their sum (a
+        # two-source decompress-reduce in the gather codec)
+        semi_q = T.empty_compressed(c_out, w.rows, w.cols, dev)
+        T.taco_decompress_reduce(c_out, [f_last, b_last], w.rows, w.cols, None, c_out, semi_q, stream=sh)
+        semi = decoded(semi_q)
         exact = torch.zeros(w.n, dtype=torch.float64, device=dev)
         for x in xs:
             exact += x.view(torch.bfloat16).reshape(-1).to(torch.float64)
         once_q = T.empty_compressed(c_out, w.rows, w.cols, dev)
         T.taco_requantize(c_out, exact.to(torch.float32), w.rows, w.cols, 1.0, once_q, stream=sh)
-        once = torch.empty(w.n, dtype=torch.float32, device=dev)
-        T.taco_decompress(c_out, once_q, w.rows, w.cols, once, 0, stream=sh)
+        once = decoded(once_q)
         # timing: K hops back to back between one pair of events
         for i in range(3):
             T.taco_ring_hop(c_out, bufs[i % 2], xs[i % N], w.rows, w.cols, None, c_out, bufs[2], stream=sh)
@@ -187,229 +856,13 @@ def measure_ring(w, xs, stream, K):
     n = w.n
     qb = n + (4 * (n // 64) if w.out_format == 2 else 5 * (n // 128))   # INT8 codes + metadata
     hop_bytes = qb + 2 * n + qb
-    mse_ring = float(((ring.double() - exact) ** 2).mean())
-    mse_once = float(((once.double() - exact) ** 2).mean())
+    mse = lambda v: float(((v.double() - exact) ** 2).mean())
     return {"hop_ms": round(hop_ms, 5), "hop_GBs": round(hop_bytes / (hop_ms * 1e-3) / 1e9, 1),
             "hop_hbm_frac": round(hop_bytes / (hop_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "hop_algorithmic_bytes": hop_bytes, "ranks": N, "hops": N - 1,
-            "ring_mse": mse_ring, "all_gather_only_mse": mse_once, "ring_codec_in": "INT8 (gather codec)"}
-
-
-def decode_bytes(w):
-    """Bytes the consumer-side decode of the gather-stage output to bf16 moves."""
-    n = w.n
-    if w.out_format in (1, 5):
-        src = n + n // w.out_block + 16
-    elif w.out_format == 2:
-        src = n + 4 * (n // 64)
-    else:
-        src = n + 5 * (n // 128)
-    return src + 2 * n
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "quantized_compression_tensor_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def read_traffic(name, workload, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
-    if not os.path.exists(p):
-        return None
-    kv = {}
-    for line in open(p):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != src_hash:
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-COPY_BYTES = 256 << 20
-KERNEL_KEYS = {"compress": ("k_fp8_had_compress", "k_quantize"), "reduce": ("k_reduce",)}
-
-
-def _csv_rows(d, suffix):
-    import csv
-    import glob
-    out = []
-    for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
-        with open(f) as fh:
-            out.extend(csv.DictReader(fh))
-    return out
-
-
-def summarize(fetch_dir, write_dir, trace_dir, workload, command, trace_log=None):
-    """Per-launch HBM bytes of the hot kernels from two counter passes, scaled by
-    what the same counters read for a plain copy of COPY_BYTES (read and write),
-    plus the kernel-trace averages and, when the profiled run's output is given,
-    the bench's own event timing in that same run; written to
-    profiles/<kernel>_<workload>_*.txt."""
-    import numpy as np
-    src_hash = kernel_source_hash()
-    bench_ms = {}
-    if trace_log:
-        lines = [l for l in open(trace_log) if l.startswith("{")]
-        if lines:
-            k = json.loads(lines[-1]).get("kernels", {})
-            bench_ms = {"compress": k.get("compress_ms"), "reduce": k.get("reduce_ms")}
-    per = {}
-    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
-        for row in _csv_rows(d, "counter_collection.csv"):
-            if row.get("Counter_Name") != cname:
-                continue
-            name = row.get("Kernel_Name", "")
-            per.setdefault((cname, name), []).append(float(row["Counter_Value"]))
-    # the calibration copies are the three largest copy dispatches of the run
-    copy_f = sorted((v for (c, k), vs in per.items() if c == "FETCH_SIZE" and "copy" in k.lower() for v in vs),
-                    reverse=True)[:3]
-    copy_w = sorted((v for (c, k), vs in per.items() if c == "WRITE_SIZE" and "copy" in k.lower() for v in vs),
-                    reverse=True)[:3]
-    f_fetch = COPY_BYTES / (np.median(copy_f) * 1024) if copy_f else None
-    f_write = COPY_BYTES / (np.median(copy_w) * 1024) if copy_w else None
-    trace = {}
-    for row in _csv_rows(trace_dir, "kernel_stats.csv"):
-        trace[row["Name"]] = row
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    written = []
-    for key, subs in KERNEL_KEYS.items():
-        fk = [(k, vs) for (c, k), vs in per.items() if c == "FETCH_SIZE" and any(t in k for t in subs)]
-        wk = [(k, vs) for (c, k), vs in per.items() if c == "WRITE_SIZE" and any(t in k for t in subs)]
-        fk.sort(key=lambda kv: -len(kv[1]))
-        wk.sort(key=lambda kv: -len(kv[1]))
-        if not fk or not wk:
-            continue
-        kname = fk[0][0]
-        fetch_kib = float(np.median(fk[0][1]))
-        write_kib = float(np.median(wk[0][1]))
-        hbm = None
-        if f_fetch and f_write:
-            hbm = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
-        tr = next((v for n, v in trace.items() if n == kname), None)
-        path = os.path.join(ROOT, "profiles", f"{key}_{workload}_counters.txt")
-        with open(path, "w") as fh:
-            fh.write(f"# rocprofv3 hardware counters for {kname}\n")
-            fh.write(f"# workload: {workload}\n# command: {command}\n")
-            fh.write("# FETCH_SIZE and WRITE_SIZE come from separate --pmc passes (KiB per dispatch,\n"
-                     "# median over dispatches); each is scaled by COPY_BYTES / counter of a plain\n"
-                     "# device-to-device copy of COPY_BYTES profiled in the same pass.\n")
-            fh.write(f"kernel: {kname}\n")
-            fh.write(f"source_hash: {src_hash}\n")
-            fh.write(f"fetch_kib_per_dispatch: {fetch_kib:.1f}\n")
-            fh.write(f"write_kib_per_dispatch: {write_kib:.1f}\n")
-            fh.write(f"copy_bytes: {COPY_BYTES}\n")
-            fh.write(f"copy_fetch_factor: {f_fetch}\n")
-            fh.write(f"copy_write_factor: {f_write}\n")
-            fh.write(f"hbm_bytes_per_launch: {hbm}\n")
-            if tr is not None:
-                fh.write(f"trace_calls: {tr.get('Calls')}\n")
-                fh.write(f"trace_average_ns: {tr.get('AverageNs')}\n")
-                fh.write(f"trace_min_ns: {tr.get('MinNs')}\n")
-                fh.write(f"trace_max_ns: {tr.get('MaxNs')}\n")
-            if bench_ms.get(key) is not None:
-                fh.write("# the bench's own HIP-event average in the profiled run (back-to-back launches,\n"
-                         "# including the gap before each launch, which the profiler widens)\n")
-                fh.write(f"bench_event_average_ns_under_profiler: {bench_ms[key] * 1e6:.0f}\n")
-        written.append(path)
-    if trace:
-        path = os.path.join(ROOT, "profiles", f"kernels_{workload}_trace.txt")
-        with open(path, "w") as fh:
-            fh.write(f"# rocprofv3 kernel-trace statistics, workload {workload}\n# command: {command}\n")
-            fh.write("# (kernel durations exclude dispatch gaps; the bench's step events include them)\n")
-            fh.write(f"source_hash: {src_hash}\n")
-            fh.write(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
-            for name, row in sorted(trace.items(), key=lambda kv: -float(kv[1]["TotalDurationNs"])):
-                fh.write(f"{int(row['Calls']):>6} {float(row['AverageNs']) / 1e3:>9.2f} "
-                         f"{float(row['MinNs']) / 1e3:>9.2f} {float(row['MaxNs']) / 1e3:>9.2f}  {name[:160]}\n")
-        written.append(path)
-    print("\n".join(written))
-
-
-def cpu_baseline(w, seconds):
-    """The oracle, as written, on a bounded sample of the same workload: row
-    chunks of every shard, compressed and reduced (+ requantized), spread over
-    a thread pool (NumPy releases the GIL inside its loops)."""
-    import numpy as np
-    import oracle
-    from oracle import codecs as cd
-    import workloads as W
-
-    cin = cd.Codec(w.in_format, w.in_block, w.hadamard)
-    cout = cd.Codec(w.out_format, w.out_block, w.hadamard) if w.out_format else None
-    nchunks = (w.rows + W.ROW_CHUNK - 1) // W.ROW_CHUNK
-    threads = max(1, min(16, os.cpu_count() or 1))
-
-    inputs = {}
-
-    def one(chunk):
-        shards = [oracle.compress(cin, inputs[(chunk, r)]) for r in range(w.shards)]
-        oracle.decompress_reduce(shards, cout)
-        return chunk
-
-    # calibrate on one chunk, then size the sample to the time budget
-    for r in range(w.shards):
-        inputs[(0, r)] = W.make_shard(w, r, chunks=[0])
-    t = time.perf_counter()
-    one(0)
-    per_chunk = time.perf_counter() - t
-    want = max(1, int(seconds * threads / max(per_chunk, 1e-6)))
-    chunks = list(range(min(nchunks, max(threads, want))))
-    for c in chunks:
-        for r in range(w.shards):
-            if (c, r) not in inputs:
-                inputs[(c, r)] = W.make_shard(w, r, chunks=[c])
-    # whole passes over the sample until the time budget is spent (a workload
-    # smaller than the budget is run several times over)
-    passes = 0
-    t = time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        while True:
-            list(ex.map(one, chunks))
-            passes += 1
-            dt = time.perf_counter() - t
-            if dt >= seconds:
-                break
-    rows = sum(min(W.ROW_CHUNK, w.rows - c * W.ROW_CHUNK) for c in chunks)
-    bytes_in = passes * w.shards * rows * w.cols * 2
-    return {"value": round(bytes_in / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.rows} rows of each of the {w.shards} shards ({len(chunks)} chunks of "
-                      f"{W.ROW_CHUNK} rows): compress + decompress-reduce"
-                      + (" + requantize" if cout else "") + f"; {passes} pass(es), {dt:.1f} s"}
-
-
-def quality(w, bufs, sets_bits, c_in):
-    """rel-MSE of the compress round trip of shard 0 (set 0) on a seeded sample of
-    row chunks: the GPU's (decoded on the GPU) next to the oracle's own."""
-    import numpy as np
-    import torch
-    import oracle
-    from oracle import codecs as cd
-    from oracle.formats import bf16_bits_to_f32
-    import quantized_compression_tensor_amd as T
-    import workloads as W
-
-    ch = W.sample_chunks(w, 3, seed=7)
-    rows_idx = W.chunk_rows(ch, w.rows)
-    d = torch.empty(w.n, dtype=torch.float32, device="cuda")
-    T.taco_decompress(c_in, bufs[0][0], w.rows, w.cols, d, 0)
-    torch.cuda.synchronize()
-    x = sets_bits[0][0][rows_idx]
-    got = d.view(w.rows, w.cols)[torch.from_numpy(rows_idx).cuda()].cpu().numpy()
-    xf = bf16_bits_to_f32(x)
-    oc = cd.Codec(w.in_format, w.in_block, w.hadamard)
-    ref = oracle.decode(oracle.compress(oc, x))
-    return {"rel_mse_gpu": oracle.rel_mse(got, xf), "rel_mse_oracle": oracle.rel_mse(ref, xf),
-            "sample_rows": int(len(rows_idx))}
+            "ring_mse": mse(ring), "semi_loop_mse": mse(semi), "all_gather_only_mse": mse(once),
+            "semi_loop": f"ranks 0..{h - 1} forwards, {N - 1}..{h} backwards, joined by one two-source reduce",
+            "ring_codec_in": "INT8 (gather codec)"}
 
 
 def measure_overlap(w, step_fn, nsets, stream, codec_ms, K):
@@ -450,234 +903,113 @@ def measure_overlap(w, step_fn, nsets, stream, codec_ms, K):
 
 def main():
     args = parse()
+    if args.summarize_issue:
+        names = [args.workload] + [x for x in args.extra.split(",") if x and x != "none"]
+        summarize_issue(args.summarize_issue, names, args.command)
+        return
     if args.summarize:
         if len(args.summarize) not in (3, 4):
             sys.exit("--summarize takes FETCH_DIR WRITE_DIR TRACE_DIR [TRACE_LOG]")
         fetch, write, trace = args.summarize[:3]
         log = args.summarize[3] if len(args.summarize) == 4 else None
-        summarize(fetch, write, trace, args.workload, args.command, log)
+        names = [args.workload] + [x for x in args.extra.split(",") if x and x != "none"]
+        summarize(fetch, write, trace, names, args.command, log)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU exchange is a design, not part of this build)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import quantized_compression_tensor_amd as T
     import workloads as W
 
-    w = W.WORKLOADS[args.workload]
-    if args.fp8_codes == "e5m2" and w.in_format == T.TACO_FMT_FP8_DUAL:
-        w = dataclasses.replace(w, in_format=T.TACO_FMT_FP8E5_DUAL,
-                                out_format=T.TACO_FMT_FP8E5_DUAL if w.out_format else None)
+    def resolve(name):
+        w = W.WORKLOADS[name]
+        if args.fp8_codes == "e5m2" and w.in_format == T.TACO_FMT_FP8_DUAL:
+            w = dataclasses.replace(w, in_format=T.TACO_FMT_FP8E5_DUAL,
+                                    out_format=T.TACO_FMT_FP8E5_DUAL if w.out_format else None)
+        return w
+
     torch.cuda.set_device(0)
-    dev = "cuda"
-    c_in = T.codec(w.in_format, w.in_block, 1 if w.hadamard else 0)
-    c_out = T.codec(w.out_format, w.out_block, 1 if w.hadamard else 0) if w.out_format else None
-    fp8 = w.in_format in T.FP8_FORMATS
-    scale = {"delayed": T.TACO_SCALE_DELAYED, "auto": T.TACO_SCALE_AUTO, "given": 0.01}[args.scale_mode] \
-        if fp8 else 1.0
-    use_ws = fp8 and args.scale_mode != "given"
-
-    in_bytes = w.shards * w.n * 2
-    nsets = max(2, min(4, -(-2 * MALL_BYTES // in_bytes) + 1))
-    sets_bits, xs, bufs, outs = [], [], [], []
-    for s in range(nsets):
-        bits = [W.make_shard(w, r + 100 * s) for r in range(w.shards)]
-        sets_bits.append(bits if s == 0 else None)
-        xs.append([torch.from_numpy(b.view(np.int16)).to(dev) for b in bits])
-        bufs.append([T.empty_compressed(c_in, w.rows, w.cols, dev) for _ in range(w.shards)])
-        if c_out is not None:
-            outs.append(T.empty_compressed(c_out, w.rows, w.cols, dev))
-        else:
-            outs.append(torch.empty(w.n, dtype=torch.float32, device=dev))
-    wss = [torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(w.shards)]
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.Stream()
-    sh = stream.cuda_stream
-
-    def compress_one(s, r):
-        T.taco_compress(c_in, xs[s][r], w.rows, w.cols, scale, bufs[s][r],
-                        workspace=wss[r] if use_ws else None, stream=sh)
-
-    def compress(s):
-        for r in range(w.shards):
-            compress_one(s, r)
-
-    def reduce(s):
-        if c_out is not None:
-            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, None, c_out, outs[s], stream=sh)
-        else:
-            T.taco_decompress_reduce(c_in, bufs[s], w.rows, w.cols, outs[s], stream=sh)
-
-    with torch.cuda.stream(stream):
-        # first calls seed the delayed-scale history with this data
-        for s in range(nsets):
-            compress(s)
-            reduce(s)
-        torch.cuda.synchronize()
-        if args.launch == "graph":
-            g_step = []
-            for s in range(nsets):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    compress(s)
-                    reduce(s)
-                g_step.append(g)
-
-        def step(s):
-            if args.launch == "graph":
-                g_step[s].replay()
-            else:
-                compress(s)
-                reduce(s)
-
-        for i in range(args.warmup):
-            step(i % nsets)
-        torch.cuda.synchronize()
-
-        K = args.steps
-        mk = lambda: torch.cuda.Event(enable_timing=True)
-        # timed region: K whole steps between one pair of events (an event
-        # record between kernels costs GPU time, so none inside the region)
-        ev0, ev1 = mk(), mk()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(K):
-            step(i % nsets)
-        ev1.record(stream)
-        host = time.perf_counter() - t0
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-
-        # per-kernel launch durations (roofline): the same launches again, each
-        # kernel's K steps' worth back to back between one pair of events on the
-        # launch stream; the average includes the short gap between dependent
-        # launches, so it is an upper bound on the kernel's own duration
-        a_c, b_c, a_r, b_r = mk(), mk(), mk(), mk()
-        a_c.record(stream)
-        for i in range(K):
-            compress(i % nsets)
-        b_c.record(stream)
-        a_r.record(stream)
-        for i in range(K):
-            reduce(i % nsets)
-        b_r.record(stream)
-        # streaming reference: a plain device copy of each shard (2 B read +
-        # 2 B written per element), timed like the compress. Left out of the
-        # counter passes, whose calibration copies must be the only large
-        # device copies of the run.
-        a_x, b_x = mk(), mk()
-        if not args.copy_calibration:
-            ref_out = torch.empty(w.n, dtype=torch.int16, device=dev)
-            a_x.record(stream)
-            for i in range(K):
-                for r in range(w.shards):
-                    ref_out.copy_(xs[i % nsets][r].reshape(-1))
-            b_x.record(stream)
-        # the consumer-side decode of the gather-stage output to bf16 (the next
-        # GEMM's input; FP8: with the inverse transform), outside the step
-        dec_out = torch.empty(w.n, dtype=torch.bfloat16, device=dev) if c_out is not None else None
-        a_d, b_d = mk(), mk()
-        if dec_out is not None:
-            a_d.record(stream)
-            for i in range(K):
-                T.taco_decompress(c_out, outs[i % nsets], w.rows, w.cols, dec_out, 1, stream=sh)
-            b_d.record(stream)
-        torch.cuda.synchronize()
-
-    t_comp = a_c.elapsed_time(b_c) / (K * w.shards)   # ms per compress launch
-    t_red = a_r.elapsed_time(b_r) / K                 # ms per reduce call
-    t_dec = a_d.elapsed_time(b_d) / K if dec_out is not None else None
-    t_ref = a_x.elapsed_time(b_x) / (K * w.shards) if not args.copy_calibration else None
-    ms_step = wall * 1e3 / K
-    gpu_ms_step = ev0.elapsed_time(ev1) / K
-    value = in_bytes / (ms_step * 1e-3) / 1e9
-
-    b_comp, b_red = algorithmic_bytes(w)
-    comp_gbs = b_comp / (t_comp * 1e-3) / 1e9
-    red_gbs = b_red / (t_red * 1e-3) / 1e9
+    w = resolve(args.workload)
+    head, ex = run_workload(w, args, True)
     src_hash = kernel_source_hash()
+    kern = head["kernels"]
+    t_comp, t_red = ex["t_comp"], ex["t_red"]
+    b_comp, b_red = algorithmic_bytes(w)
     dominant = "compress" if w.shards * t_comp >= t_red else "reduce"
-    if dominant == "compress":
-        ach, bytes_launch, kname = comp_gbs, b_comp, "compress"
-    else:
-        ach, bytes_launch, kname = red_gbs, b_red, "reduce"
-    traffic = read_traffic(kname, w.name, src_hash)
+    ach = kern["compress_GBs"] if dominant == "compress" else kern["reduce_GBs"]
+    bytes_launch = b_comp if dominant == "compress" else b_red
+    traffic = read_traffic(dominant, w.name, src_hash)
 
-    rank_share = measure_rank_share(w, xs, stream, K=max(20, K // 2)) if args.rank_share else None
-
+    rank_share = measure_rank_share(w, ex["ctx"]["xs"], ex["stream"], K=max(20, args.steps // 2)) \
+        if args.rank_share else None
     ring = None
     if args.ring:
         if w.in_format in T.FP8_FORMATS:
             sys.exit("--ring applies to the INT workloads (the FP8 codec is not a ring codec)")
-        ring = measure_ring(w, xs[0], stream, K=max(10, K // 4))
-
+        ring = measure_ring(w, ex["ctx"]["xs"][0], ex["stream"], K=max(10, args.steps // 4))
     overlap = None
     if args.overlap:
-        overlap = measure_overlap(w, step_fn=lambda s: (compress(s), reduce(s)), nsets=nsets, stream=stream,
-                                  codec_ms=ms_step, K=max(5, K // 5))
+        overlap = measure_overlap(w, step_fn=ex["step"], nsets=ex["ctx"]["nsets"], stream=ex["stream"],
+                                  codec_ms=ex["ms_step"], K=max(5, args.steps // 5))
+    del ex
+    torch.cuda.empty_cache()
+
+    extras = {}
+    for name in [x for x in args.extra.split(",") if x and x != "none" and x != args.workload]:
+        r, e = run_workload(resolve(name), args, False)
+        del e
+        torch.cuda.empty_cache()
+        extras[name] = r
 
     if args.copy_calibration:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    q = quality(w, bufs, sets_bits, c_in)
     cpu = None if args.no_cpu else cpu_baseline(w, args.cpu_seconds)
+    eight = {x["name"]: x["step_hbm_frac"] for x in [head] + list(extras.values()) if x["shards"] == 8}
 
     out = {
         "metric": "compress+reduce GB/s of bf16 input (fraction of HBM peak); quant rel-MSE",
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: {w.shards} bf16 shards of {w.rows}x{w.cols}; "
-                        f"compress {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym', 'FP8 E5M2 dual-scale'][w.in_format]} "
-                        f"block {w.in_block}{' + Hadamard' if w.hadamard else ''}; decompress-reduce "
-                        + (f"-> {['', 'FP8 dual-scale', 'INT8 sym', 'INT4 asym', 'INT8 asym', 'FP8 E5M2 dual-scale'][w.out_format]}"
-                           if w.out_format else "-> FP32 sum"),
+            "workload": head["workload"], "name": w.name,
             "shards": w.shards, "rows": w.rows, "cols": w.cols,
-            "tensor_scale": args.scale_mode if fp8 else "n/a",
-            "launch": args.launch, "input_sets": nsets,
+            "input_dtype": "bf16", "arithmetic": "f32 (bf16 widened exactly; sums and transform in f32)",
+            "tensor_scale": head["tensor_scale"], "launch": args.launch, "input_sets": head["input_sets"],
         },
         "roofline": {
-            "bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_launch,
-            "copy_reference": {
-                "kernel": "device copy of one bf16 shard (2 B read + 2 B written per element), timed like "
-                          "the compress: the streaming rate this machine reaches at this size",
-                "ms": round(t_ref, 5), "GBs": round(4 * w.n / (t_ref * 1e-3) / 1e9, 1),
-                "compress_vs_copy": round(comp_gbs / (4 * w.n / (t_ref * 1e-3) / 1e9), 3),
-            } if t_ref else None,
+            "launch_ms": kern["compress_ms"] if dominant == "compress" else kern["reduce_ms"],
+            **({"copy_reference": head["copy_reference"]} if "copy_reference" in head else {}),
         },
-        "kernels": {
-            "compress_ms": round(t_comp, 5), "compress_GBs": round(comp_gbs, 1),
-            "reduce_ms": round(t_red, 5), "reduce_GBs": round(red_gbs, 1),
-            **({"decode_bf16_ms": round(t_dec, 5),
-                "decode_bf16_GBs": round(decode_bytes(w) / (t_dec * 1e-3) / 1e9, 1)} if t_dec else {}),
-            "step_hbm_frac": round((w.shards * b_comp + b_red) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "host_ms_per_step": round(host * 1e3 / K, 5),
-            "event_ms_per_step": round(gpu_ms_step, 5),
-        },
-        **({"rank_share": rank_share} if rank_share else {}),
-        "quality": q,
+        "step_hbm_frac": head["step_hbm_frac"],
+        "step_ms_distribution": head["step_ms_distribution"],
+        "kernels": kern,
+        "algorithmic_bytes": head["algorithmic_bytes"],
+        **({"quality": head["quality"]} if "quality" in head else {}),
         "cpu_baseline": cpu,
+        "eight_shard_step_hbm_frac": eight,
+        "workloads": extras,
+        **({"rank_share": rank_share} if rank_share else {}),
         **({"overlap": overlap} if overlap else {}),
         **({"ring": ring} if ring else {}),
         "source_hash": src_hash,
