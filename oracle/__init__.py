@@ -38,8 +38,10 @@ Where the pages leave a step open the oracle takes one plain reading; each is
 listed, with its reason, in the repository's design notes and repeated in the
 docstring of the function that implements it.
 
-Parity status. Formats, transform, reduction, the ring hop and the INT8 /
-asymmetric codecs are pinned by closed forms, brute force and library
+Parity status. Formats, transform, reduction, the ring hop and the rings
+built from it, the INT8 / asymmetric codecs, the error metrics and the FP8
+tensor-scale rules (data-driven g, its clamps, the gather-stage sum) are
+pinned by closed forms, hand-worked values, brute force and library
 cross-checks in ``tests/``. TACO's reshaping, ASH transform and dual-scale quantization are
 never defined on the pages (the referee on the TACO page says the reshaping
 and adaptive scales are "not quantified"), so ``compress_fp8_dual`` and its
@@ -73,6 +75,8 @@ from .codecs import (  # noqa: F401
     dequantize,
     decompress_reduce,
     ring_hop,
+    full_loop_ring,
+    semi_loop_ring,
     requantize,
     decode,
     auto_tensor_scale,

@@ -411,6 +411,41 @@ def ring_hop(incoming: Optional[Compressed], local_bits, out_codec: Codec, in_co
     return acc.reshape(rows, cols), quantize_values(out_codec, acc, rows, cols, None)
 
 
+def full_loop_ring(locals_bits, codec: Codec):
+    """The full-loop ring for one chunk ([EQuARX] "What carries the argument":
+    bandwidth-optimal, N - 1 hops): rank 0 quantizes its shard, every later
+    rank r = 1 .. N-1 dequantizes what it received, adds its own shard and
+    quantizes again (``ring_hop``); the last rank's output is what the
+    all-gather sends. Returns the Compressed result in ``codec`` (INT8_SYM or
+    INT8_ASYM)."""
+    q = None
+    for x in locals_bits:
+        _, q = ring_hop(q, x, codec, in_codec=codec)
+    return q
+
+
+def semi_loop_ring(locals_bits, codec: Codec):
+    """The semi-loop ring for one chunk ([EQuARX] "What carries the argument":
+    it uses both ring directions to halve the number of quantization hops; its
+    adder chain is a figure the page does not reproduce). Reading: with N >= 2
+    ranks and h = N // 2, ranks 0 .. h-1 form a chain in one direction and
+    ranks N-1 .. h a chain in the other, each link a ``ring_hop`` as in the
+    full loop (every rank quantizes what it sends on); the two chains' outputs
+    meet, are dequantized to FP32 and added in the order (first chain, second
+    chain), and the sum is quantized once for the all-gather
+    (``decompress_reduce`` of the two). The longest chain has N - h
+    quantizations instead of the full loop's N.
+
+    Returns the Compressed result in ``codec``."""
+    n = len(locals_bits)
+    assert n >= 2, "the semi-loop needs two ranks or more"
+    h = n // 2
+    first = full_loop_ring(locals_bits[:h], codec)
+    second = full_loop_ring(locals_bits[h:][::-1], codec)
+    _, rq = decompress_reduce([first, second], codec)
+    return rq
+
+
 def requantize(codec, x_f32, tensor_scale=None):
     """Quantize a caller-supplied float32 tensor (FP8: taken as transformed values)."""
     x = np.asarray(x_f32, dtype=np.float32)

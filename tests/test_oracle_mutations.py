@@ -173,3 +173,84 @@ def test_e5m2_exponent_with_the_e4m3_limit_is_caught(monkeypatch):
     real = cd.block_exponent
     monkeypatch.setattr(cd, "block_exponent", lambda m, *f: real(m))
     assert _fails(TC.test_block_exponent_e5m2_bruteforce_and_range)
+
+
+# ---------------------------------------------- metrics and tensor scales --
+import oracle  # noqa: E402
+import tests.test_oracle_ring as TR  # noqa: E402
+import tests.test_oracle_scales_metrics as TS  # noqa: E402
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("mse", lambda a, b: float(np.sum((np.asarray(a, np.float64) - np.asarray(b, np.float64)) ** 2))),
+    ("rel_mse", lambda a, b: float(np.mean((np.asarray(a, np.float64) - np.asarray(b, np.float64)) ** 2))
+     / float(np.sum(np.asarray(b, np.float64) ** 2))),
+    ("rel_l2", lambda a, b: float(np.sum((np.asarray(a, np.float64) - np.asarray(b, np.float64)) ** 2))
+     / float(np.sum(np.asarray(b, np.float64) ** 2))),                        # no square roots
+    ("rel_l2", lambda a, b: float(np.linalg.norm(np.asarray(a, np.float64) - np.asarray(b, np.float64)))
+     / float(np.linalg.norm(np.asarray(a, np.float64)))),                     # the other reference
+], ids=["mse-sum", "rel_mse-mean", "rel_l2-no-sqrt", "rel_l2-swapped"])
+def test_metric_mistakes_are_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(oracle, name, bad)
+    assert _fails(TS.test_metrics_golden)
+
+
+def _auto_scale_variant(absfn=np.abs, M=None, clamp=True):
+    def f(y, fmt=cd.FP8_DUAL):
+        y = np.asarray(y, np.float32)
+        A = np.max(absfn(y)) if y.size else np.float32(0)
+        if A == 0:
+            return np.float32(1.0)
+        g = np.float32(A) / np.float32(M if M is not None else cd.FP8_MAX[fmt])
+        return np.float32(min(max(g, cd.G_MIN), cd.G_MAX)) if clamp else np.float32(g)
+    return f
+
+
+@pytest.mark.parametrize("bad", [
+    _auto_scale_variant(absfn=lambda y: y),          # signed maximum instead of the abs-max
+    _auto_scale_variant(M=447.0),                    # wrong constant
+    _auto_scale_variant(M=448.0),                    # the E4M3 constant for both formats
+], ids=["signed-max", "M-447", "M-448-for-e5m2"])
+def test_auto_tensor_scale_mistakes_are_caught(monkeypatch, bad):
+    monkeypatch.setattr(cd, "auto_tensor_scale", bad)
+    caught = _fails(TS.test_auto_tensor_scale_is_the_nearest_float_to_transformed_absmax_over_M, cd.FP8_DUAL, 448) \
+        or _fails(TS.test_auto_tensor_scale_is_the_nearest_float_to_transformed_absmax_over_M, cd.FP8E5_DUAL, 57344)
+    assert caught
+
+
+def test_auto_scale_from_untransformed_values_is_caught(monkeypatch):
+    real = cd.quantize_values
+
+    def bad(codec, y, rows, cols, tensor_scale=None):
+        if codec.format in cd.FP8_FORMATS and tensor_scale is None:
+            # the abs-max of the inverse-transformed values (the input domain)
+            x = hd.fwht(np.asarray(y, np.float32).reshape(-1), codec.block) / np.float32(codec.block)
+            tensor_scale = cd.auto_tensor_scale(x, codec.format)
+        return real(codec, y, rows, cols, tensor_scale)
+    monkeypatch.setattr(cd, "quantize_values", bad)
+    assert _fails(TS.test_auto_tensor_scale_is_the_nearest_float_to_transformed_absmax_over_M, cd.FP8_DUAL, 448)
+
+
+def test_missing_tensor_scale_clamp_is_caught(monkeypatch):
+    monkeypatch.setattr(cd, "auto_tensor_scale", _auto_scale_variant(clamp=False))
+    assert _fails(TS.test_tensor_scale_clamps, cd.FP8_DUAL)
+
+
+@pytest.mark.parametrize("bad", [
+    lambda gs: np.float32(min(max(np.float32(sum(float(g) for g in gs)), cd.G_MIN), cd.G_MAX)),   # float64 sum
+    lambda gs: np.float32(sum(np.float32(g) for g in gs)),                                          # no clamp
+], ids=["f64-sum", "no-clamp"])
+def test_gather_scale_mistakes_are_caught(monkeypatch, bad):
+    monkeypatch.setattr(cd, "sum_tensor_scales", bad)
+    assert _fails(TS.test_gather_scale_sum_order_and_clamps)
+
+
+@pytest.mark.parametrize("bad", [
+    lambda xs, codec: cd.full_loop_ring(xs, codec),                                                # no second direction
+    lambda xs, codec: cd.decompress_reduce([cd.full_loop_ring(xs[:len(xs) // 2], codec),
+                                            cd.full_loop_ring(xs[len(xs) // 2 + 1:][::-1], codec)],
+                                           codec)[1],                                              # a rank dropped
+], ids=["full-loop", "dropped-rank"])
+def test_semi_loop_mistakes_are_caught(monkeypatch, bad):
+    monkeypatch.setattr(oracle, "semi_loop_ring", bad)
+    assert _fails(TR.test_semi_loop_ring_error_statistics)

@@ -1,6 +1,8 @@
-"""Pins of the oracle's ring hop ([EQuARX] "What carries the argument": a
-received shard is dequantized to FP32, the local contribution added, and the
-partial sum quantized again for the next hop; full-loop ring of N - 1 hops).
+"""Pins of the oracle's ring hop and rings ([EQuARX] "What carries the
+argument": a received shard is dequantized to FP32, the local contribution
+added, and the partial sum quantized again for the next hop; the full-loop
+ring takes N - 1 hops, the semi-loop ring uses both directions to halve the
+number of quantization hops).
 
 The hop is one float32 add between two already pinned steps, so it is pinned
 by the cases that reduce to them, by an exact case checked against float64
@@ -100,11 +102,12 @@ def test_full_loop_ring_error_statistics():
 
 
 def test_ring_mse_matches_the_reported_values():
-    # The pages' MSE for the full-loop ring and for all-gather-only
-    # quantization (tests/golden/equarx_ring_mse.txt), reproduced within 25 %
-    # by 8 ranks of N(0, 1) data.
+    # The pages' MSE for the full-loop ring, the semi-loop ring and for
+    # all-gather-only quantization (tests/golden/equarx_ring_mse.txt),
+    # reproduced within 25 % by 8 ranks of N(0, 1) data.
     from tests.conftest import read_golden
     want = {k: float(v) for k, v in read_golden("equarx_ring_mse.txt")}
+    assert set(want) == {"full-loop", "semi-loop", "ag-only"}
     N, shape = 8, (64, 1024)
     codec = cd.Codec(cd.INT8_SYM, 64, False)
     xs = [bits(shape, 300 + r) for r in range(N)]
@@ -113,7 +116,48 @@ def test_ring_mse_matches_the_reported_values():
     for r in range(N):
         _, q = oracle.ring_hop(q, xs[r], codec, in_codec=codec)
     ring = oracle.dequantize(q).reshape(shape).astype(np.float64)
+    semi = oracle.dequantize(oracle.semi_loop_ring(xs, codec)).reshape(shape).astype(np.float64)
     once = oracle.dequantize(oracle.requantize(codec, exact.astype(np.float32))).reshape(shape)
-    got = {"full-loop": float(((ring - exact) ** 2).mean()), "ag-only": float(((once - exact) ** 2).mean())}
+    got = {"full-loop": float(((ring - exact) ** 2).mean()), "semi-loop": float(((semi - exact) ** 2).mean()),
+           "ag-only": float(((once - exact) ** 2).mean())}
     for k in want:
         assert abs(got[k] - want[k]) < 0.25 * want[k], (k, got[k], want[k])
+
+
+@pytest.mark.parametrize("codec", [cd.Codec(cd.INT8_SYM, 64, False), cd.Codec(cd.INT8_ASYM, 128, False)],
+                         ids=["i8s", "i8a"])
+def test_full_loop_ring_is_the_chain_of_hops(codec):
+    xs = [bits((4, 256), 40 + r) for r in range(5)]
+    q = None
+    for x in xs:
+        _, q = oracle.ring_hop(q, x, codec, in_codec=codec)
+    same(oracle.full_loop_ring(xs, codec), q)
+
+
+@pytest.mark.parametrize("codec", [cd.Codec(cd.INT8_SYM, 64, False), cd.Codec(cd.INT8_ASYM, 128, False)],
+                         ids=["i8s", "i8a"])
+def test_two_rank_semi_loop_is_the_reduce_of_both_compressed_shards(codec):
+    # with two ranks each chain is one rank that quantizes its own shard, and
+    # the join is the two-shard decompress-reduce with requantization
+    x0, x1 = bits((4, 256), 50), bits((4, 256), 51)
+    _, want = oracle.decompress_reduce([oracle.compress(codec, x0), oracle.compress(codec, x1)], codec)
+    same(oracle.semi_loop_ring([x0, x1], codec), want)
+
+
+def test_semi_loop_ring_error_statistics():
+    # N = 8 ranks of N(0, 1) data, block-64 INT8. The semi-loop quantizes the
+    # partial sums of 1, 2, 3, 4 addends along each of its two chains and the
+    # whole sum once for the gather (events {1..4} + {1..4} + {8}), the full
+    # loop those of 1, 2, ..., 8: with the closed form of one quantization,
+    # E[A^2] / (12 * 127^2), the semi-loop's MSE is 28/36 of the full loop's.
+    # A dropped or repeated rank would leave an error of the order of one
+    # shard (variance 1); running the full loop instead exceeds the band.
+    N, shape = 8, (64, 1024)
+    codec = cd.Codec(cd.INT8_SYM, 64, False)
+    xs = [bits(shape, 500 + r) for r in range(N)]
+    exact = sum(bf16_bits_to_f32(x).astype(np.float64) for x in xs)
+    semi = oracle.dequantize(oracle.semi_loop_ring(xs, codec)).reshape(shape).astype(np.float64)
+    mse = float(((semi - exact) ** 2).mean())
+    step = 12 * 127 ** 2
+    want = (2 * sum(block_absmax_sq(i) for i in range(1, 5)) + block_absmax_sq(N)) / step
+    assert 0.9 * want < mse < 1.1 * want, (mse, want)
