@@ -383,14 +383,15 @@ TACO_DEV void dequant_lane(const LaneIn<FMT, B>& in, float* d) {
 // left in bits 4-8 of their half, 16 c * 2^-24) exactly, and one mixed-
 // precision fused multiply-add per value forms (q - z) * s = c * s - 16 s
 // with a single rounding: c * 2^-24 * (s * 2^24) is the exact product and
-// 16 s is exact. Valid when every zero point is at most 15 and |s| < 2^100
-// (s * 2^24 finite); int4_fast_ok tells.
+// 16 s is exact. Valid when every zero point is at most 15 (what the
+// compressor writes, and a stated precondition for buffers read back) and
+// |s| < 2^100 (s * 2^24 finite); int4_fast_ok tells the latter.
 TACO_DEV float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 TACO_DEV float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 template <int B>
 TACO_DEV bool int4_fast_ok(const LaneIn<kINT4A, B>& in) {
-  return fabsf(in.s) < 0x1p100f && in.z <= 15u;
+  return fabsf(in.s) < 0x1p100f;
 }
 
 template <int B>
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reduce(ReduceArgs a) {
   // and kept ahead of the arithmetic by a scheduling barrier, before step k is
   // added. The last iteration's look-ahead lies past the end: it loads zeros.
   static_assert(NG >= 2 && NG % 2 == 0, "an even number of steps per tile");
-  int t = (int)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
+  int t = (int)xcd_ordered_block() * (kBlockThreads / kWave) + wave_in_group();
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;

@@ -22,6 +22,21 @@ constexpr int kBlockThreads = 256;
 // Index of this wave in its workgroup, as a wave-uniform (scalar) value.
 TACO_DEV int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x) / kWave; }
 
+// XCD-aware workgroup order. The dispatcher hands workgroup b to XCD b % 8,
+// so consecutive workgroups land on different XCDs, each with its own L2; a
+// 128-byte line of block metadata shared by neighbouring workgroups (one
+// zero-point byte or FP8 exponent byte per block) is then fetched by several
+// L2s. This renumbering gives each XCD one contiguous range of workgroup
+// indices -- XCD x takes [x * q + min(x, r), ...) with q = grid / 8 and
+// r = grid % 8, the first r XCDs one more -- a bijection of [0, grid), so any
+// grid stays correct whatever the dispatcher actually does.
+constexpr unsigned kXcds = 8;
+TACO_DEV unsigned xcd_ordered_block() {
+  const unsigned G = gridDim.x, b = blockIdx.x;
+  const unsigned x = b % kXcds, l = b / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + l;
+}
+
 // Blocks whose abs-max (symmetric) or range (asymmetric) is below this are
 // stored as zero codes with a zero scale, so 127/A and qmax/r stay finite.
 constexpr float kTiny = 0x1p-100f;

@@ -97,6 +97,40 @@ def test_full_loop_ring_matches_oracle_at_every_hop():
     assert 0.00105 < mse < 0.00175
 
 
+@pytest.mark.parametrize("codec", [cd.Codec(cd.INT8_SYM, 64, False), cd.Codec(cd.INT8_ASYM, 128, False)],
+                         ids=["i8s", "i8a"])
+@pytest.mark.parametrize("N", [2, 5, 8])
+def test_semi_loop_ring_matches_oracle_at_every_step(codec, N):
+    # the semi-loop: ranks 0 .. h-1 chain one way, ranks N-1 .. h the other
+    # (taco_ring_hop at every link), and the two partial sums meet in a
+    # two-source taco_decompress_reduce that quantizes for the all-gather
+    shape = (64, 1024)
+    from oracle.formats import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(4321 + N)
+    xs = [f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32)) for _ in range(N)]
+    h = N // 2
+    chains = [list(range(h)), list(range(N - 1, h - 1, -1))]
+    ends = []
+    for ci, chain in enumerate(chains):
+        ref, buf = None, None
+        for r in chain:
+            _, ref = oracle.ring_hop(ref, xs[r], codec, in_codec=codec)
+            _, buf = gpu_hop(codec, codec, buf, upload_bits(xs[r]), shape, want_sum=False)
+            assert_same(parse(buf, codec, *shape), ref, f"chain {ci}, rank {r}")
+        ends.append(buf)
+    c = ccodec(codec)
+    out = T.empty_compressed(c, *shape, DEV)
+    T.taco_decompress_reduce(c, ends, *shape, None, c, out)
+    torch.cuda.synchronize()
+    want = oracle.semi_loop_ring(xs, codec)
+    assert_same(parse(out, codec, *shape), want, "join")
+    if N == 8 and codec.format == cd.INT8_SYM:
+        exact = sum(bf16_bits_to_f32(x).astype(np.float64) for x in xs)
+        mse = float(((oracle.dequantize(want).reshape(shape) - exact) ** 2).mean())
+        print(f"[ring] 8-rank semi-loop INT8 block-64 MSE {mse:.3e} (EQuARX page: 0.001)", flush=True)
+        assert 0.00075 < mse < 0.00125
+
+
 def test_full_size_hop_sampled_rows():
     # the equarx shape (8192 x 5120): whole tensors through the GPU, the oracle on
     # sampled row chunks, bit for bit
