@@ -865,40 +865,57 @@ def measure_ring(w, xs, stream, K):
             "ring_codec_in": "INT8 (gather codec)"}
 
 
-def measure_overlap(w, step_fn, nsets, stream, codec_ms, K):
+def measure_overlap(w, step_fn, nsets, stream, K, caps=(0, 1024, 512, 256, 128, 64)):
     """The bf16 GEMM [rows, cols] x [cols, cols] that produces the next activation,
     alone and concurrently with the codec step on a second stream (default
-    priority). Reported: GEMM alone, codec alone (the timed step), both together,
-    and how much of the shorter one the overlap hid."""
+    priority), with the codec's launches capped at each of `caps` workgroups
+    (taco_set_launch_limit; 0 = uncapped). Per cap: the codec step alone, both
+    together, and the fraction of the shorter of the two that the overlap hid."""
     import torch
+    import quantized_compression_tensor_amd as T
     g_stream = torch.cuda.Stream()
     a = torch.randn(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
     b = torch.randn(w.cols, w.cols, dtype=torch.bfloat16, device="cuda")
     c = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
-    with torch.cuda.stream(g_stream):
-        for _ in range(3):
-            torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(g_stream):
-        for _ in range(K):
-            torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    gemm_ms = (time.perf_counter() - t0) * 1e3 / K
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    def gemm(i):
         with torch.cuda.stream(g_stream):
             torch.matmul(a, b, out=c)
+
+    def codec(i):
         with torch.cuda.stream(stream):
             step_fn(i % nsets)
-    torch.cuda.synchronize()
-    both_ms = (time.perf_counter() - t0) * 1e3 / K
+
+    def both(i):
+        gemm(i)
+        codec(i)
+
+    for _ in range(3):
+        gemm(0)
+    gemm_ms = timed(gemm)
     flops = 2.0 * w.rows * w.cols * w.cols
-    serial = gemm_ms + codec_ms
-    return {"gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(flops / gemm_ms / 1e9, 1),
-            "codec_ms": round(codec_ms, 4), "both_ms": round(both_ms, 4), "serial_ms": round(serial, 4),
-            "hidden_frac": round((serial - both_ms) / min(gemm_ms, codec_ms), 3)}
+    rows = []
+    for cap in caps:
+        with T.launch_limit(cap):
+            for i in range(3):
+                codec(i)
+            codec_ms = timed(codec)
+            both_ms = timed(both)
+        serial = gemm_ms + codec_ms
+        rows.append({"codec_workgroup_cap": cap, "codec_ms": round(codec_ms, 4), "both_ms": round(both_ms, 4),
+                     "serial_ms": round(serial, 4),
+                     "hidden_frac": round((serial - both_ms) / min(gemm_ms, codec_ms), 3)})
+    best = min(rows, key=lambda r: r["both_ms"])
+    return {"gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(flops / gemm_ms / 1e9, 1), "by_cap": rows,
+            "best": best}
 
 
 def main():
@@ -953,7 +970,7 @@ def main():
     overlap = None
     if args.overlap:
         overlap = measure_overlap(w, step_fn=ex["step"], nsets=ex["ctx"]["nsets"], stream=ex["stream"],
-                                  codec_ms=ex["ms_step"], K=max(5, args.steps // 5))
+                                  K=max(10, args.steps // 2))
     del ex
     torch.cuda.empty_cache()
 

@@ -225,6 +225,20 @@ int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, vo
 int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
+/* Cap on the workgroups of every later launch made by the calling host
+ * thread (0 = no cap, the default): lets the codec share the GPU with a
+ * concurrent kernel, e.g. the GEMM that produces the next activation on
+ * another stream ([TACO] abstract: the compression operator is built so that
+ * it overlaps with other work). Each kernel walks its tiles with a stride of
+ * its grid, so the results are the same under any cap; only the speed and the
+ * share of the GPU change. Applies to taco_compress, taco_compress_noalloc,
+ * taco_compress_debug, taco_requantize, taco_decompress_reduce,
+ * taco_ring_hop and taco_decompress; not to the encoder test hooks.
+ *   max_workgroups  >= 0 (256 threads each); negative is TACO_ERR_INVALID_ARG
+ *   previous        nullable; receives the cap that was in force
+ * Host only; the setting is per host thread. */
+int taco_set_launch_limit(int32_t max_workgroups, int32_t* previous);
+
 /* Name of a status code. Host only; never returns NULL. */
 const char* taco_status_string(int status);
 

@@ -39,6 +39,7 @@ EXPORTS = (
     "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
     "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
     "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string", "taco_compress_noalloc",
+    "taco_set_launch_limit",
 )
 
 
@@ -94,6 +95,7 @@ def _load():
         "taco_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
         "taco_e5m2_encode": (ctypes.c_int, [P, P, I64, P]),
         "taco_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "taco_set_launch_limit": (ctypes.c_int, [I32, ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -153,6 +155,30 @@ def taco_compressed_bytes(c, rows, cols):
 
 def taco_workspace_bytes(c, rows, cols):
     return _lib.taco_workspace_bytes(c, rows, cols)
+
+
+def taco_set_launch_limit(max_workgroups):
+    """Cap the workgroups of every later launch from this host thread (0 = no
+    cap); returns the cap that was in force."""
+    prev = ctypes.c_int32(0)
+    _check(_lib.taco_set_launch_limit(int(max_workgroups), ctypes.byref(prev)), "taco_set_launch_limit")
+    return prev.value
+
+
+class launch_limit:
+    """Context manager: ``with launch_limit(k): ...`` runs the block's calls on
+    grids of at most k workgroups and restores the previous cap after."""
+
+    def __init__(self, max_workgroups):
+        self.k = max_workgroups
+
+    def __enter__(self):
+        self.prev = taco_set_launch_limit(self.k)
+        return self
+
+    def __exit__(self, *exc):
+        taco_set_launch_limit(self.prev)
+        return False
 
 
 # ------------------------------------------------------------ device ops --

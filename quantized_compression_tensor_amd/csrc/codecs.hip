@@ -636,9 +636,10 @@ struct DequantK {
   void* out;
 };
 
-// Decode to float32 or bf16: one 1024-element tile per wave in the two-half
-// lane layout of k_quantize (8 consecutive elements of each half per lane).
-// The output uses ordinary stores: the consumer reads it next.
+// Decode to float32 or bf16: 1024-element tiles in the two-half lane layout of
+// k_quantize (8 consecutive elements of each half per lane), one per wave as
+// launched (a smaller grid walks them with a stride of the grid). The output
+// uses ordinary stores: the consumer reads it next.
 template <int FMT, int B, bool BF16OUT>
 __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   constexpr int V = 8;
@@ -649,16 +650,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   constexpr bool ASYM = FMT == kINT4A || FMT == kINT8A;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t ntiles = (a.n + kWaveElems - 1) / kWaveElems;
-  const int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group();
-  if (t >= ntiles) return;
+  const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  float g = 0.0f;
+  if constexpr (is_fp8(FMT)) g = *a.g_hdr;
+  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
   const int64_t base = t * kWaveElems;
   const int rt = t == ntiles - 1 ? (int)(a.n - base) : kWaveElems;   // a multiple of B
   const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
   const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
   const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
   const rsrc_t ro = make_rsrc32(static_cast<uint8_t*>(a.out) + base * (BF16OUT ? 2 : 4), rt * (BF16OUT ? 2 : 4));
-  float g = 0.0f;
-  if constexpr (is_fp8(FMT)) g = *a.g_hdr;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     LaneIn<FMT, B> in;
@@ -689,6 +690,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
                                 __float_as_uint(d[4 * q + 3])),
                      ro, lane * 32 + 16 * q, h * HALF * 4);
     }
+  }
   }
 }
 
@@ -1021,7 +1023,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_encode(const float* x, ui
 
 static dim3 grid_for(int64_t n) {
   const int64_t tiles = (n + kWaveElems - 1) / kWaveElems;
-  return dim3((unsigned)((tiles + 3) / 4));
+  return capped_grid((tiles + 3) / 4);
 }
 
 // One wave per tile and as many workgroups as that takes: the hardware keeps
@@ -1124,7 +1126,7 @@ template <int FIN, int BIN, int FOUT, int BOUT, int NMAX>
 static void launch_r(const ReduceArgs& a, hipStream_t s) {
   const int64_t tiles = (a.n + kWaveElems - 1) / kWaveElems;
   const int64_t per_group = 4 * kReduceTilesPerWave;
-  dim3 grid((unsigned)((tiles + per_group - 1) / per_group)), block(kBlockThreads);
+  dim3 grid = capped_grid((tiles + per_group - 1) / per_group), block(kBlockThreads);
   hipLaunchKernelGGL((k_reduce<FIN, BIN, FOUT, BOUT, NMAX>), grid, block, 0, s, a);
 }
 

@@ -368,7 +368,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
 //
 // Consumer side: dequantize (dec(q) * g * 2^-k, the combined scale is exact),
 // inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
-// factor, then float32 or bf16 output.
+// factor, then float32 or bf16 output. T wave tiles per wave as launched; a
+// smaller grid walks them with a stride of the grid.
 template <int LOGB, bool E5, bool BF16OUT, int T>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
@@ -380,7 +381,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
   const int row = lane / Gm::G;
   const float g = *g_hdr;
   const float outscale = pow2f(-LOGB) * ls.parity;
-  const int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T;
+  const int64_t ntiles = ((nblocks << LOGB) + kTileElems - 1) / kTileElems;
+  for (int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T; tile0 < ntiles; tile0 += (int64_t)gridDim.x * 4 * T) {
   uint2 raw[T];
   int kk[T];
 #pragma unroll
@@ -422,6 +424,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
       }
     }
   }
+  }
 }
 
 // ------------------------------------------------------------ launchers --
@@ -460,14 +463,14 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
   if (a.auto_prepass)
-    hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), dim3((unsigned)had_groups(LOGB, a.nblocks, kChunkTiles)), block, 0,
+    hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles)), block, 0,
                        s, x, a.nblocks, ws);
   if (small) {
     const int64_t need = had_groups(LOGB, a.nblocks, kSmallChunkTiles);
     const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
-    launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, dim3((unsigned)(need < cap ? need : cap)), s);
+    launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, capped_grid(need < cap ? need : cap), s);
   } else {
-    const dim3 grid((unsigned)had_groups(LOGB, a.nblocks, kChunkTiles));
+    const dim3 grid = capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles));
     if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, grid, s);   // test hook: the large chunks
     else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, grid, s);
   }
@@ -505,7 +508,7 @@ template <int LOGB>
 static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
   const int64_t groups = had_groups(LOGB, a.nblocks, 2);
   if (groups == 0) return hipSuccess;
-  const dim3 grid((unsigned)groups);
+  const dim3 grid = capped_grid(groups);
   if (a.e5) launch_decode_fmt<LOGB, true>(a, grid, s);
   else launch_decode_fmt<LOGB, false>(a, grid, s);
   return hipGetLastError();

@@ -193,6 +193,9 @@ int scratch_workspace(hipStream_t stream, void** ws) {
 
 namespace taco {
 
+thread_local int32_t t_launch_limit = 0;
+int launch_limit() { return t_launch_limit; }
+
 int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -401,6 +404,13 @@ int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stre
 
 int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
   return fp8_encode(true, x, codes, n, stream);
+}
+
+int taco_set_launch_limit(int32_t max_workgroups, int32_t* previous) {
+  if (max_workgroups < 0) return TACO_ERR_INVALID_ARG;
+  if (previous != nullptr) *previous = taco::t_launch_limit;
+  taco::t_launch_limit = max_workgroups;
+  return TACO_OK;
 }
 
 const char* taco_status_string(int status) {

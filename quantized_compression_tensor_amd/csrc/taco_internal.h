@@ -121,6 +121,16 @@ static_assert(4 * kReducePiece < (int64_t(1) << 31), "a piece's float32 sum must
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
+
+// Workgroup cap of the calling host thread (taco_set_launch_limit; 0 = none)
+// and a grid of `groups` workgroups under it. Every kernel it is applied to
+// walks its work with a stride of the whole grid, so any grid gives the same
+// results.
+int launch_limit();
+inline dim3 capped_grid(int64_t groups) {
+  const int lim = launch_limit();
+  return dim3((unsigned)(lim > 0 && groups > lim ? lim : groups));
+}
 // Workgroups per CU (4 waves each) of the persistent FP8 compress of small
 // tensors.
 #ifndef TACO_GROUPS_PER_CU

@@ -184,6 +184,21 @@ def test_other_entry_points_validation():
     assert _st(T.taco_e5m2_encode, A, B_, 0) == 0
 
 
+def test_launch_limit_is_per_thread_and_restorable():
+    import threading
+    assert T.taco_set_launch_limit(0) == 0
+    assert _st(T.taco_set_launch_limit, -1) == T.TACO_ERR_INVALID_ARG
+    assert T.taco_set_launch_limit(7) == 0
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(T.taco_set_launch_limit(3)))
+    th.start()
+    th.join()
+    assert seen == [0]                       # another thread starts without a cap
+    with T.launch_limit(64):
+        assert T.taco_set_launch_limit(64) == 64
+    assert T.taco_set_launch_limit(0) == 7   # the context manager restored 7
+
+
 def test_one_hip_runtime_in_the_process():
     """The binding must leave exactly one HIP runtime mapped (torch's), whatever
     was imported first: a second runtime cannot use torch's streams or memory."""
