@@ -79,6 +79,11 @@ from .codecs import (  # noqa: F401
     semi_loop_ring,
     requantize,
     decode,
+    chunk_order,
+    reorder_columns,
+    restore_columns,
+    compress_reordered,
+    decode_reordered,
     auto_tensor_scale,
     sum_tensor_scales,
 )

@@ -446,6 +446,67 @@ def semi_loop_ring(locals_bits, codec: Codec):
     return rq
 
 
+# ------------------------------------------------ data-driven reshaping -----
+
+CHUNK = 8   # channels per reordered group (the kernels move 16-byte bf16 vectors)
+
+
+def chunk_order(stats_bits):
+    """Data-driven reshaping of the hidden dimension ([TACO] abstract and
+    "What carries the argument": the tensor is reshaped adaptively, from the
+    data, before the Adaptive Scale-Hadamard Transform; the page does not say
+    how). Reading: the hidden channels are taken in groups of CHUNK = 8
+    consecutive channels; each group's statistic is its largest magnitude over
+    every row of a statistics tensor (e.g. an earlier step's activation, the
+    same on every rank); the groups are ordered by that statistic, largest
+    first, equal statistics by group index, so that the blocks of the reordered
+    tensor hold channels of similar magnitude.
+
+    Returns order (int64 [cols / 8]): reordered group j is original group
+    order[j]."""
+    x = bf16_bits_to_f32(np.asarray(stats_bits, dtype=np.uint16))
+    rows, cols = x.shape
+    assert cols % CHUNK == 0
+    m = np.max(np.abs(x), axis=0) if rows else np.zeros(cols, np.float32)
+    g = np.max(m.reshape(-1, CHUNK), axis=1)
+    g = np.where(np.isnan(g), np.float32(np.inf), g)   # reading: a NaN group sorts as the largest
+    return np.lexsort((np.arange(g.size), -g.astype(np.float64))).astype(np.int64)
+
+
+def _column_map(order, cols):
+    order = np.asarray(order, dtype=np.int64)
+    assert order.size * CHUNK == cols and np.array_equal(np.sort(order), np.arange(order.size)), \
+        "order must be a permutation of the channel groups"
+    return (order[:, None] * CHUNK + np.arange(CHUNK)[None, :]).reshape(-1)
+
+
+def reorder_columns(x, order):
+    """Columns of a [rows, cols] array in reordered form: reordered column
+    8 j + i is original column 8 order[j] + i."""
+    x = np.asarray(x)
+    return x[:, _column_map(order, x.shape[1])]
+
+
+def restore_columns(y, order):
+    """Inverse of reorder_columns."""
+    y = np.asarray(y)
+    out = np.empty_like(y)
+    out[:, _column_map(order, y.shape[1])] = y
+    return out
+
+
+def compress_reordered(codec, x_bits, order, tensor_scale=None):
+    """compress() of the reordered tensor: the codec sees the channel groups in
+    the data-driven order (the compressed buffer, the reduce and the
+    requantization all work in that order)."""
+    return compress(codec, reorder_columns(np.asarray(x_bits, dtype=np.uint16), order), tensor_scale)
+
+
+def decode_reordered(c, order, out_dtype="f32"):
+    """decode() followed by the inverse reordering of the channels."""
+    return restore_columns(decode(c, out_dtype), order)
+
+
 def requantize(codec, x_f32, tensor_scale=None):
     """Quantize a caller-supplied float32 tensor (FP8: taken as transformed values)."""
     x = np.asarray(x_f32, dtype=np.float32)

@@ -254,3 +254,29 @@ def test_gather_scale_mistakes_are_caught(monkeypatch, bad):
 def test_semi_loop_mistakes_are_caught(monkeypatch, bad):
     monkeypatch.setattr(oracle, "semi_loop_ring", bad)
     assert _fails(TR.test_semi_loop_ring_error_statistics)
+
+
+# ---------------------------------------------------- data-driven reshaping --
+import tests.test_oracle_reorder as TO  # noqa: E402
+
+
+def _order_variant(desc=True, ties_by_index=True, chunk=8):
+    def f(stats_bits):
+        x = fm.bf16_bits_to_f32(np.asarray(stats_bits, dtype=np.uint16))
+        g = np.max(np.abs(x), axis=0).reshape(-1, chunk).max(axis=1).astype(np.float64)
+        idx = np.arange(g.size) if ties_by_index else -np.arange(g.size)
+        return np.lexsort((idx, -g if desc else g)).astype(np.int64)
+    return f
+
+
+@pytest.mark.parametrize("bad", [_order_variant(desc=False), _order_variant(ties_by_index=False),
+                                 _order_variant(chunk=16)], ids=["ascending", "ties-reversed", "groups-of-16"])
+def test_order_mistakes_are_caught(monkeypatch, bad):
+    monkeypatch.setattr(oracle, "chunk_order", bad)
+    assert _fails(TO.test_hand_worked_order) or any(_fails(TO.test_order_matches_a_brute_force_sort, s)
+                                                    for s in range(4))
+
+
+def test_restore_with_the_order_itself_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "restore_columns", lambda y, order: oracle.reorder_columns(y, order))
+    assert _fails(TO.test_reorder_and_restore_are_inverse_permutations)
