@@ -225,6 +225,38 @@ int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, vo
 int taco_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
+/* ---- data-driven reshaping ------------------------------------------------
+ * [TACO] abstract and "What carries the argument": the tensor is reshaped
+ * adaptively, from the data, before the ASH transform (the rule is not given).
+ * Here: the hidden channels are taken in groups of 8 consecutive channels and
+ * the codec sees the groups in an order computed from a statistics tensor
+ * (e.g. an earlier step's activation; every rank must use the same order):
+ * largest magnitude first, equal magnitudes by group index, so that each
+ * block holds channels of similar magnitude. `order` is a device int32 array
+ * of cols / 8 entries, reordered group j being original group order[j] of the
+ * same row; it must be a permutation of [0, cols / 8) (other values are
+ * clamped into range: no fault, unspecified codes). Shapes: cols a multiple
+ * of 512 and at most 131072, FP8 block 128 (TACO_ERR_SHAPE otherwise).
+ * Compressed buffers, decompress-reduce, requantize and the ring hop work on
+ * the reordered tensor unchanged; taco_decompress_reordered restores the
+ * original channel order. */
+
+/* The order of the groups of a statistics tensor (device bf16 [rows, cols];
+ * rows may be 0: identity order) into `order` (device int32 [cols / 8]).
+ * Three launches on `stream`; `order` is their only memory. */
+int taco_chunk_order(const void* stats_bf16, int64_t rows, int64_t cols, int32_t* order, hipStream_t stream);
+
+/* taco_compress of the reordered tensor: column 8 j + i of the tensor the
+ * codec sees is column 8 order[j] + i of x_bf16 (same row). Arguments and
+ * errors as taco_compress, plus `order` (device, 16-byte aligned). */
+int taco_compress_reordered(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale,
+                            void* out, void* workspace, size_t ws_bytes, const int32_t* order, hipStream_t stream);
+
+/* taco_decompress of a buffer holding a reordered tensor, writing each
+ * decoded group j to original group order[j] of its row. */
+int taco_decompress_reordered(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                              const int32_t* order, hipStream_t stream);
+
 /* Cap on the workgroups of every later launch made by the calling host
  * thread (0 = no cap, the default): lets the codec share the GPU with a
  * concurrent kernel, e.g. the GEMM that produces the next activation on
@@ -232,8 +264,10 @@ int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stre
  * it overlaps with other work). Each kernel walks its tiles with a stride of
  * its grid, so the results are the same under any cap; only the speed and the
  * share of the GPU change. Applies to taco_compress, taco_compress_noalloc,
- * taco_compress_debug, taco_requantize, taco_decompress_reduce,
- * taco_ring_hop and taco_decompress; not to the encoder test hooks.
+ * taco_compress_debug, taco_compress_reordered, taco_requantize,
+ * taco_decompress_reduce, taco_ring_hop, taco_decompress and
+ * taco_decompress_reordered; not to taco_chunk_order or the encoder test
+ * hooks.
  *   max_workgroups  >= 0 (256 threads each); negative is TACO_ERR_INVALID_ARG
  *   previous        nullable; receives the cap that was in force
  * Host only; the setting is per host thread. */

@@ -39,7 +39,7 @@ EXPORTS = (
     "taco_layout", "taco_compressed_bytes", "taco_workspace_bytes", "taco_compress",
     "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
     "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string", "taco_compress_noalloc",
-    "taco_set_launch_limit",
+    "taco_set_launch_limit", "taco_chunk_order", "taco_compress_reordered", "taco_decompress_reordered",
 )
 
 
@@ -96,6 +96,9 @@ def _load():
         "taco_e5m2_encode": (ctypes.c_int, [P, P, I64, P]),
         "taco_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "taco_set_launch_limit": (ctypes.c_int, [I32, ctypes.POINTER(I32)]),
+        "taco_chunk_order": (ctypes.c_int, [P, I64, I64, P, P]),
+        "taco_compress_reordered": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P, P]),
+        "taco_decompress_reordered": (ctypes.c_int, [C, P, I64, I64, P, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -225,6 +228,24 @@ def taco_requantize(c_out, x_fp32, rows, cols, tensor_scale, out, workspace=None
 def taco_decompress(c, inp, rows, cols, out, out_dtype=0, stream=None):
     return _check(_lib.taco_decompress(c, _ptr(inp), rows, cols, _ptr(out), int(out_dtype), _stream(stream)),
                   "taco_decompress")
+
+
+def taco_chunk_order(stats_bf16, rows, cols, order, stream=None):
+    return _check(_lib.taco_chunk_order(_ptr(stats_bf16), rows, cols, _ptr(order), _stream(stream)),
+                  "taco_chunk_order")
+
+
+def taco_compress_reordered(c, x_bf16, rows, cols, tensor_scale, out, order, workspace=None, ws_bytes=None,
+                            stream=None):
+    wsb = ws_bytes if ws_bytes is not None else (TACO_WORKSPACE_BYTES if workspace is not None else 0)
+    return _check(_lib.taco_compress_reordered(c, _ptr(x_bf16), rows, cols, float(tensor_scale), _ptr(out),
+                                               _ptr(workspace), wsb, _ptr(order), _stream(stream)),
+                  "taco_compress_reordered")
+
+
+def taco_decompress_reordered(c, inp, rows, cols, out, order, out_dtype=0, stream=None):
+    return _check(_lib.taco_decompress_reordered(c, _ptr(inp), rows, cols, _ptr(out), int(out_dtype), _ptr(order),
+                                                 _stream(stream)), "taco_decompress_reordered")
 
 
 def taco_e4m3_encode(x, codes, n, stream=None):

@@ -427,6 +427,7 @@ struct QuantK {
   int g_from_ws;
   Workspace* ws;
   float* dbg;
+  ReorderArgs ro;
 };
 
 // Store one lane's codes (streaming stores, as for the buffer stores); the
@@ -490,8 +491,11 @@ TACO_DEV void quant_halves(float (*v)[8], float inv_g, float (*pre)[8], LaneCode
 // tensor's end (a ragged tail loads zeros and its stores are dropped). The
 // launch gives every wave one tile and relies on full occupancy for the loads
 // in flight; the loop only matters for grids smaller than that.
-template <int FMT, int B, bool F32IN, bool DEBUG>
+template <int FMT, int B, bool F32IN, bool DEBUG, bool REORD = false>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
+  static_assert(!(REORD && (F32IN || DEBUG)), "the reordering compress takes bf16 input");
+  extern __shared__ int16_t lds_order[];
+  if constexpr (REORD) load_order_lds(a.ro, lds_order);
   constexpr int V = 8;                      // elements per lane and half
   constexpr int HALF = kWaveElems / 2;      // 512
   constexpr int ES = F32IN ? 4 : 2;         // input bytes per element
@@ -534,10 +538,26 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
     const int rt = t == ntiles - 1 ? tail : kWaveElems;   // elements of this tile
     const rsrc_t rx = make_rsrc32(static_cast<const uint8_t*>(a.x) + base * ES, rt * ES);
     uint4 raw[2][NQ];
+    if constexpr (REORD) {
+      // each half is one 512-element span of a row; the lane holding group j
+      // of it loads group order[j] of that row
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        // the second half of a ragged last tile lies past the end: empty
+        // resource, no lookup
+        const int64_t e0 = base + h * HALF;
+        const bool live = e0 < a.n;
+        const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
+        const rsrc_t rr = make_rsrc32(static_cast<const uint16_t*>(a.x) + (int64_t)p.row * a.ro.cols,
+                                      live ? a.ro.cols * 2 : 0);
+        raw[h][0] = bload128<kNT>(rr, live ? reordered_group(lds_order, p, lane) * kGroupElems * 2 : 0, 0);
+      }
+    } else {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) raw[h][q] = bload128<kNT>(rx, lane * V * ES + 16 * q, h * HALF * ES);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) raw[h][q] = bload128<kNT>(rx, lane * V * ES + 16 * q, h * HALF * ES);
+    }
     float v[2][V];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -634,14 +654,17 @@ struct DequantK {
   const float* g_hdr;
   int64_t n;
   void* out;
+  ReorderArgs ro;
 };
 
 // Decode to float32 or bf16: 1024-element tiles in the two-half lane layout of
 // k_quantize (8 consecutive elements of each half per lane), one per wave as
 // launched (a smaller grid walks them with a stride of the grid). The output
 // uses ordinary stores: the consumer reads it next.
-template <int FMT, int B, bool BF16OUT>
+template <int FMT, int B, bool BF16OUT, bool REORD = false>
 __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
+  extern __shared__ int16_t lds_order[];
+  if constexpr (REORD) load_order_lds(a.ro, lds_order);
   constexpr int V = 8;
   constexpr int HALF = kWaveElems / 2;
   constexpr int G = B / V, BPH = HALF / B;
@@ -659,7 +682,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
   const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
   const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
-  const rsrc_t ro = make_rsrc32(static_cast<uint8_t*>(a.out) + base * (BF16OUT ? 2 : 4), rt * (BF16OUT ? 2 : 4));
+  const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + base * (BF16OUT ? 2 : 4), rt * (BF16OUT ? 2 : 4));
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     LaneIn<FMT, B> in;
@@ -679,16 +702,29 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
     }
     float d[V];
     dequant_lane<FMT, B, V>(in, d);
+    // output resource and this lane's offset in it: the tile, or (reordered)
+    // the row of this half's span, where group j goes back to group order[j]
+    constexpr int OB = BF16OUT ? 2 : 4;   // output bytes per element
+    rsrc_t rdst = rout;
+    int doff = lane * V * OB, dsoff = h * HALF * OB;
+    if constexpr (REORD) {
+      const int64_t e0 = base + h * HALF;
+      const bool live = e0 < a.n;   // else: the empty half of a ragged last tile
+      const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
+      rdst = make_rsrc32(static_cast<uint8_t*>(a.out) + ((int64_t)p.row * a.ro.cols) * OB, live ? a.ro.cols * OB : 0);
+      doff = live ? reordered_group(lds_order, p, lane) * kGroupElems * OB : 0;
+      dsoff = 0;
+    }
     if constexpr (BF16OUT) {
       bstore128<0>(make_uint4(f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16), f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16),
                               f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16), f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16)),
-                   ro, lane * 16, h * HALF * 2);
+                   rdst, doff, dsoff);
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         bstore128<0>(make_uint4(__float_as_uint(d[4 * q]), __float_as_uint(d[4 * q + 1]), __float_as_uint(d[4 * q + 2]),
                                 __float_as_uint(d[4 * q + 3])),
-                     ro, lane * 32 + 16 * q, h * HALF * 4);
+                     rdst, doff + 16 * q, dsoff);
     }
   }
   }
@@ -1032,9 +1068,17 @@ static dim3 grid_for(int64_t n) {
 // wave with all their loads issued first measured 2-7 % slower).
 static dim3 quant_grid(const QuantArgs& a) { return grid_for(a.n); }
 
+static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
+
 template <int FMT, int B>
 static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
   dim3 grid = quant_grid(a), block(kBlockThreads);
+  if constexpr (!is_fp8(FMT) || B == 128) {
+    if (a.ro.order != nullptr) {   // bf16 input, no debug output (checked by the caller)
+      hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), grid, block, order_lds_bytes(a.ro), s, k);
+      return;
+    }
+  }
   if (a.dbg) {
     if (a.f32_in) hipLaunchKernelGGL((k_quantize<FMT, B, true, true>), grid, block, 0, s, k);
     else hipLaunchKernelGGL((k_quantize<FMT, B, false, true>), grid, block, 0, s, k);
@@ -1046,8 +1090,9 @@ static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
+  if (a.ro.order != nullptr && (a.f32_in || a.dbg || (is_fp8(a.fmt) && a.block != 128))) return hipErrorInvalidValue;
   QuantK k{a.x, a.n, a.codes, a.scale, a.zero, a.g_hdr, a.g, a.g_from_ws ? 1 : 0,
-           static_cast<Workspace*>(a.ws), a.dbg};
+           static_cast<Workspace*>(a.ws), a.dbg, a.ro};
   if (is_fp8(a.fmt) && a.auto_prepass) {
     dim3 grid = quant_grid(a), block(kBlockThreads);
     if (a.f32_in) hipLaunchKernelGGL((k_amax<true>), grid, block, 0, s, a.x, a.n, k.ws);
@@ -1082,14 +1127,23 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 
 template <int FMT, int B>
 static void launch_dq(const DequantArgs& a, hipStream_t s) {
-  DequantK k{a.codes, a.scale, a.zero, a.g_hdr, a.n, a.out};
+  DequantK k{a.codes, a.scale, a.zero, a.g_hdr, a.n, a.out, a.ro};
   dim3 grid = grid_for(a.n), block(kBlockThreads);
+  if constexpr (!is_fp8(FMT) || B == 128) {
+    if (a.ro.order != nullptr) {
+      const size_t lds = order_lds_bytes(a.ro);
+      if (a.bf16_out) hipLaunchKernelGGL((k_dequantize<FMT, B, true, true>), grid, block, lds, s, k);
+      else hipLaunchKernelGGL((k_dequantize<FMT, B, false, true>), grid, block, lds, s, k);
+      return;
+    }
+  }
   if (a.bf16_out) hipLaunchKernelGGL((k_dequantize<FMT, B, true>), grid, block, 0, s, k);
   else hipLaunchKernelGGL((k_dequantize<FMT, B, false>), grid, block, 0, s, k);
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
+  if (a.ro.order != nullptr && is_fp8(a.fmt) && a.block != 128) return hipErrorInvalidValue;
   switch (a.fmt) {
     case kFP8:
       switch (a.block) {

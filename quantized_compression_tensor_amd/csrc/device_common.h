@@ -247,6 +247,50 @@ TACO_DEV float wave_max(float a) {
   return a;
 }
 
+// ------------------------------------------------- channel-group reorder --
+// Data-driven reshaping of the hidden dimension: the codec sees the channels
+// in groups of 8, reordered group j being original group order[j] of the same
+// row. Every access of a reordering kernel covers a 512-element span, which
+// lies inside one row (cols is a multiple of 512), and each lane's 8 elements
+// are one group, so a lane's 16-byte bf16 access just moves from group j to
+// group order[j] of its row.
+constexpr int kGroupElems = 8;
+constexpr int kSpanElems = 512;
+constexpr int kSpanShift = 9;
+
+// The order is copied into LDS (int16) at the start of the workgroup, clamped
+// into [0, ngroups) so that no access can leave its row whatever the caller
+// passed; per-span lookups then wait on LDS only, never on the data loads in
+// flight.
+TACO_DEV void load_order_lds(const ReorderArgs& ro, int16_t* lds) {
+  for (int i = (int)threadIdx.x; i < ro.ngroups; i += kBlockThreads) {
+    int v = ro.order[i];
+    v = v < 0 ? 0 : (v >= ro.ngroups ? ro.ngroups - 1 : v);
+    lds[i] = (int16_t)v;
+  }
+  __syncthreads();
+}
+
+// Row of the span starting at flat element e (a multiple of 512) and the
+// span's first column: row = floor(s / d) for the span index s = e / 512 and
+// d = cols / 512 spans per row, as (s * ceil(2^38 / d)) >> 38, exact for
+// s < 2^26 and d <= 256 (the error s * (ceil - exact) / 2^38 < 2^-12 stays
+// below 1/d).
+struct SpanPos {
+  uint32_t row, col0;
+};
+TACO_DEV SpanPos span_pos(const ReorderArgs& ro, int64_t e) {
+  const uint32_t s = (uint32_t)(e >> kSpanShift);
+  const uint32_t row = (uint32_t)(((uint64_t)s * ro.magic) >> 38);
+  return SpanPos{row, (s - row * ro.spans_per_row) * (uint32_t)kSpanElems};
+}
+
+// Source (compress) or destination (decode) group of a lane whose group in the
+// reordered span is `col0 / 8 + lane_group`.
+TACO_DEV int reordered_group(const int16_t* lds, const SpanPos& p, int lane_group) {
+  return lds[(p.col0 >> 3) + lane_group];
+}
+
 // ------------------------------------------------------------- workspace --
 // Abs-max history of an FP8 tensor scale, in caller-owned memory that is
 // zero-filled once. Calls on one workspace are ordered (one stream), and any

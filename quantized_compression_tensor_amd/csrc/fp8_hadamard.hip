@@ -164,6 +164,31 @@ struct HadChunk {
   }
 };
 
+// The chunk's loads with the input's channel groups reordered: tile i of the
+// chunk is one 512-element span of a row, and the lane whose 8 elements are
+// group j of that span loads group order[j] of the same row instead. Tiles at
+// or past the end load nothing (an empty resource returns zeros).
+template <int LOGB, int T, bool REORD>
+TACO_DEV void load_chunk(const uint16_t* x, int64_t c, int64_t elems, int elem_off, const ReorderArgs& ro,
+                         const int16_t* lds_order, uint4* raw) {
+  if constexpr (!REORD) {
+    HadChunk<LOGB, T>::load(x, c, elems, elem_off, raw);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      // spans at or past the end (the look-ahead of the last chunks) read an
+      // empty resource and look nothing up: their span index may lie beyond
+      // the range where span_pos is exact
+      const int64_t e0 = c * HadChunk<LOGB, T>::ELEMS + (int64_t)i * kTileElems;
+      const bool live = e0 < elems;
+      const SpanPos p = live ? span_pos(ro, e0) : SpanPos{0u, 0u};
+      const int src = live ? reordered_group(lds_order, p, elem_off / kGroupElems) : 0;
+      const rsrc_t r = make_rsrc32(x + (int64_t)p.row * ro.cols, live ? ro.cols * 2 : 0);
+      raw[i] = bload128<kNT>(r, src * kGroupElems * 2, 0);
+    }
+  }
+}
+
 // The transform of one tile and its block abs-max (independent of the tensor
 // scale).
 template <int LOGB>
@@ -232,16 +257,19 @@ TACO_DEV void had_compress_chunk(const uint4* raw, int64_t c, int64_t elems, con
   }
 }
 
-template <int LOGB, int T, bool E5, bool GFROM_WS, bool DEBUG, bool PERSIST>
+template <int LOGB, int T, bool E5, bool GFROM_WS, bool DEBUG, bool PERSIST, bool REORD>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ codes, int8_t* __restrict__ kexp,
     float* __restrict__ g_hdr, int64_t nblocks, float g_arg, Workspace* __restrict__ ws,
-    float* __restrict__ dbg) {
+    float* __restrict__ dbg, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB, T>;
+  static_assert(!(REORD && PERSIST), "the reordering compress runs the one-chunk-per-wave grid");
   __shared__ uint32_t lds_e;
   __shared__ float lds_g;
   __shared__ float lds_m[kBlockThreads / kWave];
+  extern __shared__ int16_t lds_order[];
+  if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
   const int row = lane / Gm::G;
@@ -268,8 +296,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   }
   __builtin_amdgcn_sched_barrier(0);
   uint4 ra[T], rb[T];
-  CH::load(x, c, elems, ls.elem_off, ra);
-  CH::load(x, c + stride, elems, ls.elem_off, rb);
+  load_chunk<LOGB, T, REORD>(x, c, elems, ls.elem_off, ro, lds_order, ra);
+  load_chunk<LOGB, T, REORD>(x, c + stride, elems, ls.elem_off, ro, lds_order, rb);
   __builtin_amdgcn_sched_barrier(0);
   // On the persistent grid the first chunk is transformed while the ticket
   // returns; only its scaling and encoding wait for the tensor scale.
@@ -308,15 +336,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     } else {
       had_compress_chunk<LOGB, T, E5, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
     }
-    CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
+    load_chunk<LOGB, T, REORD>(x, c + 2 * stride, elems, ls.elem_off, ro, lds_order, ra);
     c += stride;
     while (c < nchunks) {
       had_compress_chunk<LOGB, T, E5, DEBUG>(rb, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
-      CH::load(x, c + 2 * stride, elems, ls.elem_off, rb);
+      load_chunk<LOGB, T, REORD>(x, c + 2 * stride, elems, ls.elem_off, ro, lds_order, rb);
       c += stride;
       if (c >= nchunks) break;
       had_compress_chunk<LOGB, T, E5, DEBUG>(ra, c, elems, ls, row, inv_g, codes, kexp, dbg, run_max);
-      CH::load(x, c + 2 * stride, elems, ls.elem_off, ra);
+      load_chunk<LOGB, T, REORD>(x, c + 2 * stride, elems, ls.elem_off, ro, lds_order, ra);
       c += stride;
     }
   }
@@ -330,11 +358,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
 }
 
 // Abs-max of the transformed tensor, recorded in the workspace.
-template <int LOGB>
+template <int LOGB, bool REORD>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                                Workspace* __restrict__ ws) {
+                                                                Workspace* __restrict__ ws, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB, kChunkTiles>;
+  extern __shared__ int16_t lds_order[];
+  if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
   const int64_t elems = nblocks << LOGB;
@@ -343,7 +373,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
   float run_max = 0.0f;
   for (int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); c < nchunks; c += stride) {
     uint4 raw[kChunkTiles];
-    CH::load(x, c, elems, ls.elem_off, raw);
+    load_chunk<LOGB, kChunkTiles, REORD>(x, c, elems, ls.elem_off, ro, lds_order, raw);
 #pragma unroll
     for (int i = 0; i < kChunkTiles; ++i) {
       float v[8];
@@ -370,11 +400,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
 // inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
 // factor, then float32 or bf16 output. T wave tiles per wave as launched; a
 // smaller grid walks them with a stride of the grid.
-template <int LOGB, bool E5, bool BF16OUT, int T>
+template <int LOGB, bool E5, bool BF16OUT, int T, bool REORD>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
-    int64_t nblocks, void* __restrict__ out) {
+    int64_t nblocks, void* __restrict__ out, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
+  extern __shared__ int16_t lds_order[];
+  if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const LaneSigns<LOGB> ls(lane);
@@ -409,7 +441,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], outscale, 0.0f);
     if (blk < nblocks) {
-      const int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
+      // reordered: group j of this span goes back to group order[j] of its row
+      int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
+      if constexpr (REORD) {
+        const SpanPos p = span_pos(ro, (tile0 + i) * kTileElems);
+        eoff = (int64_t)p.row * ro.cols + (int64_t)reordered_group(lds_order, p, ls.elem_off / kGroupElems) * kGroupElems;
+      }
       if constexpr (BF16OUT) {
         uint4 o;
         o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
@@ -435,17 +472,21 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
   return (tiles + 4 * T - 1) / (4 * T);
 }
 
-template <int LOGB, int T, bool E5, bool DEBUG, bool PERSIST>
+// Dynamic LDS of the reordering kernels: the order as int16.
+static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
+
+template <int LOGB, int T, bool E5, bool DEBUG, bool PERSIST, bool REORD = false>
 static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s) {
   dim3 block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
+  const size_t lds = REORD ? order_lds_bytes(a.ro) : 0;
   if (a.g_from_ws)
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes, a.kexp,
-                       a.g_hdr, a.nblocks, a.g, ws, a.dbg);
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
+                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, a.ro);
   else
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST>), grid, block, 0, s, x, a.codes,
-                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg);
+    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
+                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, a.ro);
 }
 
 // Grid. Tensors of fewer than 2^16 large chunks take the small chunks on a
@@ -462,17 +503,28 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
   dim3 block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
+  const dim3 big_grid = capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles));
+  if (a.ro.order != nullptr) {
+    // reordered input (block 128 only): the one-chunk-per-wave grid at every size
+    if constexpr (LOGB == 7) {
+      if (a.dbg) return hipErrorInvalidValue;
+      if (a.auto_prepass)
+        hipLaunchKernelGGL((k_fp8_had_amax<LOGB, true>), big_grid, block, order_lds_bytes(a.ro), s, x, a.nblocks, ws,
+                           a.ro);
+      launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, big_grid, s);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.auto_prepass)
-    hipLaunchKernelGGL((k_fp8_had_amax<LOGB>), capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles)), block, 0,
-                       s, x, a.nblocks, ws);
+    hipLaunchKernelGGL((k_fp8_had_amax<LOGB, false>), big_grid, block, 0, s, x, a.nblocks, ws, a.ro);
   if (small) {
     const int64_t need = had_groups(LOGB, a.nblocks, kSmallChunkTiles);
     const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
     launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, capped_grid(need < cap ? need : cap), s);
   } else {
-    const dim3 grid = capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles));
-    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, grid, s);   // test hook: the large chunks
-    else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, grid, s);
+    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, big_grid, s);   // test hook: the large chunks
+    else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, big_grid, s);
   }
   return hipGetLastError();
 }
@@ -492,16 +544,17 @@ hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int LOGB, bool E5>
+template <int LOGB, bool E5, bool REORD>
 static void launch_decode_fmt(const FP8HadDecodeArgs& a, dim3 grid, hipStream_t s) {
   constexpr int T = 2;
   dim3 block(kBlockThreads);
+  const size_t lds = REORD ? order_lds_bytes(a.ro) : 0;
   if (a.bf16_out)
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, true, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr, a.nblocks,
-                       a.out);
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, true, T, REORD>), grid, block, lds, s, a.codes, a.kexp, a.g_hdr,
+                       a.nblocks, a.out, a.ro);
   else
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, false, T>), grid, block, 0, s, a.codes, a.kexp, a.g_hdr,
-                       a.nblocks, a.out);
+    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, false, T, REORD>), grid, block, lds, s, a.codes, a.kexp, a.g_hdr,
+                       a.nblocks, a.out, a.ro);
 }
 
 template <int LOGB>
@@ -509,8 +562,16 @@ static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
   const int64_t groups = had_groups(LOGB, a.nblocks, 2);
   if (groups == 0) return hipSuccess;
   const dim3 grid = capped_grid(groups);
-  if (a.e5) launch_decode_fmt<LOGB, true>(a, grid, s);
-  else launch_decode_fmt<LOGB, false>(a, grid, s);
+  if (a.ro.order != nullptr) {
+    if constexpr (LOGB == 7) {
+      if (a.e5) launch_decode_fmt<LOGB, true, true>(a, grid, s);
+      else launch_decode_fmt<LOGB, false, true>(a, grid, s);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  if (a.e5) launch_decode_fmt<LOGB, true, false>(a, grid, s);
+  else launch_decode_fmt<LOGB, false, false>(a, grid, s);
   return hipGetLastError();
 }
 

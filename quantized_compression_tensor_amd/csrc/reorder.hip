@@ -1,0 +1,94 @@
+// The order of the data-driven reshaping: rank the hidden dimension's groups
+// of 8 channels by their largest magnitude over a statistics tensor.
+//
+// Source: "TACO: Efficient Communication Compression of Intermediate Tensors
+// for Scalable Tensor-Parallel LLM Training" (Pith review page) -- abstract
+// and "What carries the argument": the tensor is reshaped adaptively, from
+// the data, before the Adaptive Scale-Hadamard Transform; the page leaves the
+// rule open. Here the groups are ranked largest magnitude first, equal
+// magnitudes by group index, so that the blocks of the reordered tensor hold
+// channels of similar magnitude.
+//
+// Three launches on the caller's stream, with the output array as the only
+// memory: it first holds each group's abs-max (float bits, as unsigned
+// integers they order like the non-negative floats they are), then the order.
+#include "device_common.h"
+#include "taco_internal.h"
+
+namespace taco {
+
+constexpr int kRankThreads = 1024;
+constexpr int kStatRows = 64;   // rows per workgroup of the statistics pass
+
+__global__ __launch_bounds__(kBlockThreads) void k_zero_u32(uint32_t* p, int n) {
+  const int i = (int)(blockIdx.x * kBlockThreads + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+// Workgroup (s, b): span s of every row (64 groups, one per lane) over the
+// row blocks b, b + gridDim.y, ... of 64 rows, the four waves taking every
+// fourth row; one atomic max per group and workgroup. |x| is formed on the
+// bits; NaN counts as infinity.
+__global__ __launch_bounds__(kBlockThreads) void k_group_absmax(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int cols, uint32_t* __restrict__ gmax) {
+  __shared__ uint32_t part[kBlockThreads / kWave][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_in_group();
+  const int group = (int)blockIdx.x * kWave + lane;
+  uint32_t m = 0u;
+  for (int64_t r0 = (int64_t)blockIdx.y * kStatRows; r0 < rows; r0 += (int64_t)gridDim.y * kStatRows) {
+    for (int64_t r = r0 + wave; r < rows && r < r0 + kStatRows; r += kBlockThreads / kWave) {
+      const uint4 w = ld16_nt(x + r * cols + (int64_t)group * kGroupElems);
+      const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (h[i] << 16) & 0x7FFFFFFFu, hi = h[i] & 0x7FFF0000u;
+        m = max(m, max(lo, hi));
+      }
+    }
+  }
+  m = min(m, 0x7F800000u);   // NaN -> infinity
+  part[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t v = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kBlockThreads / kWave; ++w) v = max(v, part[w][lane]);
+    __hip_atomic_fetch_max(&gmax[group], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One workgroup: read every group's abs-max into LDS, then give group j the
+// rank #{i : a_i > a_j} + #{i < j : a_i = a_j} and write order[rank] = j into
+// the same array (every read happens before the barrier).
+__global__ __launch_bounds__(kRankThreads) void k_rank_groups(uint32_t* __restrict__ buf, int ngroups) {
+  extern __shared__ uint32_t a[];
+  for (int i = (int)threadIdx.x; i < ngroups; i += kRankThreads) a[i] = buf[i];
+  __syncthreads();
+  for (int j = (int)threadIdx.x; j < ngroups; j += kRankThreads) {
+    const uint32_t aj = a[j];
+    int rank = 0;
+    for (int i = 0; i < ngroups; ++i) {
+      const uint32_t ai = a[i];
+      rank += (ai > aj) || (ai == aj && i < j);
+    }
+    buf[rank] = (uint32_t)j;
+  }
+}
+
+hipError_t launch_chunk_order(const void* stats, int64_t rows, int64_t cols, int32_t* order, hipStream_t s) {
+  const int ngroups = (int)(cols / kGroupElems);
+  auto* buf = reinterpret_cast<uint32_t*>(order);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((ngroups + kBlockThreads - 1) / kBlockThreads)),
+                     dim3(kBlockThreads), 0, s, buf, ngroups);
+  if (rows > 0) {
+    const int64_t blocks = (rows + kStatRows - 1) / kStatRows;
+    const dim3 grid((unsigned)(cols / kSpanElems), (unsigned)(blocks < 4096 ? blocks : 4096));
+    hipLaunchKernelGGL(k_group_absmax, grid, dim3(kBlockThreads), 0, s, static_cast<const uint16_t*>(stats), rows,
+                       (int)cols, buf);
+  }
+  hipLaunchKernelGGL(k_rank_groups, dim3(1), dim3(kRankThreads), (size_t)ngroups * 4, s, buf, ngroups);
+  return hipGetLastError();
+}
+
+}  // namespace taco

@@ -112,21 +112,40 @@ int scratch_workspace(hipStream_t stream, void** ws);
 
 // internal_ws: the FP8 workspace is the device's scratch array (fetched, and
 // cleared on its first use, only after every argument has been checked).
+// Shapes the channel-group reorder supports: cols a multiple of 512 and at
+// most 131072 (the order fits LDS as int16), FP8 block 128.
+int check_reorder(const taco_codec& c, int64_t cols) {
+  if (cols % kReorderColsMultiple != 0 || cols > kReorderMaxCols) return TACO_ERR_SHAPE;
+  if (is_fp8_format(c.format) && c.block != 128) return TACO_ERR_SHAPE;
+  return TACO_OK;
+}
+
+// internal_ws: the FP8 workspace is the device's scratch array (fetched, and
+// cleared on its first use, only after every argument has been checked).
+// order: channel-group reorder of the bf16 input (null: none).
 int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int64_t cols, float ts, void* out,
-                    void* ws, size_t ws_bytes, float* dbg, hipStream_t stream, bool internal_ws = false) {
+                    void* ws, size_t ws_bytes, float* dbg, hipStream_t stream, bool internal_ws = false,
+                    const int32_t* order = nullptr, bool reordered = false) {
   int st = check_shape(c, rows, cols);
   if (st != TACO_OK) return st;
+  if (reordered) {
+    st = check_reorder(c, cols);
+    if (st != TACO_OK) return st;
+    if (order == nullptr) return TACO_ERR_INVALID_ARG;
+  }
   int mode = 0;
   st = scale_mode(c, ts, ws, ws_bytes, internal_ws, &mode);
   if (st != TACO_OK) return st;
   const int64_t n = rows * cols;
   if (n == 0) return TACO_OK;
   if (x == nullptr || out == nullptr) return TACO_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(out) || (dbg && !aligned16(dbg))) return TACO_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(out) || (dbg && !aligned16(dbg)) || (order && !aligned16(order)))
+    return TACO_ERR_ALIGN;
   taco_layout_t L;
   layout_of(c, n, &L);
   const int64_t in_bytes = n * (f32_in ? 4 : 2);
   if (overlaps(x, in_bytes, out, L.total_bytes)) return TACO_ERR_INVALID_ARG;
+  if (order && overlaps(order, 4 * (cols / 8), out, L.total_bytes)) return TACO_ERR_INVALID_ARG;
   if (dbg && (overlaps(dbg, 4 * n, x, in_bytes) || overlaps(dbg, 4 * n, out, L.total_bytes)))
     return TACO_ERR_INVALID_ARG;
   if (internal_ws && is_fp8_format(c.format)) {
@@ -139,7 +158,7 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
     a.x = x; a.codes = R.codes; a.kexp = static_cast<int8_t*>(R.scale); a.g_hdr = R.tensor;
     a.nblocks = n / c.block; a.logb = log2_block(c.block); a.e5 = c.format == TACO_FMT_FP8E5_DUAL;
     a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
-    a.ws = ws; a.dbg = dbg;
+    a.ws = ws; a.dbg = dbg; a.ro = make_reorder(order, cols);
     clear_stale_error();
     return hip_status(launch_fp8_had_compress(a, stream));
   }
@@ -147,7 +166,7 @@ int quantize_common(taco_codec c, const void* x, bool f32_in, int64_t rows, int6
   a.fmt = c.format; a.block = c.block; a.f32_in = f32_in; a.x = x; a.n = n;
   a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
   a.g = mode == 0 ? ts : 1.0f; a.g_from_ws = mode != 0; a.auto_prepass = mode == 1;
-  a.ws = is_fp8_format(c.format) ? ws : nullptr; a.dbg = dbg;
+  a.ws = is_fp8_format(c.format) ? ws : nullptr; a.dbg = dbg; a.ro = make_reorder(order, cols);
   clear_stale_error();
   return hip_status(launch_quantize(a, stream));
 }
@@ -358,32 +377,68 @@ int taco_ring_hop(taco_codec c_in, const void* incoming, const void* local_bf16,
   return hip_status(launch_ring_hop(a, stream));
 }
 
-int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
-                    hipStream_t stream) {
+namespace {
+int decompress_common(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                      const int32_t* order, bool reordered, hipStream_t stream) {
   int st = check_shape(c, rows, cols);
   if (st != TACO_OK) return st;
+  if (reordered) {
+    st = check_reorder(c, cols);
+    if (st != TACO_OK) return st;
+    if (order == nullptr) return TACO_ERR_INVALID_ARG;
+  }
   if (out_dtype != 0 && out_dtype != 1) return TACO_ERR_INVALID_ARG;
   const int64_t n = rows * cols;
   if (n == 0) return TACO_OK;
   if (in == nullptr || out == nullptr) return TACO_ERR_INVALID_ARG;
-  if (!aligned16(in) || !aligned16(out)) return TACO_ERR_ALIGN;
+  if (!aligned16(in) || !aligned16(out) || (order && !aligned16(order))) return TACO_ERR_ALIGN;
   taco_layout_t L;
   layout_of(c, n, &L);
-  if (overlaps(in, L.total_bytes, out, n * (out_dtype ? 2 : 4))) return TACO_ERR_INVALID_ARG;
+  const int64_t out_bytes = n * (out_dtype ? 2 : 4);
+  if (overlaps(in, L.total_bytes, out, out_bytes)) return TACO_ERR_INVALID_ARG;
+  if (order && overlaps(order, 4 * (cols / 8), out, out_bytes)) return TACO_ERR_INVALID_ARG;
   Regions R = regions_of(const_cast<void*>(in), L);
   if (is_fp8_format(c.format) && c.hadamard == 1) {
     FP8HadDecodeArgs a;
     a.codes = R.codes; a.kexp = static_cast<const int8_t*>(R.scale); a.g_hdr = R.tensor;
     a.nblocks = n / c.block; a.logb = log2_block(c.block); a.e5 = c.format == TACO_FMT_FP8E5_DUAL;
-    a.bf16_out = out_dtype == 1; a.out = out;
+    a.bf16_out = out_dtype == 1; a.out = out; a.ro = make_reorder(order, cols);
     clear_stale_error();
     return hip_status(launch_fp8_had_decode(a, stream));
   }
   DequantArgs a;
   a.fmt = c.format; a.block = c.block; a.codes = R.codes; a.scale = R.scale; a.zero = R.aux; a.g_hdr = R.tensor;
-  a.n = n; a.bf16_out = out_dtype == 1; a.out = out;
+  a.n = n; a.bf16_out = out_dtype == 1; a.out = out; a.ro = make_reorder(order, cols);
   clear_stale_error();
-    return hip_status(launch_dequantize(a, stream));
+  return hip_status(launch_dequantize(a, stream));
+}
+}  // namespace
+
+int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                    hipStream_t stream) {
+  return decompress_common(c, in, rows, cols, out, out_dtype, nullptr, false, stream);
+}
+
+int taco_decompress_reordered(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
+                              const int32_t* order, hipStream_t stream) {
+  return decompress_common(c, in, rows, cols, out, out_dtype, order, true, stream);
+}
+
+int taco_compress_reordered(taco_codec c, const void* x_bf16, int64_t rows, int64_t cols, float tensor_scale,
+                            void* out, void* workspace, size_t ws_bytes, const int32_t* order, hipStream_t stream) {
+  return quantize_common(c, x_bf16, false, rows, cols, tensor_scale, out, workspace, ws_bytes, nullptr, stream,
+                         false, order, true);
+}
+
+int taco_chunk_order(const void* stats_bf16, int64_t rows, int64_t cols, int32_t* order, hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return TACO_ERR_INVALID_ARG;
+  if (cols % kReorderColsMultiple != 0 || cols > kReorderMaxCols) return TACO_ERR_SHAPE;
+  if (rows > 0 && cols > kMaxElems / rows) return TACO_ERR_INVALID_ARG;
+  if (order == nullptr || (rows > 0 && stats_bf16 == nullptr)) return TACO_ERR_INVALID_ARG;
+  if (!aligned16(order) || (stats_bf16 && !aligned16(stats_bf16))) return TACO_ERR_ALIGN;
+  if (stats_bf16 && overlaps(stats_bf16, 2 * rows * cols, order, 4 * (cols / 8))) return TACO_ERR_INVALID_ARG;
+  clear_stale_error();
+  return hip_status(launch_chunk_order(stats_bf16, rows, cols, order, stream));
 }
 
 namespace {

@@ -19,6 +19,28 @@ constexpr bool is_fp8(int f) { return f == kFP8 || f == kFP8E5; }
 constexpr float kGMin = 0x1p-60f;
 constexpr float kGMax = 0x1p60f;
 
+// Data-driven reorder of the hidden channels in groups of 8 (null order: none).
+struct ReorderArgs {
+  const int32_t* order;     // device int32 [ngroups]: reordered group j = original group order[j]
+  int ngroups;              // cols / 8
+  int cols;                 // a multiple of 512
+  uint32_t spans_per_row;   // cols / 512 (at most 256)
+  uint64_t magic;           // ceil(2^38 / spans_per_row)
+};
+constexpr int kReorderMaxCols = 131072;
+constexpr int kReorderColsMultiple = 512;
+inline ReorderArgs make_reorder(const int32_t* order, int64_t cols) {
+  ReorderArgs r{};
+  r.order = order;
+  if (order != nullptr) {
+    r.ngroups = (int)(cols / 8);
+    r.cols = (int)cols;
+    r.spans_per_row = (uint32_t)(cols / 512);
+    r.magic = ((uint64_t(1) << 38) + r.spans_per_row - 1) / r.spans_per_row;
+  }
+  return r;
+}
+
 // FP8 dual-scale with the Hadamard transform, bf16 input.
 struct FP8HadArgs {
   const void* x;        // bf16 [nblocks << logb]
@@ -33,6 +55,7 @@ struct FP8HadArgs {
   bool auto_prepass;    // run the abs-max pass first (data-driven g of this tensor)
   void* ws;             // Workspace* or null
   float* dbg;           // pre-rounding values or null
+  ReorderArgs ro;       // channel-group reorder of the input (order null: none)
 };
 
 struct FP8HadDecodeArgs {
@@ -44,6 +67,7 @@ struct FP8HadDecodeArgs {
   bool e5;              // E5M2 codes (else E4M3)
   bool bf16_out;
   void* out;
+  ReorderArgs ro;       // restore the original channel order on output (order null: none)
 };
 
 // Quantization without a transform (INT8 symmetric, asymmetric INT4/INT8,
@@ -63,6 +87,7 @@ struct QuantArgs {
   bool auto_prepass;
   void* ws;
   float* dbg;
+  ReorderArgs ro;       // channel-group reorder of a bf16 input (order null: none)
 };
 
 struct DequantArgs {
@@ -75,6 +100,7 @@ struct DequantArgs {
   int64_t n;
   bool bf16_out;
   void* out;
+  ReorderArgs ro;       // restore the original channel order on output (order null: none)
 };
 
 constexpr int kMaxShards = 16;
@@ -152,5 +178,6 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode(bool e5, const float* x, uint8_t* out, int64_t n, hipStream_t s);
+hipError_t launch_chunk_order(const void* stats, int64_t rows, int64_t cols, int32_t* order, hipStream_t s);
 
 }  // namespace taco

@@ -184,6 +184,28 @@ def test_other_entry_points_validation():
     assert _st(T.taco_e5m2_encode, A, B_, 0) == 0
 
 
+def test_reordered_calls_validation():
+    comp, dec, order_fn = T.taco_compress_reordered, T.taco_decompress_reordered, T.taco_chunk_order
+    O = A + (1 << 20)
+    assert _st(comp, FP8, A, 2, 1024, 1.0, B_, None) == T.TACO_ERR_INVALID_ARG          # no order
+    assert _st(comp, FP8, A, 2, 384, 1.0, B_, O) == T.TACO_ERR_SHAPE                    # cols not a multiple of 512
+    assert _st(comp, I8S, A, 1, 262144, 1.0, B_, O) == T.TACO_ERR_SHAPE                 # cols above 131072
+    assert _st(comp, T.codec(T.TACO_FMT_FP8_DUAL, 64, 1), A, 2, 1024, 1.0, B_, O) == T.TACO_ERR_SHAPE   # block 64
+    assert _st(comp, FP8, A, 2, 1024, 1.0, B_, O + 4) == T.TACO_ERR_ALIGN
+    assert _st(comp, FP8, A, 2, 1024, 1.0, B_, B_ + 256) == T.TACO_ERR_INVALID_ARG      # order overlaps the output
+    assert _st(comp, FP8, A, 2, 1024, 0.0, B_, O) == T.TACO_ERR_WORKSPACE               # auto needs a workspace
+    assert _st(comp, I4A, A, 0, 1024, 1.0, B_, O) == 0                                  # empty: nothing to do
+    assert _st(dec, I8S, A, 2, 1024, B_, None, 0) == T.TACO_ERR_INVALID_ARG
+    assert _st(dec, I8S, A, 2, 1000, B_, O, 0) == T.TACO_ERR_SHAPE
+    assert _st(dec, I8S, A, 2, 1024, B_, O, 2) == T.TACO_ERR_INVALID_ARG
+    assert _st(dec, I8S, A, 2, 1024, B_, B_ + 64, 1) == T.TACO_ERR_INVALID_ARG          # order overlaps the output
+    assert _st(order_fn, A, 2, 1000, O) == T.TACO_ERR_SHAPE
+    assert _st(order_fn, A, 2, 1024, None) == T.TACO_ERR_INVALID_ARG
+    assert _st(order_fn, A, -1, 1024, O) == T.TACO_ERR_INVALID_ARG
+    assert _st(order_fn, A, 2, 1024, O + 8) == T.TACO_ERR_ALIGN
+    assert _st(order_fn, A, 2, 1024, A + 16) == T.TACO_ERR_INVALID_ARG                  # order overlaps the statistics
+
+
 def test_launch_limit_is_per_thread_and_restorable():
     import threading
     assert T.taco_set_launch_limit(0) == 0
