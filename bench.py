@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--ring", action="store_true",
                     help="INT workloads: also time one quantized ring reduce-scatter hop (taco_ring_hop) at "
                          "full size and run the full-loop and semi-loop rings over the shards for their MSE")
+    ap.add_argument("--reorder", action="store_true",
+                    help="also time the reordered compress (data-driven reshaping) and compare the rel-MSE with "
+                         "and without the reorder, for the workload's codec and for INT8 / INT4 on its data")
     ap.add_argument("--overlap", action="store_true",
                     help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
                          "next activation, on a second stream, and report the overlap")
@@ -865,12 +868,109 @@ def measure_ring(w, xs, stream, K):
             "ring_codec_in": "INT8 (gather codec)"}
 
 
-def measure_overlap(w, step_fn, nsets, stream, K, caps=(0, 1024, 512, 256, 128, 64)):
+def measure_reorder(w, ctx, stream, K):
+    """The data-driven reshaping (taco_chunk_order, taco_compress_reordered):
+    the order of the 8-channel groups comes from another input set of the
+    workload (an earlier step's activation of rank 0). Reported: the reordered
+    compress's launch time beside the plain one, and the compress round trip's
+    rel-MSE with and without the reorder on a seeded sample of rows, for the
+    workload's codec and for the INT8 (block 64) and INT4 (group 128) codecs on
+    the same data, the GPU's figure checked against the oracle's."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import codecs as cd
+    from oracle.formats import bf16_bits_to_f32
+    import quantized_compression_tensor_amd as T
+    import workloads as W
+    dev = "cuda"
+    xs, bits0 = ctx["xs"], ctx["sets_bits"]
+    order = torch.empty(w.cols // 8, dtype=torch.int32, device=dev)
+    T.taco_chunk_order(xs[1][0], w.rows, w.cols, order, stream=stream.cuda_stream)
+    torch.cuda.synchronize()
+    o = order.cpu().numpy().astype(np.int64)
+    c_in = ctx["c_in"]
+    fp8 = ctx["fp8"]
+    sh = stream.cuda_stream
+    wss = [torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) for _ in range(w.shards)]
+    bufs = ctx["bufs"][0]
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run(reordered):
+        for i in range(K):
+            r = i % w.shards
+            s = i % ctx["nsets"]
+            if reordered:
+                T.taco_compress_reordered(c_in, xs[s][r], w.rows, w.cols, T.TACO_SCALE_DELAYED if fp8 else 1.0,
+                                          bufs[r], order, workspace=wss[r] if fp8 else None, stream=sh)
+            else:
+                T.taco_compress(c_in, xs[s][r], w.rows, w.cols, T.TACO_SCALE_DELAYED if fp8 else 1.0, bufs[r],
+                                workspace=wss[r] if fp8 else None, stream=sh)
+
+    times = {}
+    with torch.cuda.stream(stream):
+        for reordered in (False, True, False, True):
+            run(reordered)
+            a, b = mk(), mk()
+            a.record(stream)
+            run(reordered)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.setdefault(reordered, []).append(a.elapsed_time(b) / K)
+    t_plain, t_re = min(times[False]), min(times[True])
+    b_comp, _ = algorithmic_bytes(w)
+    # quality on sampled rows, GPU and oracle, plain and reordered
+    ch = W.sample_chunks(w, 3, seed=7)
+    idx = W.chunk_rows(ch, w.rows)
+    it = torch.from_numpy(idx).to(dev)
+    x0 = bits0[0][idx]
+    xf = bf16_bits_to_f32(x0)
+    codecs = [(cd.Codec(w.in_format, w.in_block, w.hadamard), "workload codec"),
+              (cd.Codec.int8_sym(), "INT8 sym 64"), (cd.Codec.int4_asym(), "INT4 asym 128")]
+    if w.in_format == 2:
+        codecs = codecs[:1] + codecs[2:]
+    elif w.in_format == 3:
+        codecs = codecs[:2]
+    q = []
+    d = torch.empty(w.n, dtype=torch.float32, device=dev)
+    for oc, label in codecs:
+        c = T.codec(oc.format, oc.block, int(oc.hadamard))
+        f8 = oc.format in cd.FP8_FORMATS
+        buf = T.empty_compressed(c, w.rows, w.cols, dev)
+        row = {"codec": label}
+        for reordered in (False, True):
+            ws = torch.zeros(T.TACO_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev) if f8 else None
+            g = np.float32(2.0 ** -9)     # a given tensor scale keeps the oracle to the sampled rows
+            if reordered:
+                T.taco_compress_reordered(c, xs[0][0], w.rows, w.cols, float(g) if f8 else 1.0, buf, order,
+                                          workspace=ws)
+                T.taco_decompress_reordered(c, buf, w.rows, w.cols, d, order, 0)
+                ref = oracle.decode_reordered(oracle.compress_reordered(oc, x0, o, tensor_scale=g if f8 else None), o)
+            else:
+                T.taco_compress(c, xs[0][0], w.rows, w.cols, float(g) if f8 else 1.0, buf, workspace=ws)
+                T.taco_decompress(c, buf, w.rows, w.cols, d, 0)
+                ref = oracle.decode(oracle.compress(oc, x0, tensor_scale=g if f8 else None))
+            got = d.view(w.rows, w.cols)[it].cpu().numpy()
+            key = "reordered" if reordered else "plain"
+            row[f"rel_mse_{key}"] = oracle.rel_mse(got, xf)
+            row[f"gpu_equals_oracle_{key}"] = bool((got.view(np.uint32) == ref.reshape(got.shape).view(np.uint32)).all())
+        row["reordered_over_plain"] = round(row["rel_mse_reordered"] / row["rel_mse_plain"], 4)
+        q.append(row)
+    return {"order_from": "input set 1, rank 0 (an earlier step's activation)",
+            "compress_ms_plain": round(t_plain, 5), "compress_ms_reordered": round(t_re, 5),
+            "compress_hbm_frac_reordered": round(b_comp / (t_re * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "sample_rows": int(len(idx)), "tensor_scale": "given 2^-9 (FP8 codecs)", "quality": q}
+
+
+def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 128, 64)):
     """The bf16 GEMM [rows, cols] x [cols, cols] that produces the next activation,
     alone and concurrently with the codec step on a second stream (default
     priority), with the codec's launches capped at each of `caps` workgroups
     (taco_set_launch_limit; 0 = uncapped). Per cap: the codec step alone, both
-    together, and the fraction of the shorter of the two that the overlap hid."""
+    together, and the fraction of the shorter of the two that the overlap hid.
+    Also the consumer side: the decode of the gather-stage output to bf16
+    followed by the GEMM on it, against the GEMM alone (the decode's share of
+    the consumer's time)."""
     import torch
     import quantized_compression_tensor_amd as T
     g_stream = torch.cuda.Stream()
@@ -914,8 +1014,28 @@ def measure_overlap(w, step_fn, nsets, stream, K, caps=(0, 1024, 512, 256, 128, 
                      "serial_ms": round(serial, 4),
                      "hidden_frac": round((serial - both_ms) / min(gemm_ms, codec_ms), 3)})
     best = min(rows, key=lambda r: r["both_ms"])
+    # consumer: decode the gather-stage output to bf16, then the GEMM on it
+    dec = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
+    c_out = ctx["c_out"]
+
+    def consumer(i):
+        with torch.cuda.stream(g_stream):
+            T.taco_decompress(c_out, ctx["outs"][i % nsets], w.rows, w.cols, dec, 1, stream=g_stream.cuda_stream)
+            torch.matmul(dec, b, out=c)
+
+    def decode_only(i):
+        with torch.cuda.stream(g_stream):
+            T.taco_decompress(c_out, ctx["outs"][i % nsets], w.rows, w.cols, dec, 1, stream=g_stream.cuda_stream)
+
+    consumer(0)
+    cons_ms = timed(consumer)
+    dec_ms = timed(decode_only)
+    gemm2_ms = timed(gemm)
     return {"gemm_ms": round(gemm_ms, 4), "gemm_tflops": round(flops / gemm_ms / 1e9, 1), "by_cap": rows,
-            "best": best}
+            "best": best,
+            "consumer": {"decode_bf16_ms": round(dec_ms, 4), "gemm_ms": round(gemm2_ms, 4),
+                         "decode_then_gemm_ms": round(cons_ms, 4),
+                         "decode_share": round((cons_ms - gemm2_ms) / cons_ms, 4)}}
 
 
 def main():
@@ -967,10 +1087,11 @@ def main():
         if w.in_format in T.FP8_FORMATS:
             sys.exit("--ring applies to the INT workloads (the FP8 codec is not a ring codec)")
         ring = measure_ring(w, ex["ctx"]["xs"][0], ex["stream"], K=max(10, args.steps // 4))
+    reorder = measure_reorder(w, ex["ctx"], ex["stream"], K=max(16, args.steps)) if args.reorder else None
     overlap = None
     if args.overlap:
         overlap = measure_overlap(w, step_fn=ex["step"], nsets=ex["ctx"]["nsets"], stream=ex["stream"],
-                                  K=max(10, args.steps // 2))
+                                  K=max(10, args.steps // 2), ctx=ex["ctx"])
     del ex
     torch.cuda.empty_cache()
 
@@ -1028,6 +1149,7 @@ def main():
         "workloads": extras,
         **({"rank_share": rank_share} if rank_share else {}),
         **({"overlap": overlap} if overlap else {}),
+        **({"reorder": reorder} if reorder else {}),
         **({"ring": ring} if ring else {}),
         "source_hash": src_hash,
     }
