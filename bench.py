@@ -141,7 +141,7 @@ def kernel_patterns(w):
     if w.in_format in (1, 5) and w.hadamard:
         comp = f"k_fp8_had_compress<{7 if w.in_block == 128 else w.in_block.bit_length() - 1}, "
     else:
-        comp = f"k_quantize<{w.in_format}, {w.in_block}, false, false>"
+        comp = f"k_quantize<{w.in_format}, {w.in_block}, false, false, false>"
     nmax = 2 if w.shards <= 2 else 4 if w.shards <= 4 else 8 if w.shards <= 8 else 16
     fout = w.out_format if w.out_format else w.in_format
     bout = w.out_block if w.out_format else w.in_block
