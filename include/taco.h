@@ -207,15 +207,22 @@ int taco_decompress_reduce(taco_codec c_in, const void* const* shards, int32_t n
 int taco_ring_hop(taco_codec c_in, const void* incoming, const void* local_bf16, int64_t rows, int64_t cols,
                   float* sum_fp32, taco_codec c_out, void* requant_out, hipStream_t stream);
 
-/* Quantize a caller-supplied float32 tensor with c_out (the gather-stage
- * re-quantization on its own). FP8 takes the values as already transformed
- * (no transform is applied); tensor_scale / workspace as for taco_compress. */
+/* Quantize a caller-supplied float32 tensor with c_out: the gather-stage
+ * re-quantization on its own ([FlashComm] "What carries the argument": the
+ * locally summed partial results are quantized again, to INT8, before the
+ * All-Gather; [EQuARX] "What carries the argument": the partial sum is
+ * quantized again before it is sent on; [TACO] Fig. 7: dual-scale FP8
+ * quantization of values already in the transformed domain). FP8 takes the
+ * values as already transformed (no transform is applied); tensor_scale /
+ * workspace as for taco_compress. */
 int taco_requantize(taco_codec c_out, const float* x_fp32, int64_t rows, int64_t cols, float tensor_scale, void* out,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Consumer-side decode of one compressed tensor to float32 (out_dtype 0) or
- * bf16 (out_dtype 1, nearest-even): dequantize and, for FP8 with hadamard,
- * undo the transform (x = H y * 2^-log2(block), since H H = block * I). */
+ * bf16 (out_dtype 1, nearest-even): dequantize ([FlashComm] Algorithm 1:
+ * dequantization from codes, zero point and scale; [EQuARX] "What carries the
+ * argument": q * s) and, for FP8 with hadamard, undo the ASH transform of
+ * [TACO] Fig. 7 (x = H y * 2^-log2(block), since H H = block * I). */
 int taco_decompress(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
                     hipStream_t stream);
 

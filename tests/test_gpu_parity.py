@@ -198,19 +198,38 @@ def test_workspace_history_over_many_grid_sizes():
         assert calls == i + 1 and np.float32(amax) == prev, f"call {i}: history ({calls}, {amax}) != {prev}"
 
 
+@pytest.mark.parametrize("tiny", [False, True], ids=["normal", "with-tiny"])
 @pytest.mark.parametrize("oc", ALL, ids=cid)
-def test_compress_debug_prequant(oc):
-    shape = (5, 2560) if oc.block != 128 or oc.format != cd.INT8_SYM else (5, 2560)
+def test_compress_debug_prequant(oc, tiny):
+    shape = (5, 2560)
     bits = bits_for(shape, seed=77 + oc.format, body="t3", sigma=0.05)
+    if tiny:
+        # every 16th value about 2^-131 (a bf16 subnormal): with g = 0.05 its
+        # w = y / g is a float32 subnormal inside blocks of ordinary values
+        from oracle.formats import f32_to_bf16_bits
+        rng = np.random.default_rng(5)
+        t = (rng.uniform(1.0, 2.0, size=shape) * 2.0 ** -131 * rng.choice([-1.0, 1.0], size=shape)).astype(np.float32)
+        bits = bits.copy()
+        bits[:, ::16] = f32_to_bf16_bits(t)[:, ::16]
     g = np.float32(0.05)
     ref = oracle.compress(oc, bits, tensor_scale=g)
     buf, pre = gpu_compress(oc, bits, scale=float(g), debug=True)
-    assert_same(parse(buf, oc, *shape), ref, cid(oc))
+    assert_same(parse(buf, oc, *shape), ref, cid(oc))    # every code, including the tiny values'
     p = pre.cpu().numpy()
     r = ref.prequant.astype(np.float32)
-    # below 2^-126 the oracle scales with a rounding ldexp, the GPU with one
-    # multiply; both encode to the same (zero) code, compare the rest bit for bit
-    live = np.abs(r) >= 2.0 ** -126
+    live = np.ones(r.shape, bool)
+    if oc.format in cd.FP8_FORMATS:
+        # the oracle rounds w = y * (1/g) and scales it exactly by 2^k; the
+        # kernel forms y * ((1/g) * 2^k) in one rounding. The two agree unless w
+        # is a float32 subnormal; there |v| < 2^-126 * 2^63 = 2^-63, far below
+        # the smallest FP8 code (2^-9 E4M3, 2^-16 E5M2), so both codes are zero
+        # (compared above) and only the pre-rounding values are left out here
+        k = np.repeat(ref.scale.astype(np.int64), oc.block)
+        w = np.ldexp(r.astype(np.float64), -k)
+        live = np.abs(w) >= 2.0 ** -126
+        assert (np.abs(r[~live]) < 2.0 ** -63).all()
+    if tiny and oc.format in cd.FP8_FORMATS and not oc.hadamard:
+        assert (~live).sum() > 0    # without the transform the tiny values keep a subnormal w
     assert same_f32_bits(p[live], r[live]).all()
 
 
