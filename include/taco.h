@@ -264,6 +264,32 @@ int taco_compress_reordered(taco_codec c, const void* x_bf16, int64_t rows, int6
 int taco_decompress_reordered(taco_codec c, const void* in, int64_t rows, int64_t cols, void* out, int32_t out_dtype,
                               const int32_t* order, hipStream_t stream);
 
+/* ---- decode fused into the consumer -----------------------------------
+ * [FlashComm] "What carries the argument" and Fig. 8: the quantized volume is
+ * dequantized on the receiving side and handed to the next computation. This
+ * is that computation for a linear layer, with the decode in its prologue:
+ *   out[M, N] = decode(A)[M, K] * W^T,
+ * where decode(A) is the bf16 tensor taco_decompress(c, a, M, K, ., 1, .)
+ * writes (each value the nearest-even bf16 of the exact decoded value; for a
+ * NaN the sign and payload may differ), W is bf16 [N, K] row-major (the
+ * weight layout of a linear layer), and the products are summed in float32
+ * on the matrix cores. The decoded activation is never written to memory.
+ *   c          a compressed format without the Hadamard transform: INT8_SYM,
+ *              INT4_ASYM, INT8_ASYM, or FP8_DUAL / FP8E5_DUAL with hadamard 0
+ *              and block 32, 64 or 128 (hadamard 1 or block 16:
+ *              TACO_ERR_FORMAT / TACO_ERR_SHAPE)
+ *   a          device buffer in the compressed layout of an [M, K] tensor
+ *   M, N, K    multiples of 128 (else TACO_ERR_SHAPE), K >= 128, N >= 128;
+ *              M may be 0 (nothing enqueued); M * K, N * K and M * N at most
+ *              2^35 (else TACO_ERR_INVALID_ARG)
+ *   w          device bf16 [N, K]
+ *   out        device [M, N], float32 (out_dtype 0) or bf16 (1, nearest-even);
+ *              must overlap neither a nor w
+ * One launch on `stream`; the launch cap does not apply (one workgroup per
+ * 128 x 128 output tile). */
+int taco_decompress_gemm(taco_codec c, const void* a, int64_t M, int64_t K, const void* w_bf16, int64_t N, void* out,
+                         int32_t out_dtype, hipStream_t stream);
+
 /* Cap on the workgroups of every later launch made by the calling host
  * thread (0 = no cap, the default): lets the codec share the GPU with a
  * concurrent kernel, e.g. the GEMM that produces the next activation on

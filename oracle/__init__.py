@@ -86,5 +86,6 @@ from .codecs import (  # noqa: F401
     decode_reordered,
     auto_tensor_scale,
     sum_tensor_scales,
+    decode_gemm,
 )
 from .metrics import rel_mse, rel_l2, mse  # noqa: F401

@@ -533,3 +533,25 @@ def decode(c: Compressed, out_dtype="f32"):
     if out_dtype == "bf16":
         return f32_to_bf16_bits(x)
     return x
+
+
+def decode_gemm(c: Compressed, w_bits):
+    """The consumer of a gathered activation: decode(A) @ W^T.
+
+    [FlashComm] "What carries the argument" and Fig. 8: the quantized volume is
+    dequantized on the receiving side and handed to the next computation, here
+    a linear layer with weight W (bf16 bit patterns [N, K], the rows of W are
+    the output features). The activation is the bf16 tensor decode() writes;
+    the products are summed in float64, so the result is the exact value of
+    the product up to float64 rounding.
+
+    Returns (out, mag), both float64 [M, N]: out = A W^T and mag = |A| |W|^T,
+    the sum of the magnitudes of the products, which bounds any summation
+    order's rounding error when scaled by the unit roundoff of the
+    accumulator.
+    """
+    a = bf16_bits_to_f32(decode(c, "bf16")).astype(np.float64)
+    w = bf16_bits_to_f32(np.asarray(w_bits, dtype=np.uint16)).astype(np.float64)
+    if w.ndim != 2 or w.shape[1] != c.cols:
+        raise ValueError("W must be [N, K] with K the activation's cols")
+    return a @ w.T, np.abs(a) @ np.abs(w).T

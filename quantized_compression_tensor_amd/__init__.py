@@ -40,6 +40,7 @@ EXPORTS = (
     "taco_compress_debug", "taco_decompress_reduce", "taco_ring_hop", "taco_requantize", "taco_decompress",
     "taco_e4m3_encode", "taco_e5m2_encode", "taco_status_string", "taco_compress_noalloc",
     "taco_set_launch_limit", "taco_chunk_order", "taco_compress_reordered", "taco_decompress_reordered",
+    "taco_decompress_gemm",
 )
 
 
@@ -99,6 +100,7 @@ def _load():
         "taco_chunk_order": (ctypes.c_int, [P, I64, I64, P, P]),
         "taco_compress_reordered": (ctypes.c_int, [C, P, I64, I64, F32, P, P, SZ, P, P]),
         "taco_decompress_reordered": (ctypes.c_int, [C, P, I64, I64, P, I32, P, P]),
+        "taco_decompress_gemm": (ctypes.c_int, [C, P, I64, I64, P, I64, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -246,6 +248,12 @@ def taco_compress_reordered(c, x_bf16, rows, cols, tensor_scale, out, order, wor
 def taco_decompress_reordered(c, inp, rows, cols, out, order, out_dtype=0, stream=None):
     return _check(_lib.taco_decompress_reordered(c, _ptr(inp), rows, cols, _ptr(out), int(out_dtype), _ptr(order),
                                                  _stream(stream)), "taco_decompress_reordered")
+
+
+def taco_decompress_gemm(c, a, M, K, w_bf16, N, out, out_dtype=0, stream=None):
+    """out[M, N] = decode(a)[M, K] @ w_bf16[N, K]^T, the decode fused into the GEMM."""
+    return _check(_lib.taco_decompress_gemm(c, _ptr(a), M, K, _ptr(w_bf16), N, _ptr(out), int(out_dtype),
+                                            _stream(stream)), "taco_decompress_gemm")
 
 
 def taco_e4m3_encode(x, codes, n, stream=None):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libtaco.so")
 
-SOURCES = ["taco_abi.hip", "fp8_hadamard.hip", "codecs.hip", "reorder.hip"]
+SOURCES = ["taco_abi.hip", "fp8_hadamard.hip", "codecs.hip", "reorder.hip", "dequant_gemm.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: no fused multiply-adds except the explicit fmaf calls,

@@ -430,6 +430,33 @@ int taco_compress_reordered(taco_codec c, const void* x_bf16, int64_t rows, int6
                          false, order, true);
 }
 
+int taco_decompress_gemm(taco_codec c, const void* a, int64_t M, int64_t K, const void* w_bf16, int64_t N, void* out,
+                         int32_t out_dtype, hipStream_t stream) {
+  int st = check_codec(c);
+  if (st != TACO_OK) return st;
+  if (c.hadamard != 0) return TACO_ERR_FORMAT;
+  if (is_fp8_format(c.format) && c.block < 32) return TACO_ERR_SHAPE;
+  if (M < 0 || N <= 0 || K <= 0) return TACO_ERR_INVALID_ARG;
+  if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0) return TACO_ERR_SHAPE;
+  if (K > kMaxElems / N || (M > 0 && (K > kMaxElems / M || N > kMaxElems / M))) return TACO_ERR_INVALID_ARG;
+  // M * N <= 2^35 keeps the grid, one workgroup per 128 x 128 tile, below 2^21
+  if (out_dtype != 0 && out_dtype != 1) return TACO_ERR_INVALID_ARG;
+  if (M == 0) return TACO_OK;
+  if (a == nullptr || w_bf16 == nullptr || out == nullptr) return TACO_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w_bf16) || !aligned16(out)) return TACO_ERR_ALIGN;
+  taco_layout_t L;
+  layout_of(c, M * K, &L);
+  const int64_t out_bytes = M * N * (out_dtype ? 2 : 4);
+  if (overlaps(a, L.total_bytes, out, out_bytes) || overlaps(w_bf16, 2 * N * K, out, out_bytes))
+    return TACO_ERR_INVALID_ARG;
+  Regions R = regions_of(const_cast<void*>(a), L);
+  DGemmArgs d;
+  d.fmt = c.format; d.block = c.block; d.codes = R.codes; d.scale = R.scale; d.zero = R.aux; d.g_hdr = R.tensor;
+  d.w = static_cast<const uint16_t*>(w_bf16); d.M = M; d.N = N; d.K = K; d.bf16_out = out_dtype == 1; d.out = out;
+  clear_stale_error();
+  return hip_status(launch_dequant_gemm(d, stream));
+}
+
 int taco_chunk_order(const void* stats_bf16, int64_t rows, int64_t cols, int32_t* order, hipStream_t stream) {
   if (rows < 0 || cols <= 0) return TACO_ERR_INVALID_ARG;
   if (cols % kReorderColsMultiple != 0 || cols > kReorderMaxCols) return TACO_ERR_SHAPE;

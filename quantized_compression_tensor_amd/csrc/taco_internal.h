@@ -103,6 +103,20 @@ struct DequantArgs {
   ReorderArgs ro;       // restore the original channel order on output (order null: none)
 };
 
+// Decode fused into the consumer's GEMM: out[M, N] = decode(A)[M, K] * W^T.
+struct DGemmArgs {
+  int fmt;
+  int block;
+  const uint8_t* codes;   // A's codes, [M, K] in the compressed layout
+  const void* scale;
+  const uint8_t* zero;
+  const float* g_hdr;
+  const uint16_t* w;      // bf16 [N, K] row-major
+  int64_t M, N, K;        // multiples of 128
+  bool bf16_out;
+  void* out;              // [M, N] row-major, float32 or bf16
+};
+
 constexpr int kMaxShards = 16;
 
 struct ShardPtrs {
@@ -178,6 +192,7 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ring_hop(const HopArgs& a, hipStream_t s);
 hipError_t launch_fp8_encode(bool e5, const float* x, uint8_t* out, int64_t n, hipStream_t s);
+hipError_t launch_dequant_gemm(const DGemmArgs& a, hipStream_t s);
 hipError_t launch_chunk_order(const void* stats, int64_t rows, int64_t cols, int32_t* order, hipStream_t s);
 
 }  // namespace taco

@@ -93,3 +93,22 @@ def same_buffers(b1, b2, oc, rows, cols):
             return False
     g1, g2 = p1["g"], p2["g"]
     return (g1 is None and g2 is None) or (np.float32(g1).view(np.uint32) == np.float32(g2).view(np.uint32))
+
+
+def upload_compressed(ref: oracle.Compressed):
+    """A device buffer in the library's layout holding an oracle shard (codes,
+    scales, zero points and, for FP8, the tensor scale g); bytes between the
+    regions are zero."""
+    c = ccodec(ref.codec)
+    buf = T.empty_compressed(c, ref.rows, ref.cols)
+    buf.zero_()
+    codes, sc, aux, ten = T.regions(buf, c, ref.rows, ref.cols)
+    codes.copy_(torch.from_numpy(np.ascontiguousarray(ref.codes, np.uint8)))
+    if ref.codec.format in cd.FP8_FORMATS:
+        sc.copy_(torch.from_numpy(np.ascontiguousarray(ref.scale, np.int8)))
+        ten[0] = float(np.float32(ref.tensor_scale))
+    else:
+        sc.copy_(torch.from_numpy(np.ascontiguousarray(ref.scale, np.float32)))
+    if ref.zero is not None:
+        aux.copy_(torch.from_numpy(np.ascontiguousarray(ref.zero, np.uint8)))
+    return buf

@@ -206,6 +206,31 @@ def test_reordered_calls_validation():
     assert _st(order_fn, A, 2, 1024, A + 16) == T.TACO_ERR_INVALID_ARG                  # order overlaps the statistics
 
 
+def test_decompress_gemm_validation():
+    g = T.taco_decompress_gemm
+    Wt, O = A + (1 << 24), A + (1 << 26)
+    I8A = T.codec(T.TACO_FMT_INT8_ASYM, 128)
+    assert _st(g, FP8, A, 128, 128, Wt, 128, O) == T.TACO_ERR_FORMAT                     # Hadamard codec
+    assert _st(g, T.codec(T.TACO_FMT_FP8_DUAL, 16, 0), A, 128, 128, Wt, 128, O) == T.TACO_ERR_SHAPE
+    assert _st(g, I8A, A, 100, 128, Wt, 128, O) == T.TACO_ERR_SHAPE                      # M
+    assert _st(g, I8A, A, 128, 192, Wt, 128, O) == T.TACO_ERR_SHAPE                      # K
+    assert _st(g, I8A, A, 128, 128, Wt, 64, O) == T.TACO_ERR_SHAPE                       # N
+    assert _st(g, I8A, A, 128, 128, Wt, 0, O) == T.TACO_ERR_INVALID_ARG
+    assert _st(g, I8A, A, -128, 128, Wt, 128, O) == T.TACO_ERR_INVALID_ARG
+    assert _st(g, I8A, A, 1 << 20, 1 << 16, Wt, 128, O) == T.TACO_ERR_INVALID_ARG        # 2^36 activation elements
+    assert _st(g, I8A, A, 1 << 18, 128, Wt, 1 << 18, O) == T.TACO_ERR_INVALID_ARG        # 2^36 outputs
+    assert _st(g, I8A, A, 128, 128, Wt, 128, O, 2) == T.TACO_ERR_INVALID_ARG             # out_dtype
+    assert _st(g, I8A, None, 128, 128, Wt, 128, O) == T.TACO_ERR_INVALID_ARG
+    assert _st(g, I8A, A, 128, 128, None, 128, O) == T.TACO_ERR_INVALID_ARG
+    assert _st(g, I8A, A, 128, 128, Wt, 128, None) == T.TACO_ERR_INVALID_ARG
+    assert _st(g, I8A, A + 8, 128, 128, Wt, 128, O) == T.TACO_ERR_ALIGN
+    assert _st(g, I8A, A, 128, 128, Wt + 8, 128, O) == T.TACO_ERR_ALIGN
+    assert _st(g, I8A, A, 128, 128, Wt, 128, O + 8) == T.TACO_ERR_ALIGN
+    assert _st(g, I8A, A, 128, 128, Wt, 128, A + 1024) == T.TACO_ERR_INVALID_ARG         # out overlaps A
+    assert _st(g, I8A, A, 128, 128, Wt, 128, Wt + 1024) == T.TACO_ERR_INVALID_ARG        # out overlaps W
+    assert _st(g, I8A, None, 0, 128, None, 128, None) == 0                               # M = 0: nothing to do
+
+
 def test_launch_limit_is_per_thread_and_restorable():
     import threading
     assert T.taco_set_launch_limit(0) == 0

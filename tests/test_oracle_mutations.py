@@ -280,3 +280,27 @@ def test_order_mistakes_are_caught(monkeypatch, bad):
 def test_restore_with_the_order_itself_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "restore_columns", lambda y, order: oracle.reorder_columns(y, order))
     assert _fails(TO.test_reorder_and_restore_are_inverse_permutations)
+
+
+def _gemm_variant(kind):
+    def bad(c, w_bits):
+        if kind == "f32_activation":
+            a = cd.decode(c, "f32").astype(np.float64)
+        else:
+            a = fm.bf16_bits_to_f32(cd.decode(c, "bf16")).astype(np.float64)
+        w = fm.bf16_bits_to_f32(np.asarray(w_bits, np.uint16)).astype(np.float64)
+        if kind == "magnitude_weight":
+            w = np.abs(w)
+        if kind == "reversed_k":
+            w = w[:, ::-1]
+        return a @ w.T, np.abs(a) @ np.abs(w).T
+    return bad
+
+
+@pytest.mark.parametrize("kind", ["f32_activation", "magnitude_weight", "reversed_k"])
+def test_decode_gemm_mistakes_are_caught(monkeypatch, kind):
+    import oracle
+    import tests.test_oracle_gemm as TG
+    monkeypatch.setattr(oracle, "decode_gemm", _gemm_variant(kind))
+    assert _fails(TG.test_decode_gemm_equals_exact_sum, cd.INT8_ASYM)
+    assert _fails(TG.test_decode_gemm_equals_exact_sum, cd.FP8_DUAL)
