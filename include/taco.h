@@ -279,7 +279,9 @@ int taco_decompress_reordered(taco_codec c, const void* in, int64_t rows, int64_
  *              and block 32, 64 or 128 (hadamard 1 or block 16:
  *              TACO_ERR_FORMAT / TACO_ERR_SHAPE)
  *   a          device buffer in the compressed layout of an [M, K] tensor
- *   M, N, K    multiples of 128 (else TACO_ERR_SHAPE), K >= 128, N >= 128;
+ *   M, N, K    multiples of 128 and K at most 2^20 (else TACO_ERR_SHAPE),
+ *              K >= 128, N >= 128 (256 x 256 output tiles when M and N are
+ *              multiples of 256, else 128 x 128);
  *              M may be 0 (nothing enqueued); M * K, N * K and M * N at most
  *              2^35 (else TACO_ERR_INVALID_ARG)
  *   w          device bf16 [N, K]

@@ -437,7 +437,7 @@ int taco_decompress_gemm(taco_codec c, const void* a, int64_t M, int64_t K, cons
   if (c.hadamard != 0) return TACO_ERR_FORMAT;
   if (is_fp8_format(c.format) && c.block < 32) return TACO_ERR_SHAPE;
   if (M < 0 || N <= 0 || K <= 0) return TACO_ERR_INVALID_ARG;
-  if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0) return TACO_ERR_SHAPE;
+  if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0 || K > (int64_t(1) << 20)) return TACO_ERR_SHAPE;
   if (K > kMaxElems / N || (M > 0 && (K > kMaxElems / M || N > kMaxElems / M))) return TACO_ERR_INVALID_ARG;
   // M * N <= 2^35 keeps the grid, one workgroup per 128 x 128 tile, below 2^21
   if (out_dtype != 0 && out_dtype != 1) return TACO_ERR_INVALID_ARG;
@@ -453,6 +453,7 @@ int taco_decompress_gemm(taco_codec c, const void* a, int64_t M, int64_t K, cons
   DGemmArgs d;
   d.fmt = c.format; d.block = c.block; d.codes = R.codes; d.scale = R.scale; d.zero = R.aux; d.g_hdr = R.tensor;
   d.w = static_cast<const uint16_t*>(w_bf16); d.M = M; d.N = N; d.K = K; d.bf16_out = out_dtype == 1; d.out = out;
+  d.neg_zero = -0.0f;
   clear_stale_error();
   return hip_status(launch_dequant_gemm(d, stream));
 }

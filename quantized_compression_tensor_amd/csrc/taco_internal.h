@@ -115,6 +115,7 @@ struct DGemmArgs {
   int64_t M, N, K;        // multiples of 128
   bool bf16_out;
   void* out;              // [M, N] row-major, float32 or bf16
+  float neg_zero;         // -0.0f (an addend the compiler cannot fold away)
 };
 
 constexpr int kMaxShards = 16;

@@ -215,6 +215,7 @@ def test_decompress_gemm_validation():
     assert _st(g, I8A, A, 100, 128, Wt, 128, O) == T.TACO_ERR_SHAPE                      # M
     assert _st(g, I8A, A, 128, 192, Wt, 128, O) == T.TACO_ERR_SHAPE                      # K
     assert _st(g, I8A, A, 128, 128, Wt, 64, O) == T.TACO_ERR_SHAPE                       # N
+    assert _st(g, I8A, A, 128, (1 << 20) + 128, Wt, 128, O) == T.TACO_ERR_SHAPE          # K above 2^20
     assert _st(g, I8A, A, 128, 128, Wt, 0, O) == T.TACO_ERR_INVALID_ARG
     assert _st(g, I8A, A, -128, 128, Wt, 128, O) == T.TACO_ERR_INVALID_ARG
     assert _st(g, I8A, A, 1 << 20, 1 << 16, Wt, 128, O) == T.TACO_ERR_INVALID_ARG        # 2^36 activation elements

@@ -1,7 +1,9 @@
 """Parity of the decode fused into the consumer's GEMM (taco_decompress_gemm)
 with the oracle's decode(A) @ W^T, through the C ABI.
 
-Three kinds of check:
+Shapes with M and N multiples of 256 run the 256 x 256 tiles, the others
+the 128 x 128 ones; (2304, 512, 768) has nine tile rows (a group of eight
+and a group of one). Three kinds of check:
  * a permutation weight: every output is one decoded activation value times
    1.0, so the result is exact and is compared value for value with the
    oracle's bf16 decode (this pins the in-kernel decode, its bf16 rounding and
@@ -61,10 +63,11 @@ def _tolerance(ref, mag, K, out_dtype):
     return tol
 
 
+@pytest.mark.parametrize("M", [384, 512], ids=["tiles128", "tiles256"])
 @pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
 @pytest.mark.parametrize("oc", CODECS, ids=cid)
-def test_permutation_weight_is_exact(oc, out_dtype):
-    M, K = 384, 512
+def test_permutation_weight_is_exact(oc, out_dtype, M):
+    K = 512
     ref = _activation(oc, M, K, seed=50 + oc.format + oc.block)
     perm = np.random.default_rng(7).permutation(K)
     w_bits = np.zeros((K, K), np.uint16)
@@ -76,7 +79,7 @@ def test_permutation_weight_is_exact(oc, out_dtype):
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ; first at {np.argwhere(bad)[:4].tolist()}"
 
 
-@pytest.mark.parametrize("shape", [(256, 384, 256), (1152, 640, 640), (128, 128, 1280)], ids=str)
+@pytest.mark.parametrize("shape", [(256, 384, 256), (2304, 512, 768), (1152, 640, 640), (128, 128, 1280)], ids=str)
 @pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
 @pytest.mark.parametrize("oc", CODECS, ids=cid)
 def test_dense_weight_matches_oracle(oc, out_dtype, shape):
