@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--reorder", action="store_true",
                     help="also time the reordered compress (data-driven reshaping) and compare the rel-MSE with "
                          "and without the reorder, for the workload's codec and for INT8 / INT4 on its data")
+    ap.add_argument("--no-consumer", action="store_true",
+                    help="skip the consumer measurement (decode + GEMM vs the fused decode-GEMM) of the "
+                         "workloads whose gather stage has no Hadamard transform")
     ap.add_argument("--overlap", action="store_true",
                     help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
                          "next activation, on a second stream, and report the overlap")
@@ -733,9 +736,80 @@ def run_workload(w, args, headline):
             "compress_vs_copy": round(comp_gbs / (4 * w.n / (t_ref * 1e-3) / 1e9), 3)}
     if not args.no_quality:
         res["quality"] = quality(w, ctx)
+    if not args.no_consumer and c_out is not None:
+        res["consumer"] = measure_consumer(w, ctx, stream, K=max(10, K // 2))
     extras = {"stream": stream, "step": lambda s: (compress(s), reduce(s)), "ctx": ctx, "t_comp": t_comp,
               "t_red": t_red, "ms_step": ms_step}
     return res, extras
+
+
+def measure_consumer(w, ctx, stream, K):
+    """The next layer's input: the gather-stage output (the requantized sum,
+    resident from the step) times a bf16 weight W [cols, cols] in the layout
+    of a linear layer. Unfused: taco_decompress to bf16, then torch.matmul
+    (hipBLASLt) on it; fused: taco_decompress_gemm, the decode in the GEMM's
+    prologue. Both write bf16 [rows, cols]. Codecs with the Hadamard
+    transform are not taken by the fused kernel (reported as such)."""
+    import torch
+    import quantized_compression_tensor_amd as T
+    c = ctx["c_out"]
+    if c.hadamard:
+        return {"note": "gather codec applies the Hadamard transform: the fused decode-GEMM takes codecs "
+                        "without it (the decode + GEMM path is the decode_bf16_ms kernel + a library GEMM)"}
+    rows, cols, outs, nsets = w.rows, w.cols, ctx["outs"], ctx["nsets"]
+    sh = stream.cuda_stream
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 77)
+    wt = (torch.randn(cols, cols, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    dec = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    y_unf = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    y_fus = torch.empty_like(y_unf)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def decode(i):
+        T.taco_decompress(c, outs[i % nsets], rows, cols, dec, 1, stream=sh)
+
+    def gemm(i):
+        torch.matmul(dec, wt.t(), out=y_unf)
+
+    def fused(i):
+        T.taco_decompress_gemm(c, outs[i % nsets], rows, cols, wt, cols, y_fus, 1, stream=sh)
+
+    def timed(*fns):
+        for i in range(3):
+            for f in fns:
+                f(i)
+        a, b = mk(), mk()
+        a.record(stream)
+        for i in range(K):
+            for f in fns:
+                f(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    with torch.cuda.stream(stream):
+        t_dec = timed(decode)
+        t_gemm = timed(gemm)
+        t_both = timed(decode, gemm)
+        t_fused = timed(fused)
+        decode(0)
+        gemm(0)
+        fused(0)
+        torch.cuda.synchronize()
+        ref = y_unf.float()
+        ref_max = float(ref.abs().max())
+        diff = (y_fus.float() - ref).abs()
+        rel = float(diff.max()) / ref_max if ref_max > 0 else float("nan")
+        differ = float((diff > 0).float().mean())
+    flops = 2.0 * rows * cols * cols
+    return {"shape": f"[{rows}, {cols}] x [{cols}, {cols}]^T, bf16 out",
+            "decode_bf16_ms": round(t_dec, 5), "gemm_ms": round(t_gemm, 5),
+            "gemm_tflops": round(flops / t_gemm / 1e9, 1),
+            "decode_then_gemm_ms": round(t_both, 5), "fused_ms": round(t_fused, 5),
+            "fused_tflops": round(flops / t_fused / 1e9, 1),
+            "fused_speedup_vs_decode_then_gemm": round(t_both / t_fused, 3),
+            "max_rel_diff_vs_unfused": float(f"{rel:.3g}"), "max_abs_output": float(f"{ref_max:.4g}"),
+            "outputs_differing_frac": round(differ, 4)}
 
 
 def measure_rank_share(w, xs, stream, K):
@@ -1144,6 +1218,7 @@ def main():
         "kernels": kern,
         "algorithmic_bytes": head["algorithmic_bytes"],
         **({"quality": head["quality"]} if "quality" in head else {}),
+        **({"consumer": head["consumer"]} if "consumer" in head else {}),
         "cpu_baseline": cpu,
         "eight_shard_step_hbm_frac": eight,
         "workloads": extras,
