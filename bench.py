@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--summarize-issue", metavar="DIR",
                     help="turn a rocprofv3 --pmc run of instruction and busy counters (with --kernel-trace) into "
                          "profiles/issue_<kernel>_<workload>.txt and exit")
+    ap.add_argument("--summarize-consumer", nargs=2, metavar=("TRACE_DIR", "MFMA_DIR"),
+                    help="write profiles/consumer_gemm.txt from a kernel trace of the default bench command and "
+                         "an MFMA counter pass (then exit)")
     ap.add_argument("--command", default="", help="with --summarize: the profiled command, recorded")
     return ap.parse_args()
 
@@ -1112,8 +1115,47 @@ def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 
                          "decode_share": round((cons_ms - gemm2_ms) / cons_ms, 4)}}
 
 
+def summarize_consumer(trace_dir, mfma_dir, command):
+    """Kernel-trace statistics of the consumer kernels (the fused decode-GEMM,
+    the library GEMM, the bf16 decode) and the fused kernel's MFMA counters:
+    MFMA pipe busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs * GRBM_GUI_ACTIVE
+    / 8 XCDs), and the other VALU instructions per MFMA instruction."""
+    keep = ("k_dequant_gemm", "Cijk", "k_dequantize")
+    lines = ["# consumer kernels: the gather-stage output times a bf16 weight W [cols, cols] (linear-layer layout)",
+             f"# command: {command}",
+             f"source_hash: {kernel_source_hash()}",
+             " calls    avg_us    min_us    max_us  kernel"]
+    for r in sorted(_csv_rows(trace_dir, "kernel_stats.csv"), key=lambda r: -float(r["AverageNs"])):
+        n = r["Name"]
+        if any(k in n for k in keep) and ("k_dequantize" not in n or ", true, false>" in n):
+            lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                         f"{float(r['MaxNs']) / 1e3:9.2f}  {n[:140]}")
+    per = {}
+    for row in _csv_rows(mfma_dir, "counter_collection.csv"):
+        n = row.get("Kernel_Name", "")
+        if "k_dequant_gemm" not in n:
+            continue
+        d = per.setdefault(n, {}).setdefault(row["Dispatch_Id"], {})
+        d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    for n, disp in per.items():
+        last = disp[max(disp, key=int)]
+        busy = last.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024 * last.get("GRBM_GUI_ACTIVE", 1.0) / 8)
+        lines += [f"kernel: {n[:140]}",
+                  *[f"  {k}: {v:.6g}" for k, v in sorted(last.items())],
+                  f"  mfma_busy_frac: {busy:.3f}",
+                  # SQ_INSTS_VALU counts the MFMA instructions too
+                  f"  other_valu_per_mfma: {(last.get('SQ_INSTS_VALU', 0.0) - last.get('SQ_INSTS_MFMA', 0.0)) / max(1.0, last.get('SQ_INSTS_MFMA', 1.0)):.2f}"]
+    path = os.path.join(ROOT, "profiles", "consumer_gemm.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def main():
     args = parse()
+    if args.summarize_consumer:
+        summarize_consumer(*args.summarize_consumer, args.command)
+        return
     if args.summarize_issue:
         names = [args.workload] + [x for x in args.extra.split(",") if x and x != "none"]
         summarize_issue(args.summarize_issue, names, args.command)
