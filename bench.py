@@ -791,10 +791,15 @@ def measure_consumer(w, ctx, stream, K):
         return a.elapsed_time(b) / K
 
     with torch.cuda.stream(stream):
-        t_dec = timed(decode)
-        t_gemm = timed(gemm)
-        t_both = timed(decode, gemm)
-        t_fused = timed(fused)
+        # three interleaved rounds, the fastest of each (clock drift between
+        # the measurements would otherwise favour one side)
+        runs = {"dec": [], "gemm": [], "both": [], "fused": []}
+        for _ in range(3):
+            runs["dec"].append(timed(decode))
+            runs["gemm"].append(timed(gemm))
+            runs["both"].append(timed(decode, gemm))
+            runs["fused"].append(timed(fused))
+        t_dec, t_gemm, t_both, t_fused = (min(runs[k]) for k in ("dec", "gemm", "both", "fused"))
         decode(0)
         gemm(0)
         fused(0)

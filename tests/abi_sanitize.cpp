@@ -89,6 +89,13 @@ int main() {
   EXPECT(taco_compress_reordered(fp8, A, 2, 1024, 1.0f, B, nullptr, 0, nullptr, 0), TACO_ERR_INVALID_ARG);
   EXPECT(taco_compress_reordered(i8s, A, 1, 262144, 1.0f, B, nullptr, 0, (int32_t*)O, 0), TACO_ERR_SHAPE);
   EXPECT(taco_decompress_reordered(i8s, A, 2, 1024, B, 0, (int32_t*)((char*)O + 4), 0), TACO_ERR_ALIGN);
+  EXPECT(taco_decompress_gemm(fp8, A, 128, 128, B, 128, O, 0, 0), TACO_ERR_FORMAT);        // Hadamard codec
+  EXPECT(taco_decompress_gemm(i8a, A, 100, 128, B, 128, O, 0, 0), TACO_ERR_SHAPE);
+  EXPECT(taco_decompress_gemm(i8a, A, 128, 128, B, 128, O, 2, 0), TACO_ERR_INVALID_ARG);
+  EXPECT(taco_decompress_gemm(i8a, A, 128, 128, B, 128, (char*)O + 8, 0, 0), TACO_ERR_ALIGN);
+  EXPECT(taco_decompress_gemm(i8a, A, 1 << 18, 128, B, 1 << 18, O, 0, 0), TACO_ERR_INVALID_ARG);
+  EXPECT(taco_decompress_gemm(i8a, A, 128, 128, B, 128, (char*)A + 64, 0, 0), TACO_ERR_INVALID_ARG);
+  EXPECT(taco_decompress_gemm(i8a, nullptr, 0, 128, nullptr, 128, nullptr, 0, 0), TACO_OK);
   EXPECT(taco_e4m3_encode((const float*)A, (uint8_t*)A + 16, 64, 0), TACO_ERR_INVALID_ARG);
   EXPECT(taco_e5m2_encode((const float*)A, nullptr, 16, 0), TACO_ERR_INVALID_ARG);
   EXPECT(taco_e5m2_encode((const float*)A, (uint8_t*)B, 0, 0), TACO_OK);

@@ -12,7 +12,19 @@ import pytest
 from tests.conftest import ROOT
 
 CSRC = os.path.join(ROOT, "quantized_compression_tensor_amd", "csrc")
-SOURCES = ["taco_abi.hip", "fp8_hadamard.hip", "codecs.hip", "reorder.hip"]
+
+
+def _library_sources():
+    """The library's source list, from its build script (one list to keep)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "taco_build", os.path.join(ROOT, "quantized_compression_tensor_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return list(mod.SOURCES)
+
+
+SOURCES = _library_sources()
 HIPCC = "/opt/rocm/bin/hipcc"
 
 
