@@ -114,3 +114,31 @@ def test_writes_stay_inside_buffers(oc, shape):
         T.taco_ring_hop(c, shards[1].buf(), xs[2].buf(), rows, cols, hs.buf(torch.float32), co, hq.buf())
         hs.assert_guards("ring hop sum")
         hq.assert_guards("ring hop requant")
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 128), (384, 256, 640), (512, 384, 256)], ids=str)
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(32, False), cd.Codec.int8_sym(), cd.Codec.int4_asym(),
+                                cd.Codec.int8_asym()], ids=lambda oc: f"f{oc.format}-b{oc.block}")
+@pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
+def test_decompress_gemm_stays_inside_buffers(oc, shape, out_dtype):
+    """The fused decode-GEMM reads its compressed A and its weight, and writes its
+    output, only inside the buffers given (both tile sizes: (512, 384, 256) runs
+    the 256 x 256 tiles); the inputs are left unchanged."""
+    M, K, N = shape
+    c = ccodec(oc)
+    print(f"bounds: decode-GEMM codec {oc} shape {shape} out {out_dtype}", flush=True)
+    body = "t3" if oc.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    bits = W.random_bits((M, K), seed=91, sigma=0.05, body=body)
+    x = Arena(2 * M * K).fill(bits)
+    a = Arena(T.taco_compressed_bytes(c, M, K))
+    T.taco_compress(c, x.buf(), M, K, 0.05, a.buf())
+    a.assert_guards("compress of the activation")
+    a_before = a.buf().clone()
+    w = Arena(2 * N * K).fill(W.random_bits((N, K), seed=92, sigma=0.05))
+    w_before = w.buf().clone()
+    out = Arena(M * N * (2 if out_dtype else 4))
+    T.taco_decompress_gemm(c, a.buf(), M, K, w.buf(), N, out.buf(), out_dtype)
+    out.assert_guards("decode-GEMM output")
+    a.assert_guards("decode-GEMM activation")
+    w.assert_guards("decode-GEMM weight")
+    assert torch.equal(a.buf(), a_before) and torch.equal(w.buf(), w_before), "an input was written"
