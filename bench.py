@@ -27,7 +27,7 @@ Per workload:
 
 value = N * rows * cols * 2 bytes of bf16 input / step time (GB/s).
 
-Prints one JSON line. --gpus above 1 is refused: this build measures one GPU.
+Prints one JSON line. --gpus above 1 is refused: the benchmark measures one GPU.
 """
 
 import argparse
@@ -1175,7 +1175,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU exchange is a design, not part of this build)", file=sys.stderr)
+              "(the multi-GPU exchange is designed, not implemented: one GPU is measured)", file=sys.stderr)
         sys.exit(2)
 
     import torch
