@@ -83,8 +83,9 @@ def parse():
                     help="skip the consumer measurement (decode + GEMM vs the fused decode-GEMM) of the "
                          "workloads whose gather stage has no Hadamard transform")
     ap.add_argument("--overlap", action="store_true",
-                    help="qwen-tp: also run the step concurrently with the bf16 GEMM that produces the "
-                         "next activation, on a second stream, and report the overlap")
+                    help="sweep launch caps of the codec beside the bf16 GEMM that produces the next "
+                         "activation (workloads with a GEMM, qwen-tp; without the flag only the uncapped "
+                         "overlap is measured)")
     ap.add_argument("--rank-share", action="store_true",
                     help="also time the decompress-reduce at one rank's share: (rows / N) x cols from N sources "
                          "(kept out of the default run so the profiled runs hold only full-size launches)")
@@ -1045,7 +1046,7 @@ def measure_reorder(w, ctx, stream, K):
 
 
 def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 128, 64)):
-    """The bf16 GEMM [rows, cols] x [cols, cols] that produces the next activation,
+    """The bf16 GEMM [rows, cols] x [cols, cols]^T (a weight in linear-layer layout) that produces the next activation,
     alone and concurrently with the codec step on a second stream (default
     priority), with the codec's launches capped at each of `caps` workgroups
     (taco_set_launch_limit; 0 = uncapped). Per cap: the codec step alone, both
@@ -1057,7 +1058,7 @@ def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 
     import quantized_compression_tensor_amd as T
     g_stream = torch.cuda.Stream()
     a = torch.randn(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
-    b = torch.randn(w.cols, w.cols, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(w.cols, w.cols, dtype=torch.bfloat16, device="cuda")   # a weight [N, K], linear-layer layout
     c = torch.empty(w.rows, w.cols, dtype=torch.bfloat16, device="cuda")
 
     def timed(fn):
@@ -1070,7 +1071,7 @@ def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 
 
     def gemm(i):
         with torch.cuda.stream(g_stream):
-            torch.matmul(a, b, out=c)
+            torch.matmul(a, b.t(), out=c)
 
     def codec(i):
         with torch.cuda.stream(stream):
@@ -1103,7 +1104,7 @@ def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 
     def consumer(i):
         with torch.cuda.stream(g_stream):
             T.taco_decompress(c_out, ctx["outs"][i % nsets], w.rows, w.cols, dec, 1, stream=g_stream.cuda_stream)
-            torch.matmul(dec, b, out=c)
+            torch.matmul(dec, b.t(), out=c)
 
     def decode_only(i):
         with torch.cuda.stream(g_stream):
@@ -1210,9 +1211,12 @@ def main():
         ring = measure_ring(w, ex["ctx"]["xs"][0], ex["stream"], K=max(10, args.steps // 4))
     reorder = measure_reorder(w, ex["ctx"], ex["stream"], K=max(16, args.steps)) if args.reorder else None
     overlap = None
-    if args.overlap:
+    if args.overlap or w.gemm:
+        # the workload's GEMM alone, the codec step alone and both on two streams; --overlap adds the sweep
+        # of launch caps
         overlap = measure_overlap(w, step_fn=ex["step"], nsets=ex["ctx"]["nsets"], stream=ex["stream"],
-                                  K=max(10, args.steps // 2), ctx=ex["ctx"])
+                                  K=max(10, args.steps // 2), ctx=ex["ctx"],
+                                  caps=(0, 1024, 512, 256, 128, 64) if args.overlap else (0,))
     del ex
     torch.cuda.empty_cache()
 
