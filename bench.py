@@ -197,6 +197,46 @@ def _csv_rows(d, suffix):
     return out
 
 
+def _trace_stats(trace_dir, concurrent_with, by_grid=()):
+    """Per-kernel statistics (calls, average, min, max, total in ns) from the
+    per-dispatch kernel trace, leaving out every dispatch that ran at the same
+    time as a dispatch of another kernel whose name contains one of the
+    patterns in `concurrent_with` (e.g. the codec launches timed beside a
+    library GEMM). Kernels whose name contains a pattern in `by_grid` are
+    kept apart by grid size (one kernel serving several shapes)."""
+    import bisect
+
+    def key(r):
+        n = r["Kernel_Name"]
+        grid = r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+        return f"{n} [grid {grid}]" if any(p in n for p in by_grid) else n
+    rows = [(key(r), int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+            for r in _csv_rows(trace_dir, "kernel_trace.csv")]
+    others = sorted((a, b, n) for n, a, b in rows if any(p in n for p in concurrent_with))
+    starts = [a for a, _, _ in others]
+    ends_max, m = [], 0      # running max of the ends, for the interval test
+    for _, b, _ in others:
+        m = max(m, b)
+        ends_max.append(m)
+    stats = {}
+    for n, a, b in rows:
+        if not any(p in n for p in concurrent_with):
+            # the other dispatches that start before this one ends; one of them
+            # overlaps it if the latest end among them lies after its start
+            i = bisect.bisect_left(starts, b) - 1
+            if i >= 0 and ends_max[i] > a:
+                continue
+        d = b - a
+        st = stats.setdefault(n, {"Calls": 0, "TotalDurationNs": 0, "MinNs": d, "MaxNs": d})
+        st["Calls"] += 1
+        st["TotalDurationNs"] += d
+        st["MinNs"] = min(st["MinNs"], d)
+        st["MaxNs"] = max(st["MaxNs"], d)
+    for st in stats.values():
+        st["AverageNs"] = st["TotalDurationNs"] / st["Calls"]
+    return stats
+
+
 def summarize(fetch_dir, write_dir, trace_dir, names, command, trace_log=None):
     """Per-launch HBM bytes of each workload's compress and reduce kernels from
     two counter passes, scaled by what the same counters read for a plain copy
@@ -229,7 +269,7 @@ def summarize(fetch_dir, write_dir, trace_dir, names, command, trace_log=None):
                     reverse=True)[:3]
     f_fetch = COPY_BYTES / (np.median(copy_f) * 1024) if copy_f else None
     f_write = COPY_BYTES / (np.median(copy_w) * 1024) if copy_w else None
-    trace = {row["Name"]: row for row in _csv_rows(trace_dir, "kernel_stats.csv")}
+    trace = _trace_stats(trace_dir, concurrent_with=("Cijk",))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     written = []
     for wname in names:
@@ -286,7 +326,8 @@ def summarize(fetch_dir, write_dir, trace_dir, names, command, trace_log=None):
             with open(path, "w") as fh:
                 fh.write(f"# rocprofv3 kernel-trace statistics: the kernels of workload {wname}\n"
                          f"# command: {command}\n")
-                fh.write("# (kernel durations exclude dispatch gaps; the bench's phase events include them)\n")
+                fh.write("# (kernel durations exclude dispatch gaps; the bench's phase events include them;\n"
+                         "# launches that ran at the same time as a library GEMM are left out)\n")
                 fh.write(f"source_hash: {src_hash}\n")
                 fh.write(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
                 for name in sorted(set(mine), key=lambda n: -float(trace[n]["TotalDurationNs"])):
@@ -1121,6 +1162,14 @@ def measure_overlap(w, step_fn, nsets, stream, K, ctx, caps=(0, 1024, 512, 256, 
                          "decode_share": round((cons_ms - gemm2_ms) / cons_ms, 4)}}
 
 
+def _short(name):
+    """A kernel name cut to 100 characters, keeping a trailing [grid ...] tag."""
+    if " [grid " in name:
+        base, tag = name.rsplit(" [grid ", 1)
+        return f"{base[:100]} [grid {tag}"
+    return name[:140]
+
+
 def summarize_consumer(trace_dir, mfma_dir, command):
     """Kernel-trace statistics of the consumer kernels (the fused decode-GEMM,
     the library GEMM, the bf16 decode) and the fused kernel's MFMA counters:
@@ -1131,11 +1180,12 @@ def summarize_consumer(trace_dir, mfma_dir, command):
              f"# command: {command}",
              f"source_hash: {kernel_source_hash()}",
              " calls    avg_us    min_us    max_us  kernel"]
-    for r in sorted(_csv_rows(trace_dir, "kernel_stats.csv"), key=lambda r: -float(r["AverageNs"])):
-        n = r["Name"]
+    stats = _trace_stats(trace_dir, concurrent_with=("k_fp8_had_compress", "k_reduce", "k_quantize"),
+                         by_grid=("Cijk", "k_dequant_gemm"))
+    for n, r in sorted(stats.items(), key=lambda kv: -float(kv[1]["AverageNs"])):
         if any(k in n for k in keep) and ("k_dequantize" not in n or ", true, false>" in n):
             lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
-                         f"{float(r['MaxNs']) / 1e3:9.2f}  {n[:140]}")
+                         f"{float(r['MaxNs']) / 1e3:9.2f}  {_short(n)}")
     per = {}
     for row in _csv_rows(mfma_dir, "counter_collection.csv"):
         n = row.get("Kernel_Name", "")
