@@ -44,3 +44,26 @@ def test_algorithmic_bytes_per_element(name):
     # shard, far below one part in 10^5 of these sizes
     assert comp == pytest.approx(want_c * w.n, rel=1e-5, abs=16)
     assert red == pytest.approx(want_r * w.n, rel=1e-5, abs=16 * (w.shards + 1))
+
+
+def test_trace_stats_leave_out_launches_beside_a_gemm(tmp_path):
+    """Per-kernel statistics from a kernel trace drop every dispatch that ran at
+    the same time as a library GEMM, keep the GEMM's own dispatches, and can
+    split a kernel by grid size."""
+    import bench
+    rows = [("Cijk_gemm", 100, 200, 65536), ("Cijk_gemm", 300, 400, 4096),
+            ("taco::k_reduce", 50, 90, 1024),      # before the first GEMM: kept
+            ("taco::k_reduce", 150, 170, 1024),    # inside it: dropped
+            ("taco::k_reduce", 190, 260, 1024),    # overlaps its end: dropped
+            ("taco::k_reduce", 200, 300, 1024),    # touches both ends only: kept
+            ("taco::k_reduce", 410, 450, 1024)]    # after the last: kept
+    lines = ['"Kernel_Name","Start_Timestamp","End_Timestamp","Grid_Size_X"']
+    lines += [f'"{n}",{a},{b},{g}' for n, a, b, g in rows]
+    (tmp_path / "run_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    st = bench._trace_stats(str(tmp_path), concurrent_with=("Cijk",))
+    assert st["taco::k_reduce"]["Calls"] == 3
+    assert st["taco::k_reduce"]["AverageNs"] == (40 + 100 + 40) / 3
+    assert st["Cijk_gemm"]["Calls"] == 2
+    split = bench._trace_stats(str(tmp_path), concurrent_with=(), by_grid=("Cijk",))
+    assert split["Cijk_gemm [grid 65536]"]["Calls"] == 1 and split["Cijk_gemm [grid 4096]"]["Calls"] == 1
+    assert split["taco::k_reduce"]["Calls"] == 5
