@@ -1042,6 +1042,29 @@ def measure_reorder(w, ctx, stream, K):
             torch.cuda.synchronize()
             times.setdefault(reordered, []).append(a.elapsed_time(b) / K)
     t_plain, t_re = min(times[False]), min(times[True])
+    # the decode to bf16, plain and restoring the channel order
+    dec = torch.empty(w.n, dtype=torch.bfloat16, device=dev)
+
+    def run_dec(reordered):
+        for i in range(K):
+            src = bufs[i % w.shards]
+            if reordered:
+                T.taco_decompress_reordered(c_in, src, w.rows, w.cols, dec, order, 1, stream=sh)
+            else:
+                T.taco_decompress(c_in, src, w.rows, w.cols, dec, 1, stream=sh)
+
+    dtimes = {}
+    with torch.cuda.stream(stream):
+        for reordered in (False, True, False, True):
+            run_dec(reordered)
+            a, b = mk(), mk()
+            a.record(stream)
+            run_dec(reordered)
+            b.record(stream)
+            torch.cuda.synchronize()
+            dtimes.setdefault(reordered, []).append(a.elapsed_time(b) / K)
+    td_plain, td_re = min(dtimes[False]), min(dtimes[True])
+    del dec
     b_comp, _ = algorithmic_bytes(w)
     # quality on sampled rows, GPU and oracle, plain and reordered
     ch = W.sample_chunks(w, 3, seed=7)
@@ -1083,6 +1106,7 @@ def measure_reorder(w, ctx, stream, K):
     return {"order_from": "input set 1, rank 0 (an earlier step's activation)",
             "compress_ms_plain": round(t_plain, 5), "compress_ms_reordered": round(t_re, 5),
             "compress_hbm_frac_reordered": round(b_comp / (t_re * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_bf16_ms_plain": round(td_plain, 5), "decode_bf16_ms_reordered": round(td_re, 5),
             "sample_rows": int(len(idx)), "tensor_scale": "given 2^-9 (FP8 codecs)", "quality": q}
 
 

@@ -494,7 +494,7 @@ TACO_DEV void quant_halves(float (*v)[8], float inv_g, float (*pre)[8], LaneCode
 template <int FMT, int B, bool F32IN, bool DEBUG, bool REORD = false>
 __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   static_assert(!(REORD && (F32IN || DEBUG)), "the reordering compress takes bf16 input");
-  extern __shared__ int16_t lds_order[];
+  extern __shared__ __attribute__((aligned(16))) int16_t lds_order[];
   if constexpr (REORD) load_order_lds(a.ro, lds_order);
   constexpr int V = 8;                      // elements per lane and half
   constexpr int HALF = kWaveElems / 2;      // 512
@@ -533,31 +533,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.g_hdr = g;
   }
   float run_max = 0.0f;
-  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
-    const int64_t base = t * kWaveElems;
-    const int rt = t == ntiles - 1 ? tail : kWaveElems;   // elements of this tile
-    const rsrc_t rx = make_rsrc32(static_cast<const uint8_t*>(a.x) + base * ES, rt * ES);
-    uint4 raw[2][NQ];
-    if constexpr (REORD) {
-      // each half is one 512-element span of a row; the lane holding group j
-      // of it loads group order[j] of that row
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // the second half of a ragged last tile lies past the end: empty
-        // resource, no lookup
-        const int64_t e0 = base + h * HALF;
-        const bool live = e0 < a.n;
-        const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
-        const rsrc_t rr = make_rsrc32(static_cast<const uint16_t*>(a.x) + (int64_t)p.row * a.ro.cols,
-                                      live ? a.ro.cols * 2 : 0);
-        raw[h][0] = bload128<kNT>(rr, live ? reordered_group(lds_order, p, lane) * kGroupElems * 2 : 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) raw[h][q] = bload128<kNT>(rx, lane * V * ES + 16 * q, h * HALF * ES);
-    }
+  // quantize and store tile `base` (rt elements) from its loaded lanes
+  auto finish = [&](int64_t base, int rt, uint4 (&raw)[2][NQ]) {
     float v[2][V];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -600,6 +577,70 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
                     rd, lane * V * 4 + 16 * q, h * HALF * 4);
       }
     }
+  };
+  bool done = false;
+  if constexpr (REORD) {
+    if (a.ro.staged) {
+      // rows through LDS in units of stage_rows rows (a multiple of 1024
+      // elements): a unit is loaded contiguously, then each lane reads group
+      // order[j] of its span's row from LDS; the unit's tiles are the
+      // tensor's tiles
+      uint16_t* rows_lds = reinterpret_cast<uint16_t*>(lds_order) + reorder_stage_offset(a.ro);
+      const int cols = a.ro.cols, ur = a.ro.stage_rows;
+      const int64_t nrows = a.n / cols, npairs = (nrows + ur - 1) / ur;
+      for (int64_t rp = blockIdx.x; rp < npairs; rp += gridDim.x) {
+        const int64_t pbase = rp * ur * cols;
+        const int pelems = (int)(a.n - pbase < (int64_t)ur * cols ? a.n - pbase : (int64_t)ur * cols);
+        const rsrc_t rrow = make_rsrc32(static_cast<const uint16_t*>(a.x) + pbase, pelems * 2);
+        for (int i = (int)threadIdx.x; i < pelems / 8; i += kBlockThreads)
+          *reinterpret_cast<uint4*>(rows_lds + 8 * i) = bload128<kNT>(rrow, 16 * i, 0);
+        __syncthreads();
+        for (int lt = wave_in_group(); lt * kWaveElems < pelems; lt += kBlockThreads / kWave) {
+          const int64_t base = pbase + (int64_t)lt * kWaveElems;
+          const int rt = a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems;
+          uint4 raw[2][NQ];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e0 = lt * kWaveElems + h * HALF;   // span start inside the unit
+            const bool live = e0 < pelems;
+            const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+            const int src = live ? lds_order[(col0 >> 3) + lane] : 0;
+            raw[h][0] = live ? *reinterpret_cast<const uint4*>(rows_lds + lrow * cols + src * kGroupElems)
+                             : make_uint4(0, 0, 0, 0);
+          }
+          finish(base, rt, raw);
+        }
+        __syncthreads();   // the unit's LDS rows are read before the next unit's load
+      }
+      done = true;
+    }
+  }
+  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); !done && t < ntiles; t += stride) {
+    const int64_t base = t * kWaveElems;
+    const int rt = t == ntiles - 1 ? tail : kWaveElems;   // elements of this tile
+    const rsrc_t rx = make_rsrc32(static_cast<const uint8_t*>(a.x) + base * ES, rt * ES);
+    uint4 raw[2][NQ];
+    if constexpr (REORD) {
+      // each half is one 512-element span of a row; the lane holding group j
+      // of it loads group order[j] of that row
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // the second half of a ragged last tile lies past the end: empty
+        // resource, no lookup
+        const int64_t e0 = base + h * HALF;
+        const bool live = e0 < a.n;
+        const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
+        const rsrc_t rr = make_rsrc32(static_cast<const uint16_t*>(a.x) + (int64_t)p.row * a.ro.cols,
+                                      live ? a.ro.cols * 2 : 0);
+        raw[h][0] = bload128<kNT>(rr, live ? reordered_group(lds_order, p, lane) * kGroupElems * 2 : 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) raw[h][q] = bload128<kNT>(rx, lane * V * ES + 16 * q, h * HALF * ES);
+    }
+    finish(base, rt, raw);
   }
   if constexpr (is_fp8(FMT)) {
     if (a.ws != nullptr) {
@@ -663,7 +704,7 @@ struct DequantK {
 // uses ordinary stores: the consumer reads it next.
 template <int FMT, int B, bool BF16OUT, bool REORD = false>
 __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
-  extern __shared__ int16_t lds_order[];
+  extern __shared__ __attribute__((aligned(16))) int16_t lds_order[];
   if constexpr (REORD) load_order_lds(a.ro, lds_order);
   constexpr int V = 8;
   constexpr int HALF = kWaveElems / 2;
@@ -676,15 +717,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float g = 0.0f;
   if constexpr (is_fp8(FMT)) g = *a.g_hdr;
-  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
-  const int64_t base = t * kWaveElems;
-  const int rt = t == ntiles - 1 ? (int)(a.n - base) : kWaveElems;   // a multiple of B
-  const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
-  const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
-  const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
-  const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + base * (BF16OUT ? 2 : 4), rt * (BF16OUT ? 2 : 4));
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  constexpr int OB = BF16OUT ? 2 : 4;   // output bytes per element
+  // the lane's 8 decoded values of half h of tile `base` (rt elements)
+  auto decode = [&](int64_t base, int rt, int h, float* d) {
+    const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
+    const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
+    const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
     LaneIn<FMT, B> in;
     if constexpr (FMT == kINT4A) in.q = make_uint4(bload32(rc, lane * 4, h * HALF / 2), 0, 0, 0);
     else {
@@ -700,33 +738,85 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
       in.s = __uint_as_float(bload32(rs, 4 * (lane / G), 4 * h * BPH));
       if constexpr (ASYM) in.z = bload8(rz, lane / G, h * BPH);
     }
-    float d[V];
     dequant_lane<FMT, B, V>(in, d);
-    // output resource and this lane's offset in it: the tile, or (reordered)
-    // the row of this half's span, where group j goes back to group order[j]
-    constexpr int OB = BF16OUT ? 2 : 4;   // output bytes per element
-    rsrc_t rdst = rout;
-    int doff = lane * V * OB, dsoff = h * HALF * OB;
-    if constexpr (REORD) {
-      const int64_t e0 = base + h * HALF;
-      const bool live = e0 < a.n;   // else: the empty half of a ragged last tile
-      const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
-      rdst = make_rsrc32(static_cast<uint8_t*>(a.out) + ((int64_t)p.row * a.ro.cols) * OB, live ? a.ro.cols * OB : 0);
-      doff = live ? reordered_group(lds_order, p, lane) * kGroupElems * OB : 0;
-      dsoff = 0;
-    }
+  };
+  // the output bytes of 8 values: one 16-byte word (bf16) or two (float32)
+  auto out_words = [&](const float* d, uint4* w) {
     if constexpr (BF16OUT) {
-      bstore128<0>(make_uint4(f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16), f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16),
-                              f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16), f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16)),
-                   rdst, doff, dsoff);
+      w[0] = make_uint4(f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16), f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16),
+                        f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16), f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16));
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        bstore128<0>(make_uint4(__float_as_uint(d[4 * q]), __float_as_uint(d[4 * q + 1]), __float_as_uint(d[4 * q + 2]),
-                                __float_as_uint(d[4 * q + 3])),
-                     rdst, doff + 16 * q, dsoff);
+        w[q] = make_uint4(__float_as_uint(d[4 * q]), __float_as_uint(d[4 * q + 1]), __float_as_uint(d[4 * q + 2]),
+                          __float_as_uint(d[4 * q + 3]));
+    }
+  };
+  constexpr int NW = BF16OUT ? 1 : 2;
+  if constexpr (REORD) {
+    if (a.ro.staged) {
+      // rows through LDS in units of stage_rows rows: each lane writes its
+      // decoded group j to group order[j] of its span's row in LDS, then the
+      // unit is stored contiguously
+      uint8_t* rows_lds = reinterpret_cast<uint8_t*>(lds_order) + 2 * reorder_stage_offset(a.ro);
+      const int cols = a.ro.cols, ur = a.ro.stage_rows;
+      const int64_t nrows = a.n / cols, npairs = (nrows + ur - 1) / ur;
+      for (int64_t rp = blockIdx.x; rp < npairs; rp += gridDim.x) {
+        const int64_t pbase = rp * ur * cols;
+        const int pelems = (int)(a.n - pbase < (int64_t)ur * cols ? a.n - pbase : (int64_t)ur * cols);
+        for (int lt = wave_in_group(); lt * kWaveElems < pelems; lt += kBlockThreads / kWave) {
+          const int64_t base = pbase + (int64_t)lt * kWaveElems;
+          const int rt = a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float d[V];
+            decode(base, rt, h, d);
+            const int e0 = lt * kWaveElems + h * HALF;   // span start inside the unit
+            if (e0 < pelems) {
+              const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+              const int dst = lds_order[(col0 >> 3) + lane];
+              uint4 w[NW];
+              out_words(d, w);
+              uint4* p = reinterpret_cast<uint4*>(rows_lds + ((int64_t)lrow * cols + dst * kGroupElems) * OB);
+#pragma unroll
+              for (int q = 0; q < NW; ++q) p[q] = w[q];
+            }
+          }
+        }
+        __syncthreads();
+        const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + pbase * OB, pelems * OB);
+        for (int i = (int)threadIdx.x; i < pelems * OB / 16; i += kBlockThreads)
+          bstore128<0>(*reinterpret_cast<const uint4*>(rows_lds + 16 * i), rout, 16 * i, 0);
+        __syncthreads();   // the unit's LDS rows are stored before the next unit's decode
+      }
+      return;
     }
   }
+  for (int64_t t = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); t < ntiles; t += stride) {
+    const int64_t base = t * kWaveElems;
+    const int rt = t == ntiles - 1 ? (int)(a.n - base) : kWaveElems;   // a multiple of B
+    const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + base * OB, rt * OB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float d[V];
+      decode(base, rt, h, d);
+      // output resource and this lane's offset in it: the tile, or (reordered)
+      // the row of this half's span, where group j goes back to group order[j]
+      rsrc_t rdst = rout;
+      int doff = lane * V * OB, dsoff = h * HALF * OB;
+      if constexpr (REORD) {
+        const int64_t e0 = base + h * HALF;
+        const bool live = e0 < a.n;   // else: the empty half of a ragged last tile
+        const SpanPos p = live ? span_pos(a.ro, e0) : SpanPos{0u, 0u};
+        rdst = make_rsrc32(static_cast<uint8_t*>(a.out) + ((int64_t)p.row * a.ro.cols) * OB, live ? a.ro.cols * OB : 0);
+        doff = live ? reordered_group(lds_order, p, lane) * kGroupElems * OB : 0;
+        dsoff = 0;
+      }
+      uint4 w[NW];
+      out_words(d, w);
+#pragma unroll
+      for (int q = 0; q < NW; ++q) bstore128<0>(w[q], rdst, doff + 16 * q, dsoff);
+    }
   }
 }
 
@@ -1070,12 +1160,28 @@ static dim3 quant_grid(const QuantArgs& a) { return grid_for(a.n); }
 
 static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
 
+// Staged reorder: the order and one unit of stage_rows rows of `elem_bytes`
+// per element; one workgroup per unit.
+static size_t staged_lds_bytes(const ReorderArgs& ro, int elem_bytes) {
+  return (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * elem_bytes;
+}
+static dim3 staged_grid(int64_t n, const ReorderArgs& ro) {
+  return capped_grid((n / ro.cols + ro.stage_rows - 1) / ro.stage_rows);
+}
+
 template <int FMT, int B>
 static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
   dim3 grid = quant_grid(a), block(kBlockThreads);
   if constexpr (!is_fp8(FMT) || B == 128) {
     if (a.ro.order != nullptr) {   // bf16 input, no debug output (checked by the caller)
-      hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), grid, block, order_lds_bytes(a.ro), s, k);
+      QuantK ks = k;
+      ks.ro.stage_rows = stage_rows_for(a.ro.cols, 2);
+      ks.ro.staged = ks.ro.stage_rows > 0;
+      if (ks.ro.staged)
+        hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), staged_grid(a.n, ks.ro), block,
+                           staged_lds_bytes(ks.ro, 2), s, ks);
+      else
+        hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), grid, block, order_lds_bytes(a.ro), s, ks);
       return;
     }
   }
@@ -1131,7 +1237,10 @@ static void launch_dq(const DequantArgs& a, hipStream_t s) {
   dim3 grid = grid_for(a.n), block(kBlockThreads);
   if constexpr (!is_fp8(FMT) || B == 128) {
     if (a.ro.order != nullptr) {
-      const size_t lds = order_lds_bytes(a.ro);
+      k.ro.stage_rows = stage_rows_for(a.ro.cols, a.bf16_out ? 2 : 4);
+      k.ro.staged = k.ro.stage_rows > 0;
+      const size_t lds = k.ro.staged ? staged_lds_bytes(k.ro, a.bf16_out ? 2 : 4) : order_lds_bytes(a.ro);
+      if (k.ro.staged) grid = staged_grid(a.n, k.ro);
       if (a.bf16_out) hipLaunchKernelGGL((k_dequantize<FMT, B, true, true>), grid, block, lds, s, k);
       else hipLaunchKernelGGL((k_dequantize<FMT, B, false, true>), grid, block, lds, s, k);
       return;

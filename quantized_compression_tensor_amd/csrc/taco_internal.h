@@ -26,9 +26,33 @@ struct ReorderArgs {
   int cols;                 // a multiple of 512
   uint32_t spans_per_row;   // cols / 512 (at most 256)
   uint64_t magic;           // ceil(2^38 / spans_per_row)
+  bool staged;              // INT codecs: rows staged through LDS (set per launch, stage_rows_for)
+  int stage_rows;           // rows per staged unit
 };
 constexpr int kReorderMaxCols = 131072;
 constexpr int kReorderColsMultiple = 512;
+// Widest row the INT reorder kernels stage through LDS; wider rows are
+// gathered from global memory group by group.
+constexpr int kReorderStageMaxCols = 16384;
+constexpr int kReorderStageMaxBytes = 65536;
+// Rows per staged unit for `elem_bytes` per element (0: not staged): the fewest
+// rows that hold whole 1024-element tiles and at least 8192 elements (about two
+// tiles per wave of a workgroup; larger units hold more LDS per workgroup and
+// fewer workgroups fit on a CU), within kReorderStageMaxBytes; else the fewest
+// that hold whole tiles.
+inline int stage_rows_for(int64_t cols, int elem_bytes) {
+  if (cols > kReorderStageMaxCols) return 0;
+  int first = 0;
+  for (int r = 1; r <= 16; ++r) {
+    if ((r * cols) % 1024 != 0 || r * cols * elem_bytes > kReorderStageMaxBytes) continue;
+    if (r * cols >= 8192) return r;
+    if (first == 0) first = r;
+  }
+  return first;
+}
+// LDS of the staged reorder kernels: the order (int16, rounded up to 16
+// bytes) and then the staged rows; the offset of the rows in int16 units.
+__host__ __device__ inline int reorder_stage_offset(const ReorderArgs& ro) { return (ro.ngroups + 7) & ~7; }
 inline ReorderArgs make_reorder(const int32_t* order, int64_t cols) {
   ReorderArgs r{};
   r.order = order;
@@ -37,6 +61,7 @@ inline ReorderArgs make_reorder(const int32_t* order, int64_t cols) {
     r.cols = (int)cols;
     r.spans_per_row = (uint32_t)(cols / 512);
     r.magic = ((uint64_t(1) << 38) + r.spans_per_row - 1) / r.spans_per_row;
+
   }
   return r;
 }

@@ -20,7 +20,11 @@ pytestmark = pytest.mark.gpu
 
 CODECS = [cd.Codec.fp8(128, True), cd.Codec.fp8e5(128, True), cd.Codec.fp8(128, False), cd.Codec.int8_sym(),
           cd.Codec.int4_asym(), cd.Codec.int8_asym()]
-SHAPES = [(1, 512), (3, 1024), (37, 1536), (300, 4096), (64, 5120)]
+# The INT codecs stage rows through LDS (one row at a time when cols is a
+# multiple of 1024, else pairs) up to 16384 columns, while a unit stays within
+# 64 KiB, and gather from global memory beyond: 9728 (pairs) takes the staged
+# bf16 decode and the gathered float32 one, 16896 gathers throughout.
+SHAPES = [(1, 512), (3, 1024), (37, 1536), (300, 4096), (64, 5120), (7, 9728), (3, 16896)]
 
 
 def cid(oc):
