@@ -184,3 +184,37 @@ def test_full_size_reordered_compress_sampled_rows():
     it = torch.from_numpy(idx).to(DEV)
     assert (codes.view(w.rows, w.cols)[it].cpu().numpy().reshape(-1) == ref.codes).all()
     assert (k.view(w.rows, w.cols // 128)[it].cpu().numpy().reshape(-1) == ref.scale).all()
+
+
+@pytest.mark.parametrize("name", ["equarx", "flashcomm"])
+def test_full_size_staged_reorder_sampled_rows(name):
+    """The INT codecs' reordered compress and bf16 decode at the workload's full
+    size (rows staged through LDS: two rows per unit at 5120 columns, one at
+    8192), sampled row chunks against the oracle with the same order."""
+    w = W.WORKLOADS[name]
+    oc = cd.Codec(w.in_format, w.in_block, False)
+    c = ccodec(oc)
+    print(f"full-size staged reorder {name}: {w.rows}x{w.cols}", flush=True)
+    order = torch.empty(w.cols // 8, dtype=torch.int32, device=DEV)
+    stats = W.make_shard(w, 1, chunks=list(range(4)))
+    T.taco_chunk_order(upload_bits(stats), stats.shape[0], w.cols, order)
+    x = W.make_shard(w, 0)
+    buf = T.empty_compressed(c, w.rows, w.cols)
+    T.taco_compress_reordered(c, upload_bits(x), w.rows, w.cols, 1.0, buf, order)
+    dec = torch.empty(w.rows * w.cols, dtype=torch.int16, device=DEV)
+    T.taco_decompress_reordered(c, buf, w.rows, w.cols, dec, order, 1)
+    torch.cuda.synchronize()
+    o = order.cpu().numpy().astype(np.int64)
+    assert (o == oracle.chunk_order(stats)).all()
+    idx = W.chunk_rows(W.sample_chunks(w, 2, seed=11), w.rows)
+    ref = oracle.compress_reordered(oc, x[idx], o)
+    codes, sc, aux, _ = T.regions(buf, c, w.rows, w.cols)
+    it = torch.from_numpy(idx).to(DEV)
+    per_row = w.cols // (2 if oc.format == cd.INT4_ASYM else 1)
+    assert (codes.view(w.rows, per_row)[it].cpu().numpy().reshape(-1) == ref.codes).all(), "codes"
+    got_s = sc.view(w.rows, w.cols // oc.block)[it].cpu().numpy().reshape(-1)
+    assert (got_s.view(np.uint32) == ref.scale.astype(np.float32).view(np.uint32)).all(), "scales"
+    if ref.zero is not None:
+        assert (aux.view(w.rows, w.cols // oc.block)[it].cpu().numpy().reshape(-1) == ref.zero).all(), "zero points"
+    got_d = dec.view(w.rows, w.cols)[it].cpu().numpy().view(np.uint16).reshape(-1)
+    assert (got_d == oracle.decode_reordered(ref, o, "bf16").reshape(-1)).all(), "decode"
