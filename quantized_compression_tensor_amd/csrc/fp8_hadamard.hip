@@ -268,11 +268,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   __shared__ uint32_t lds_e;
   __shared__ float lds_g;
   __shared__ float lds_m[kBlockThreads / kWave];
-  extern __shared__ int16_t lds_order[];
+  extern __shared__ __attribute__((aligned(16))) int16_t lds_order[];
   if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
   const int row = lane / Gm::G;
+  bool staged = false;   // rows staged through LDS (reordered input, rows up to 16384 columns)
+  if constexpr (REORD) staged = ro.staged;
 
   const int64_t elems = nblocks << LOGB;
   const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
@@ -296,8 +298,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   }
   __builtin_amdgcn_sched_barrier(0);
   uint4 ra[T], rb[T];
-  load_chunk<LOGB, T, REORD>(x, c, elems, ls.elem_off, ro, lds_order, ra);
-  load_chunk<LOGB, T, REORD>(x, c + stride, elems, ls.elem_off, ro, lds_order, rb);
+  if (!staged) {
+    load_chunk<LOGB, T, REORD>(x, c, elems, ls.elem_off, ro, lds_order, ra);
+    load_chunk<LOGB, T, REORD>(x, c + stride, elems, ls.elem_off, ro, lds_order, rb);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // On the persistent grid the first chunk is transformed while the ticket
   // returns; only its scaling and encoding wait for the tensor scale.
@@ -326,6 +330,43 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
   }
   const float inv_g = 1.0f / g;
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_hdr = g;
+
+  if constexpr (REORD) {
+    if (staged) {
+      // units of stage_rows whole rows (a multiple of the chunk): loaded into
+      // LDS contiguously, then the lane that holds group j of a span takes
+      // group order[j] of the span's row from LDS; the unit's chunks are the
+      // tensor's chunks
+      uint16_t* rows_lds = reinterpret_cast<uint16_t*>(lds_order) + reorder_stage_offset(ro);
+      const int cols = ro.cols, ur = ro.stage_rows;
+      const int64_t nrows = elems / cols, nunits = (nrows + ur - 1) / ur;
+      for (int64_t rp = blockIdx.x; rp < nunits; rp += gridDim.x) {
+        const int64_t pbase = rp * ur * cols;
+        const int pelems = (int)(elems - pbase < (int64_t)ur * cols ? elems - pbase : (int64_t)ur * cols);
+        const rsrc_t rrow = make_rsrc32(x + pbase, pelems * 2);
+        for (int i = (int)threadIdx.x; i < pelems / 8; i += kBlockThreads)
+          *reinterpret_cast<uint4*>(rows_lds + 8 * i) = bload128<kNT>(rrow, 16 * i, 0);
+        __syncthreads();
+        for (int lc = wave_in_group(); lc * CH::ELEMS < pelems; lc += kBlockThreads / kWave) {
+          uint4 raw[T];
+#pragma unroll
+          for (int i = 0; i < T; ++i) {
+            const int e0 = lc * CH::ELEMS + i * kTileElems;   // span start inside the unit
+            const bool live = e0 < pelems;
+            const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+            const int src = live ? lds_order[(col0 >> 3) + ls.elem_off / kGroupElems] : 0;
+            raw[i] = live ? *reinterpret_cast<const uint4*>(rows_lds + lrow * cols + src * kGroupElems)
+                          : make_uint4(0, 0, 0, 0);
+          }
+          had_compress_chunk<LOGB, T, E5, DEBUG>(raw, pbase / CH::ELEMS + lc, elems, ls, row, inv_g, codes, kexp,
+                                                 dbg, run_max);
+        }
+        __syncthreads();   // the unit's LDS rows are read before the next unit's load
+      }
+      if (ws != nullptr) ws_record_group(ws, e, run_max, lds_m);
+      return;
+    }
+  }
 
   if (c < nchunks) {
     // first chunk (ra), then the chunks alternate between rb and ra
@@ -476,17 +517,17 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
 static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
 
 template <int LOGB, int T, bool E5, bool DEBUG, bool PERSIST, bool REORD = false>
-static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s) {
+static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s, const ReorderArgs& ro,
+                              size_t lds = 0) {
   dim3 block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
-  const size_t lds = REORD ? order_lds_bytes(a.ro) : 0;
   if (a.g_from_ws)
     hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
-                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, a.ro);
+                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, ro);
   else
     hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
-                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, a.ro);
+                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, ro);
 }
 
 // Grid. Tensors of fewer than 2^16 large chunks take the small chunks on a
@@ -511,7 +552,17 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
       if (a.auto_prepass)
         hipLaunchKernelGGL((k_fp8_had_amax<LOGB, true>), big_grid, block, order_lds_bytes(a.ro), s, x, a.nblocks, ws,
                            a.ro);
-      launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, big_grid, s);
+      // rows staged through LDS in units of whole chunks, else gathered
+      ReorderArgs ro = a.ro;
+      ro.stage_rows = stage_rows_for(ro.cols, 2, kChunkTiles * kTileElems);
+      ro.staged = ro.stage_rows > 0;
+      if (ro.staged) {
+        const int64_t units = (elems / ro.cols + ro.stage_rows - 1) / ro.stage_rows;
+        const size_t lds = (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * 2;
+        launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, capped_grid(units), s, ro, lds);
+      } else {
+        launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, big_grid, s, ro, order_lds_bytes(a.ro));
+      }
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
@@ -521,10 +572,10 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
   if (small) {
     const int64_t need = had_groups(LOGB, a.nblocks, kSmallChunkTiles);
     const int64_t cap = (int64_t)device_cu_count() * kPersistentGroupsPerCU;
-    launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, capped_grid(need < cap ? need : cap), s);
+    launch_compress_t<LOGB, kSmallChunkTiles, E5, false, true>(a, capped_grid(need < cap ? need : cap), s, a.ro);
   } else {
-    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, big_grid, s);   // test hook: the large chunks
-    else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, big_grid, s);
+    if (a.dbg) launch_compress_t<LOGB, kChunkTiles, E5, true, false>(a, big_grid, s, a.ro);   // test hook: the large chunks
+    else launch_compress_t<LOGB, kChunkTiles, E5, false, false>(a, big_grid, s, a.ro);
   }
   return hipGetLastError();
 }

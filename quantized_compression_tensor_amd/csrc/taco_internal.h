@@ -35,16 +35,17 @@ constexpr int kReorderColsMultiple = 512;
 // gathered from global memory group by group.
 constexpr int kReorderStageMaxCols = 16384;
 constexpr int kReorderStageMaxBytes = 65536;
-// Rows per staged unit for `elem_bytes` per element (0: not staged): the fewest
-// rows that hold whole 1024-element tiles and at least 8192 elements (about two
-// tiles per wave of a workgroup; larger units hold more LDS per workgroup and
-// fewer workgroups fit on a CU), within kReorderStageMaxBytes; else the fewest
-// that hold whole tiles.
-inline int stage_rows_for(int64_t cols, int elem_bytes) {
+// Rows per staged unit for `elem_bytes` per element and units that are
+// multiples of `align` elements (the kernel's tile or chunk; 0: not staged):
+// the fewest rows that hold whole units of `align` and at least 8192 elements
+// (about two 1024-element tiles per wave of a workgroup; larger units hold more
+// LDS per workgroup and fewer workgroups fit on a CU), within
+// kReorderStageMaxBytes; else the fewest that hold whole units.
+inline int stage_rows_for(int64_t cols, int elem_bytes, int align = 1024) {
   if (cols > kReorderStageMaxCols) return 0;
   int first = 0;
   for (int r = 1; r <= 16; ++r) {
-    if ((r * cols) % 1024 != 0 || r * cols * elem_bytes > kReorderStageMaxBytes) continue;
+    if ((r * cols) % align != 0 || r * cols * elem_bytes > kReorderStageMaxBytes) continue;
     if (r * cols >= 8192) return r;
     if (first == 0) first = r;
   }
