@@ -581,20 +581,24 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
   bool done = false;
   if constexpr (REORD) {
     if (a.ro.staged) {
-      // rows through LDS in units of stage_rows rows (a multiple of 1024
-      // elements): a unit is loaded contiguously, then each lane reads group
-      // order[j] of its span's row from LDS; the unit's tiles are the
-      // tensor's tiles
+      // rows through LDS in units of stage_rows rows (whole 1024-element
+      // tiles, at most kStageMaxElems elements): a unit is loaded
+      // contiguously, then each lane reads group order[j] of its span's row
+      // from LDS; the unit's tiles are the tensor's tiles. The next unit's
+      // loads are issued into registers before this unit's tiles are
+      // quantized, so they are in flight during the arithmetic.
       uint16_t* rows_lds = reinterpret_cast<uint16_t*>(lds_order) + reorder_stage_offset(a.ro);
-      const int cols = a.ro.cols, ur = a.ro.stage_rows;
-      const int64_t nrows = a.n / cols, npairs = (nrows + ur - 1) / ur;
-      for (int64_t rp = blockIdx.x; rp < npairs; rp += gridDim.x) {
-        const int64_t pbase = rp * ur * cols;
-        const int pelems = (int)(a.n - pbase < (int64_t)ur * cols ? a.n - pbase : (int64_t)ur * cols);
-        const rsrc_t rrow = make_rsrc32(static_cast<const uint16_t*>(a.x) + pbase, pelems * 2);
-        for (int i = (int)threadIdx.x; i < pelems / 8; i += kBlockThreads)
-          *reinterpret_cast<uint4*>(rows_lds + 8 * i) = bload128<kNT>(rrow, 16 * i, 0);
+      const int cols = a.ro.cols;
+      const auto* x = static_cast<const uint16_t*>(a.x);
+      const StageUnits su(a.n, cols, a.ro.stage_rows);
+      uint4 next[8];
+      stage_issue(x, su, blockIdx.x, next);
+      for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
+        const int64_t pbase = su.base(u);
+        const int pelems = su.elems(u);
+        stage_commit(next, reinterpret_cast<uint4*>(rows_lds), pelems);
         __syncthreads();
+        stage_issue(x, su, u + gridDim.x, next);
         for (int lt = wave_in_group(); lt * kWaveElems < pelems; lt += kBlockThreads / kWave) {
           const int64_t base = pbase + (int64_t)lt * kWaveElems;
           const int rt = a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems;
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_quantize(QuantK a) {
           }
           finish(base, rt, raw);
         }
-        __syncthreads();   // the unit's LDS rows are read before the next unit's load
+        __syncthreads();   // the unit's LDS rows are read before the next unit's are written
       }
       done = true;
     }
@@ -718,8 +722,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   float g = 0.0f;
   if constexpr (is_fp8(FMT)) g = *a.g_hdr;
   constexpr int OB = BF16OUT ? 2 : 4;   // output bytes per element
-  // the lane's 8 decoded values of half h of tile `base` (rt elements)
-  auto decode = [&](int64_t base, int rt, int h, float* d) {
+  // the lane's codes, scale and zero point of half h of tile `base` (rt elements)
+  auto load_in = [&](int64_t base, int rt, int h) {
     const rsrc_t rc = make_rsrc32(a.codes + base / CB, rt / CB);
     const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (base / B) * MB, (rt / B) * MB);
     const rsrc_t rz = make_rsrc32(ASYM ? a.zero + base / B : a.codes, ASYM ? rt / B : 0);
@@ -738,8 +742,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
       in.s = __uint_as_float(bload32(rs, 4 * (lane / G), 4 * h * BPH));
       if constexpr (ASYM) in.z = bload8(rz, lane / G, h * BPH);
     }
-    dequant_lane<FMT, B, V>(in, d);
+    return in;
   };
+  // the lane's 8 decoded values of half h of tile `base`
+  auto decode = [&](int64_t base, int rt, int h, float* d) { dequant_lane<FMT, B, V>(load_in(base, rt, h), d); };
   // the output bytes of 8 values: one 16-byte word (bf16) or two (float32)
   auto out_words = [&](const float* d, uint4* w) {
     if constexpr (BF16OUT) {
@@ -755,38 +761,51 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   constexpr int NW = BF16OUT ? 1 : 2;
   if constexpr (REORD) {
     if (a.ro.staged) {
-      // rows through LDS in units of stage_rows rows: each lane writes its
-      // decoded group j to group order[j] of its span's row in LDS, then the
-      // unit is stored contiguously
+      // rows through LDS in units of stage_rows rows (whole 1024-element
+      // tiles, at most kStageMaxElems elements): the waves take the unit's
+      // tiles in turn, four at a time with their loads in flight together,
+      // and each lane writes its decoded group j to group order[j] of its
+      // span's row in LDS; then the unit is stored contiguously. (Holding the
+      // next unit's loads in registers as well measured slower here: the
+      // registers cost more workgroups per CU than the early loads gain.)
+      constexpr int WG = kBlockThreads / kWave;
       uint8_t* rows_lds = reinterpret_cast<uint8_t*>(lds_order) + 2 * reorder_stage_offset(a.ro);
-      const int cols = a.ro.cols, ur = a.ro.stage_rows;
-      const int64_t nrows = a.n / cols, npairs = (nrows + ur - 1) / ur;
-      for (int64_t rp = blockIdx.x; rp < npairs; rp += gridDim.x) {
-        const int64_t pbase = rp * ur * cols;
-        const int pelems = (int)(a.n - pbase < (int64_t)ur * cols ? a.n - pbase : (int64_t)ur * cols);
-        for (int lt = wave_in_group(); lt * kWaveElems < pelems; lt += kBlockThreads / kWave) {
-          const int64_t base = pbase + (int64_t)lt * kWaveElems;
-          const int rt = a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems;
+      const int cols = a.ro.cols;
+      const StageUnits su(a.n, cols, a.ro.stage_rows);
+      for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
+        const int64_t pbase = su.base(u);
+        const int pelems = su.elems(u);
+        for (int lt0 = wave_in_group(); lt0 * kWaveElems < pelems; lt0 += 4 * WG) {
+          LaneIn<FMT, B> in[4][2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float d[V];
-            decode(base, rt, h, d);
-            const int e0 = lt * kWaveElems + h * HALF;   // span start inside the unit
-            if (e0 < pelems) {
-              const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
-              const int dst = lds_order[(col0 >> 3) + lane];
-              uint4 w[NW];
-              out_words(d, w);
-              uint4* p = reinterpret_cast<uint4*>(rows_lds + ((int64_t)lrow * cols + dst * kGroupElems) * OB);
+          for (int j = 0; j < 4; ++j) {   // tiles past the unit's end load nothing
+            const int lt = lt0 + j * WG;
+            const int64_t base = pbase + (int64_t)lt * kWaveElems;
+            const int rt = lt * kWaveElems >= pelems ? 0 : (a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems);
 #pragma unroll
-              for (int q = 0; q < NW; ++q) p[q] = w[q];
-            }
+            for (int h = 0; h < 2; ++h) in[j][h] = load_in(base, rt, h);
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float d[V];
+              dequant_lane<FMT, B, V>(in[j][h], d);
+              const int e0 = (lt0 + j * WG) * kWaveElems + h * HALF;   // span start inside the unit
+              if (e0 < pelems) {
+                const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+                const int dst = lds_order[(col0 >> 3) + lane];
+                uint4 w[NW];
+                out_words(d, w);
+                uint4* p = reinterpret_cast<uint4*>(rows_lds + ((int64_t)lrow * cols + dst * kGroupElems) * OB);
+#pragma unroll
+                for (int q = 0; q < NW; ++q) p[q] = w[q];
+              }
+            }
         }
         __syncthreads();
-        const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + pbase * OB, pelems * OB);
-        for (int i = (int)threadIdx.x; i < pelems * OB / 16; i += kBlockThreads)
-          bstore128<0>(*reinterpret_cast<const uint4*>(rows_lds + 16 * i), rout, 16 * i, 0);
+        stage_drain(reinterpret_cast<const uint4*>(rows_lds),
+                    make_rsrc32(static_cast<uint8_t*>(a.out) + pbase * OB, pelems * OB), pelems * OB / 16);
         __syncthreads();   // the unit's LDS rows are stored before the next unit's decode
       }
       return;
@@ -1161,13 +1180,11 @@ static dim3 quant_grid(const QuantArgs& a) { return grid_for(a.n); }
 static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
 
 // Staged reorder: the order and one unit of stage_rows rows of `elem_bytes`
-// per element; one workgroup per unit.
+// per element; the units of a tensor.
 static size_t staged_lds_bytes(const ReorderArgs& ro, int elem_bytes) {
   return (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * elem_bytes;
 }
-static dim3 staged_grid(int64_t n, const ReorderArgs& ro) {
-  return capped_grid((n / ro.cols + ro.stage_rows - 1) / ro.stage_rows);
-}
+static int64_t staged_units(int64_t n, const ReorderArgs& ro) { return (n / ro.cols + ro.stage_rows - 1) / ro.stage_rows; }
 
 template <int FMT, int B>
 static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
@@ -1175,12 +1192,14 @@ static void launch_q(const QuantArgs& a, const QuantK& k, hipStream_t s) {
   if constexpr (!is_fp8(FMT) || B == 128) {
     if (a.ro.order != nullptr) {   // bf16 input, no debug output (checked by the caller)
       QuantK ks = k;
-      ks.ro.stage_rows = stage_rows_for(a.ro.cols, 2);
+      ks.ro.stage_rows = stage_rows_for(a.ro.cols, kWaveElems);
       ks.ro.staged = ks.ro.stage_rows > 0;
-      if (ks.ro.staged)
-        hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), staged_grid(a.n, ks.ro), block,
-                           staged_lds_bytes(ks.ro, 2), s, ks);
-      else
+      if (ks.ro.staged) {
+        auto* kern = k_quantize<FMT, B, false, false, true>;
+        const size_t lds = staged_lds_bytes(ks.ro, 2);
+        hipLaunchKernelGGL(kern, resident_grid(reinterpret_cast<const void*>(kern), lds, staged_units(a.n, ks.ro)),
+                           block, lds, s, ks);
+      } else
         hipLaunchKernelGGL((k_quantize<FMT, B, false, false, true>), grid, block, order_lds_bytes(a.ro), s, ks);
       return;
     }
@@ -1237,10 +1256,10 @@ static void launch_dq(const DequantArgs& a, hipStream_t s) {
   dim3 grid = grid_for(a.n), block(kBlockThreads);
   if constexpr (!is_fp8(FMT) || B == 128) {
     if (a.ro.order != nullptr) {
-      k.ro.stage_rows = stage_rows_for(a.ro.cols, a.bf16_out ? 2 : 4);
+      k.ro.stage_rows = stage_rows_for(a.ro.cols, kWaveElems);
       k.ro.staged = k.ro.stage_rows > 0;
       const size_t lds = k.ro.staged ? staged_lds_bytes(k.ro, a.bf16_out ? 2 : 4) : order_lds_bytes(a.ro);
-      if (k.ro.staged) grid = staged_grid(a.n, k.ro);
+      if (k.ro.staged) grid = capped_grid(staged_units(a.n, k.ro));   // one workgroup per unit
       if (a.bf16_out) hipLaunchKernelGGL((k_dequantize<FMT, B, true, true>), grid, block, lds, s, k);
       else hipLaunchKernelGGL((k_dequantize<FMT, B, false, true>), grid, block, lds, s, k);
       return;

@@ -291,6 +291,47 @@ TACO_DEV int reordered_group(const int16_t* lds, const SpanPos& p, int lane_grou
   return lds[(p.col0 >> 3) + lane_group];
 }
 
+// Units of whole rows staged through LDS. A workgroup walks units
+// u = blockIdx.x, blockIdx.x + gridDim.x, ...; unit u starts at element
+// u * rows * cols and holds rows * cols elements (at most kStageMaxElems), the
+// last one possibly fewer.
+struct StageUnits {
+  int64_t n, per, count;
+  TACO_DEV StageUnits(int64_t n_, int cols, int rows)
+      : n(n_), per((int64_t)rows * cols), count((n_ / cols + rows - 1) / rows) {}
+  TACO_DEV int64_t base(int64_t u) const { return u * per; }
+  TACO_DEV int elems(int64_t u) const { return u >= count ? 0 : (int)(n - u * per < per ? n - u * per : per); }
+};
+static_assert(8 * 8 * kBlockThreads == kStageMaxElems, "a staged bf16 unit is eight 16-byte words per thread");
+
+// The loads of bf16 unit u into registers, eight 16-byte words per thread;
+// past the last unit, or past its end, zeros from the resource.
+TACO_DEV void stage_issue(const uint16_t* x, const StageUnits& su, int64_t u, uint4* next) {
+  const rsrc_t r = make_rsrc32(x + (u < su.count ? su.base(u) : 0), su.elems(u) * 2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) next[j] = bload128<kNT>(r, 16 * ((int)threadIdx.x + j * kBlockThreads), 0);
+}
+// The unit's words from registers into LDS (its first elems / 8 words).
+TACO_DEV void stage_commit(const uint4* next, uint4* lds, int elems) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int w = (int)threadIdx.x + j * kBlockThreads;
+    if (w < elems / 8) lds[w] = next[j];
+  }
+}
+// A decoded unit (n16 16-byte words) from LDS to global memory, eight words per
+// thread at once.
+TACO_DEV void stage_drain(const uint4* lds, rsrc_t dst, int n16) {
+  for (int i0 = (int)threadIdx.x; i0 < n16; i0 += 8 * kBlockThreads) {
+    uint4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = i0 + j * kBlockThreads < n16 ? lds[i0 + j * kBlockThreads] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (i0 + j * kBlockThreads < n16) bstore128<0>(t[j], dst, 16 * (i0 + j * kBlockThreads), 0);
+  }
+}
+
 // ------------------------------------------------------------- workspace --
 // Abs-max history of an FP8 tensor scale, in caller-owned memory that is
 // zero-filled once. Calls on one workspace are ordered (one stream), and any

@@ -333,35 +333,45 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
 
   if constexpr (REORD) {
     if (staged) {
-      // units of stage_rows whole rows (a multiple of the chunk): loaded into
-      // LDS contiguously, then the lane that holds group j of a span takes
-      // group order[j] of the span's row from LDS; the unit's chunks are the
-      // tensor's chunks
+      // units of stage_rows whole rows (at most kStageMaxElems elements):
+      // loaded into LDS contiguously, then the lane that holds group j of a
+      // span takes group order[j] of the span's row from LDS; the waves take
+      // the unit's tiles in turn, four at a time. The next unit's loads are
+      // issued into registers before this unit's tiles are encoded, so they
+      // are in flight during the arithmetic.
+      constexpr int NW = kBlockThreads / kWave;
       uint16_t* rows_lds = reinterpret_cast<uint16_t*>(lds_order) + reorder_stage_offset(ro);
-      const int cols = ro.cols, ur = ro.stage_rows;
-      const int64_t nrows = elems / cols, nunits = (nrows + ur - 1) / ur;
-      for (int64_t rp = blockIdx.x; rp < nunits; rp += gridDim.x) {
-        const int64_t pbase = rp * ur * cols;
-        const int pelems = (int)(elems - pbase < (int64_t)ur * cols ? elems - pbase : (int64_t)ur * cols);
-        const rsrc_t rrow = make_rsrc32(x + pbase, pelems * 2);
-        for (int i = (int)threadIdx.x; i < pelems / 8; i += kBlockThreads)
-          *reinterpret_cast<uint4*>(rows_lds + 8 * i) = bload128<kNT>(rrow, 16 * i, 0);
+      const int cols = ro.cols;
+      const StageUnits su(elems, cols, ro.stage_rows);
+      uint4 next[8];
+      stage_issue(x, su, blockIdx.x, next);
+      for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
+        const int64_t ubase = su.base(u);
+        const int uelems = su.elems(u);
+        const int utiles = uelems / kTileElems;   // cols is a multiple of the tile
+        stage_commit(next, reinterpret_cast<uint4*>(rows_lds), uelems);
         __syncthreads();
-        for (int lc = wave_in_group(); lc * CH::ELEMS < pelems; lc += kBlockThreads / kWave) {
-          uint4 raw[T];
+        stage_issue(x, su, u + gridDim.x, next);
+        for (int lt0 = wave_in_group(); lt0 < utiles; lt0 += 4 * NW) {
+          uint4 raw[4];
 #pragma unroll
-          for (int i = 0; i < T; ++i) {
-            const int e0 = lc * CH::ELEMS + i * kTileElems;   // span start inside the unit
-            const bool live = e0 < pelems;
+          for (int i = 0; i < 4; ++i) {
+            const int lt = lt0 + i * NW;
+            const int e0 = lt * kTileElems;   // span start inside the unit
             const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
-            const int src = live ? lds_order[(col0 >> 3) + ls.elem_off / kGroupElems] : 0;
-            raw[i] = live ? *reinterpret_cast<const uint4*>(rows_lds + lrow * cols + src * kGroupElems)
-                          : make_uint4(0, 0, 0, 0);
+            raw[i] = make_uint4(0, 0, 0, 0);
+            if (lt < utiles) {
+              const int src = lds_order[(col0 >> 3) + ls.elem_off / kGroupElems];
+              raw[i] = *reinterpret_cast<const uint4*>(rows_lds + lrow * cols + src * kGroupElems);
+            }
           }
-          had_compress_chunk<LOGB, T, E5, DEBUG>(raw, pbase / CH::ELEMS + lc, elems, ls, row, inv_g, codes, kexp,
-                                                 dbg, run_max);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (lt0 + i * NW < utiles)
+              had_compress_chunk<LOGB, 1, E5, DEBUG>(raw + i, ubase / kTileElems + lt0 + i * NW, elems, ls, row,
+                                                     inv_g, codes, kexp, dbg, run_max);
         }
-        __syncthreads();   // the unit's LDS rows are read before the next unit's load
+        __syncthreads();   // the unit's LDS rows are read before the next unit's are written
       }
       if (ws != nullptr) ws_record_group(ws, e, run_max, lds_m);
       return;
@@ -441,12 +451,27 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
 // inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
 // factor, then float32 or bf16 output. T wave tiles per wave as launched; a
 // smaller grid walks them with a stride of the grid.
+// One wave tile of the decode: the lane's eight codes times g * 2^-k, the
+// inverse transform (the forward one, which is its own inverse up to 2^-LOGB),
+// then 2^-LOGB and the lane's sign.
+template <bool E5, int LOGB>
+TACO_DEV void decode_tile(uint2 raw, float d, float outscale, const LaneSigns<LOGB>& ls, float* v) {
+  Fp8Code<E5>::unpack4(raw.x, v);
+  Fp8Code<E5>::unpack4(raw.y, v + 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = v[e] * d;
+  fwht_in_lane(v);
+  fwht_cross_lane<HadGeom<LOGB>::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], outscale, 0.0f);
+}
+
 template <int LOGB, bool E5, bool BF16OUT, int T, bool REORD>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
     int64_t nblocks, void* __restrict__ out, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
-  extern __shared__ int16_t lds_order[];
+  extern __shared__ __attribute__((aligned(16))) int16_t lds_order[];
   if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -455,6 +480,74 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
   const float g = *g_hdr;
   const float outscale = pow2f(-LOGB) * ls.parity;
   const int64_t ntiles = ((nblocks << LOGB) + kTileElems - 1) / kTileElems;
+  if constexpr (REORD) {
+    if (ro.staged) {
+      // units of stage_rows whole rows (at most kStageMaxElems elements, 32
+      // tiles): wave w decodes tiles w, w + 4, ... of the unit and each lane
+      // writes its decoded group j to group order[j] of the span's row in LDS;
+      // then the unit is stored contiguously. The next unit's codes and block
+      // exponents are loaded before this unit is decoded, so they are in
+      // flight during the arithmetic and the store.
+      constexpr int OB = BF16OUT ? 2 : 4;
+      constexpr int NW = kBlockThreads / kWave;
+      constexpr int TW = kStageMaxElems / kTileElems / NW;   // tiles per wave and unit, at most
+      uint8_t* rows_lds = reinterpret_cast<uint8_t*>(lds_order) + 2 * reorder_stage_offset(ro);
+      const int cols = ro.cols;
+      const StageUnits su(nblocks << LOGB, cols, ro.stage_rows);
+      uint2 nraw[TW];
+      int nk[TW];
+      auto issue = [&](int64_t u) {   // past the last unit, or past its end: zeros
+        const int64_t tb = u < su.count ? su.base(u) / kTileElems : 0;
+        const int ut = su.elems(u) / kTileElems;
+        const rsrc_t rc = make_rsrc32(codes + tb * kTileElems, ut * kTileElems);
+        const rsrc_t rk = make_rsrc32(kexp + tb * Gm::BPT, ut * Gm::BPT);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          const int lt = wave + i * NW;
+          nraw[i] = bload64<kNT>(rc, lt * kTileElems + ls.elem_off, 0);
+          nk[i] = (int)(int8_t)(uint8_t)bload8(rk, lt * Gm::BPT + row, 0);
+        }
+      };
+      issue(blockIdx.x);
+      for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
+        const int uelems = su.elems(u);
+        const int utiles = uelems / kTileElems;   // cols is a multiple of the tile
+        uint2 raw[TW];
+        int kk[TW];
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          raw[i] = nraw[i];
+          kk[i] = nk[i];
+        }
+        issue(u + gridDim.x);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+          const int lt = wave + i * NW;
+          if (lt < utiles) {
+            float v[8];
+            decode_tile<E5>(raw[i], g * pow2f(-kk[i]), outscale, ls, v);
+            const int e0 = lt * kTileElems;   // span start inside the unit
+            const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+            const int dst = lds_order[(col0 >> 3) + ls.elem_off / kGroupElems];
+            uint8_t* p = rows_lds + ((int64_t)lrow * cols + dst * kGroupElems) * OB;
+            if constexpr (BF16OUT) {
+              *reinterpret_cast<uint4*>(p) = make_uint4(
+                  f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16),
+                  f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16), f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16));
+            } else {
+              reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+              reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
+          }
+        }
+        __syncthreads();
+        stage_drain(reinterpret_cast<const uint4*>(rows_lds),
+                    make_rsrc32(static_cast<uint8_t*>(out) + su.base(u) * OB, uelems * OB), uelems * OB / 16);
+        __syncthreads();   // the unit is stored before the next unit's decode writes LDS
+      }
+      return;
+    }
+  }
   for (int64_t tile0 = ((int64_t)blockIdx.x * 4 + wave) * T; tile0 < ntiles; tile0 += (int64_t)gridDim.x * 4 * T) {
   uint2 raw[T];
   int kk[T];
@@ -471,16 +564,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const int64_t blk = (tile0 + i) * Gm::BPT + row;
-    const float d = g * pow2f(-kk[i]);
     float v[8];
-    Fp8Code<E5>::unpack4(raw[i].x, v);
-    Fp8Code<E5>::unpack4(raw[i].y, v + 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * d;
-    fwht_in_lane(v);
-    fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], outscale, 0.0f);
+    decode_tile<E5>(raw[i], g * pow2f(-kk[i]), outscale, ls, v);
     if (blk < nblocks) {
       // reordered: group j of this span goes back to group order[j] of its row
       int64_t eoff = (tile0 + i) * kTileElems + ls.elem_off;
@@ -516,18 +601,18 @@ static int64_t had_groups(int logb, int64_t nblocks, int T) {
 // Dynamic LDS of the reordering kernels: the order as int16.
 static size_t order_lds_bytes(const ReorderArgs& ro) { return ro.order ? ((size_t)ro.ngroups * 2 + 3) & ~size_t(3) : 0; }
 
+// walk_units > 0: the grid is every resident workgroup, at most walk_units
+// (a kernel that prefetches its next unit), instead of `grid`.
 template <int LOGB, int T, bool E5, bool DEBUG, bool PERSIST, bool REORD = false>
 static void launch_compress_t(const FP8HadArgs& a, dim3 grid, hipStream_t s, const ReorderArgs& ro,
-                              size_t lds = 0) {
+                              size_t lds = 0, int64_t walk_units = 0) {
   dim3 block(kBlockThreads);
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* ws = static_cast<Workspace*>(a.ws);
-  if (a.g_from_ws)
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
-                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, ro);
-  else
-    hipLaunchKernelGGL((k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST, REORD>), grid, block, lds, s, x, a.codes,
-                       a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, ro);
+  auto* kern = a.g_from_ws ? k_fp8_had_compress<LOGB, T, E5, true, DEBUG, PERSIST, REORD>
+                           : k_fp8_had_compress<LOGB, T, E5, false, DEBUG, PERSIST, REORD>;
+  if (walk_units > 0) grid = resident_grid(reinterpret_cast<const void*>(kern), lds, walk_units);
+  hipLaunchKernelGGL(kern, grid, block, lds, s, x, a.codes, a.kexp, a.g_hdr, a.nblocks, a.g, ws, a.dbg, ro);
 }
 
 // Grid. Tensors of fewer than 2^16 large chunks take the small chunks on a
@@ -552,14 +637,14 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
       if (a.auto_prepass)
         hipLaunchKernelGGL((k_fp8_had_amax<LOGB, true>), big_grid, block, order_lds_bytes(a.ro), s, x, a.nblocks, ws,
                            a.ro);
-      // rows staged through LDS in units of whole chunks, else gathered
+      // rows staged through LDS in units of whole rows, else gathered
       ReorderArgs ro = a.ro;
-      ro.stage_rows = stage_rows_for(ro.cols, 2, kChunkTiles * kTileElems);
+      ro.stage_rows = stage_rows_for(ro.cols, kTileElems);
       ro.staged = ro.stage_rows > 0;
       if (ro.staged) {
         const int64_t units = (elems / ro.cols + ro.stage_rows - 1) / ro.stage_rows;
         const size_t lds = (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * 2;
-        launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, capped_grid(units), s, ro, lds);
+        launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, dim3(1), s, ro, lds, units);
       } else {
         launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, big_grid, s, ro, order_lds_bytes(a.ro));
       }
@@ -595,17 +680,15 @@ hipError_t launch_fp8_had_compress(const FP8HadArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// walk_units > 0: the grid is every resident workgroup, at most walk_units.
 template <int LOGB, bool E5, bool REORD>
-static void launch_decode_fmt(const FP8HadDecodeArgs& a, dim3 grid, hipStream_t s) {
+static void launch_decode_fmt(const FP8HadDecodeArgs& a, dim3 grid, hipStream_t s, const ReorderArgs& ro,
+                              size_t lds, int64_t walk_units = 0) {
   constexpr int T = 2;
   dim3 block(kBlockThreads);
-  const size_t lds = REORD ? order_lds_bytes(a.ro) : 0;
-  if (a.bf16_out)
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, true, T, REORD>), grid, block, lds, s, a.codes, a.kexp, a.g_hdr,
-                       a.nblocks, a.out, a.ro);
-  else
-    hipLaunchKernelGGL((k_fp8_had_decode<LOGB, E5, false, T, REORD>), grid, block, lds, s, a.codes, a.kexp, a.g_hdr,
-                       a.nblocks, a.out, a.ro);
+  auto* kern = a.bf16_out ? k_fp8_had_decode<LOGB, E5, true, T, REORD> : k_fp8_had_decode<LOGB, E5, false, T, REORD>;
+  if (walk_units > 0) grid = resident_grid(reinterpret_cast<const void*>(kern), lds, walk_units);
+  hipLaunchKernelGGL(kern, grid, block, lds, s, a.codes, a.kexp, a.g_hdr, a.nblocks, a.out, ro);
 }
 
 template <int LOGB>
@@ -615,14 +698,25 @@ static hipError_t launch_decode_logb(const FP8HadDecodeArgs& a, hipStream_t s) {
   const dim3 grid = capped_grid(groups);
   if (a.ro.order != nullptr) {
     if constexpr (LOGB == 7) {
-      if (a.e5) launch_decode_fmt<LOGB, true, true>(a, grid, s);
-      else launch_decode_fmt<LOGB, false, true>(a, grid, s);
+      // rows staged through LDS in units of whole rows, else scattered
+      ReorderArgs ro = a.ro;
+      const int ob = a.bf16_out ? 2 : 4;
+      ro.stage_rows = stage_rows_for(ro.cols, kTileElems);
+      ro.staged = ro.stage_rows > 0;
+      size_t lds = order_lds_bytes(ro);
+      int64_t units = 0;
+      if (ro.staged) {
+        units = ((a.nblocks << LOGB) / ro.cols + ro.stage_rows - 1) / ro.stage_rows;
+        lds = (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * ob;
+      }
+      if (a.e5) launch_decode_fmt<LOGB, true, true>(a, grid, s, ro, lds, units);
+      else launch_decode_fmt<LOGB, false, true>(a, grid, s, ro, lds, units);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
   }
-  if (a.e5) launch_decode_fmt<LOGB, true, false>(a, grid, s);
-  else launch_decode_fmt<LOGB, false, false>(a, grid, s);
+  if (a.e5) launch_decode_fmt<LOGB, true, false>(a, grid, s, a.ro, 0);
+  else launch_decode_fmt<LOGB, false, false>(a, grid, s, a.ro, 0);
   return hipGetLastError();
 }
 

@@ -227,6 +227,35 @@ int device_cu_count() {
   return v;
 }
 
+int resident_groups(const void* kernel, size_t lds) {
+  struct Entry {
+    const void* kernel;
+    size_t lds;
+    int dev, groups;
+  };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].kernel == kernel && cache[i].lds == lds && cache[i].dev == dev) return cache[i].groups;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, lds) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 64) cache[used++] = Entry{kernel, lds, dev, n};
+  return n;
+}
+
 }  // namespace taco
 
 namespace {

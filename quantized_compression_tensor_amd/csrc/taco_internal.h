@@ -26,26 +26,27 @@ struct ReorderArgs {
   int cols;                 // a multiple of 512
   uint32_t spans_per_row;   // cols / 512 (at most 256)
   uint64_t magic;           // ceil(2^38 / spans_per_row)
-  bool staged;              // INT codecs: rows staged through LDS (set per launch, stage_rows_for)
+  bool staged;              // rows staged through LDS (set per launch, stage_rows_for)
   int stage_rows;           // rows per staged unit
 };
 constexpr int kReorderMaxCols = 131072;
 constexpr int kReorderColsMultiple = 512;
-// Widest row the INT reorder kernels stage through LDS; wider rows are
-// gathered from global memory group by group.
-constexpr int kReorderStageMaxCols = 16384;
-constexpr int kReorderStageMaxBytes = 65536;
-// Rows per staged unit for `elem_bytes` per element and units that are
-// multiples of `align` elements (the kernel's tile or chunk; 0: not staged):
-// the fewest rows that hold whole units of `align` and at least 8192 elements
+// Largest unit of whole rows the reorder kernels stage through LDS (rows at
+// most this wide; wider rows are gathered from global memory group by group).
+// A staging workgroup holds the next unit's loads in registers: 16384 bf16
+// elements are eight 16-byte words per thread of 256, 16384 FP8 codes eight
+// 512-element tiles per wave.
+constexpr int kStageMaxElems = 16384;
+// Rows per staged unit whose elements are a multiple of `align` (the kernel's
+// tile; 0: not staged): the fewest rows that hold at least 8192 elements
 // (about two 1024-element tiles per wave of a workgroup; larger units hold more
-// LDS per workgroup and fewer workgroups fit on a CU), within
-// kReorderStageMaxBytes; else the fewest that hold whole units.
-inline int stage_rows_for(int64_t cols, int elem_bytes, int align = 1024) {
-  if (cols > kReorderStageMaxCols) return 0;
+// LDS per workgroup and fewer workgroups fit on a CU) within kStageMaxElems;
+// else the fewest that fit.
+inline int stage_rows_for(int64_t cols, int align) {
+  if (cols <= 0 || cols > kStageMaxElems) return 0;
   int first = 0;
-  for (int r = 1; r <= 16; ++r) {
-    if ((r * cols) % align != 0 || r * cols * elem_bytes > kReorderStageMaxBytes) continue;
+  for (int r = 1; r * cols <= kStageMaxElems; ++r) {
+    if ((r * cols) % align != 0) continue;
     if (r * cols >= 8192) return r;
     if (first == 0) first = r;
   }
@@ -197,6 +198,18 @@ int launch_limit();
 inline dim3 capped_grid(int64_t groups) {
   const int lim = launch_limit();
   return dim3((unsigned)(lim > 0 && groups > lim ? lim : groups));
+}
+// Workgroups of `kernel` (256 threads, `lds` bytes of dynamic LDS) that fit on
+// one CU at once (the runtime's occupancy figure, cached per device, kernel and
+// LDS size; 1 if it cannot be had).
+int resident_groups(const void* kernel, size_t lds);
+// Grid of a kernel that walks `units` units with a stride of the grid and
+// keeps the next unit's loads in flight: every workgroup resident at once (one
+// pass over the device, so no workgroup waits for another to end), at most
+// `units`, under the launch limit.
+inline dim3 resident_grid(const void* kernel, size_t lds, int64_t units) {
+  const int64_t full = (int64_t)device_cu_count() * resident_groups(kernel, lds);
+  return capped_grid(units < full ? units : full);
 }
 // Workgroups per CU (4 waves each) of the persistent FP8 compress of small
 // tensors.

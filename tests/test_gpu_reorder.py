@@ -20,11 +20,14 @@ pytestmark = pytest.mark.gpu
 
 CODECS = [cd.Codec.fp8(128, True), cd.Codec.fp8e5(128, True), cd.Codec.fp8(128, False), cd.Codec.int8_sym(),
           cd.Codec.int4_asym(), cd.Codec.int8_asym()]
-# The INT codecs stage rows through LDS (one row at a time when cols is a
-# multiple of 1024, else pairs) up to 16384 columns, while a unit stays within
-# 64 KiB, and gather from global memory beyond: 9728 (pairs) takes the staged
-# bf16 decode and the gathered float32 one, 16896 gathers throughout.
-SHAPES = [(1, 512), (3, 1024), (37, 1536), (300, 4096), (64, 5120), (7, 9728), (3, 16896)]
+# Compress and decode stage whole rows through LDS in units of the fewest rows
+# that hold at least 8192 elements, at most 16384, and whole tiles (1024
+# elements for the INT codecs, 512 for the FP8 Hadamard kernels); other rows
+# are gathered from global memory. The shapes take partial last units (1 x 512,
+# 3 x 1024, 37 x 1536), 9728 (INT: gathered, no unit of whole tiles fits;
+# FP8: one row), one 16384-column row (a 64 KiB float32 unit) and 16896,
+# gathered throughout.
+SHAPES = [(1, 512), (3, 1024), (37, 1536), (300, 4096), (64, 5120), (7, 9728), (2, 16384), (3, 16896)]
 
 
 def cid(oc):
@@ -164,7 +167,8 @@ def test_order_entries_out_of_range_are_clamped_into_the_row():
 
 def test_full_size_reordered_compress_sampled_rows():
     # qwen-tp shape: the order from another shard, the whole tensor through the
-    # GPU, sampled row chunks through the oracle with the same order
+    # GPU (compress, then the bf16 decode; each workgroup walks several staged
+    # units), sampled row chunks through the oracle with the same order
     w = W.WORKLOADS["qwen-tp"]
     oc = cd.Codec.fp8(128, True)
     c = ccodec(oc)
@@ -184,6 +188,12 @@ def test_full_size_reordered_compress_sampled_rows():
     it = torch.from_numpy(idx).to(DEV)
     assert (codes.view(w.rows, w.cols)[it].cpu().numpy().reshape(-1) == ref.codes).all()
     assert (k.view(w.rows, w.cols // 128)[it].cpu().numpy().reshape(-1) == ref.scale).all()
+    del x
+    dec = torch.empty(w.rows * w.cols, dtype=torch.int16, device=DEV)
+    T.taco_decompress_reordered(c, buf, w.rows, w.cols, dec, order, 1)
+    torch.cuda.synchronize()
+    got_d = dec.view(w.rows, w.cols)[it].cpu().numpy().view(np.uint16).reshape(-1)
+    assert (got_d == oracle.decode_reordered(ref, o, "bf16").reshape(-1)).all(), "decode"
 
 
 @pytest.mark.parametrize("name", ["equarx", "flashcomm"])
