@@ -31,6 +31,12 @@
  *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
  *    the caller synchronizes. All validation happens before anything is
  *    enqueued; a call that returns an error has enqueued nothing.
+ *  - Host state: per-device caches filled on first use (the CU count, the
+ *    occupancy the reordering kernels size their grids by, the address of
+ *    the scratch array of taco_compress_noalloc), each under an atomic or a
+ *    lock, and the calling thread's launch cap (taco_set_launch_limit).
+ *    Calls from several host threads are safe; calls that share a workspace
+ *    or the scratch array must be ordered on the device by the caller.
  *  - rows == 0 is valid and enqueues nothing; rows * cols above 2^35 is
  *    TACO_ERR_INVALID_ARG.
  *  - Return value: TACO_OK or a negative TACO_ERR_* code
