@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
                                                                 Workspace* __restrict__ ws, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB, kChunkTiles>;
-  extern __shared__ int16_t lds_order[];
+  extern __shared__ __attribute__((aligned(16))) int16_t lds_order[];
   if constexpr (REORD) load_order_lds(ro, lds_order);
   const int lane = threadIdx.x & (kWave - 1);
   const LaneSigns<LOGB> ls(lane);
@@ -422,7 +422,38 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
   const int64_t nchunks = (elems + CH::ELEMS - 1) / CH::ELEMS;
   const int64_t stride = (int64_t)gridDim.x * (kBlockThreads / kWave);
   float run_max = 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); c < nchunks; c += stride) {
+  bool staged = false;
+  if constexpr (REORD) staged = ro.staged;
+  if (staged) {
+    // units of whole rows through LDS as in the staged compress (the next
+    // unit's loads in registers while this one is transformed)
+    constexpr int NW = kBlockThreads / kWave;
+    const uint16_t* rows_lds = reinterpret_cast<const uint16_t*>(lds_order) + reorder_stage_offset(ro);
+    const int cols = ro.cols;
+    const StageUnits su(elems, cols, ro.stage_rows);
+    uint4 next[8];
+    stage_issue(x, su, blockIdx.x, next);
+    for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
+      const int utiles = su.elems(u) / kTileElems;
+      stage_commit(next, reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(lds_order) + reorder_stage_offset(ro)),
+                   su.elems(u));
+      __syncthreads();
+      stage_issue(x, su, u + gridDim.x, next);
+      for (int lt = wave_in_group(); lt < utiles; lt += NW) {
+        const int e0 = lt * kTileElems;   // span start inside the unit
+        const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
+        const int src = lds_order[(col0 >> 3) + ls.elem_off / kGroupElems];
+        float v[8];
+        widen8(*reinterpret_cast<const uint4*>(rows_lds + lrow * cols + src * kGroupElems), v);
+        fwht_in_lane(v);
+        fwht_cross_lane<Gm::STAGES>(v, ls.s0, ls.s1, ls.s2, ls.s3);
+        run_max = fmaxf(run_max, absmax8(v));
+      }
+      __syncthreads();   // the unit's LDS rows are read before the next unit's are written
+    }
+  }
+  for (int64_t c = (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_group(); !staged && c < nchunks;
+       c += stride) {
     uint4 raw[kChunkTiles];
     load_chunk<LOGB, kChunkTiles, REORD>(x, c, elems, ls.elem_off, ro, lds_order, raw);
 #pragma unroll
@@ -447,10 +478,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_amax(const uint16_t* 
 
 // --------------------------------------------------------------- decode --
 //
-// Consumer side: dequantize (dec(q) * g * 2^-k, the combined scale is exact),
-// inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
-// factor, then float32 or bf16 output. T wave tiles per wave as launched; a
-// smaller grid walks them with a stride of the grid.
 // One wave tile of the decode: the lane's eight codes times g * 2^-k, the
 // inverse transform (the forward one, which is its own inverse up to 2^-LOGB),
 // then 2^-LOGB and the lane's sign.
@@ -466,6 +493,10 @@ TACO_DEV void decode_tile(uint2 raw, float d, float outscale, const LaneSigns<LO
   for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], outscale, 0.0f);
 }
 
+// Consumer side: dequantize (dec(q) * g * 2^-k, the combined scale is exact),
+// inverse transform (the same butterflies; H H = B I) and the 2^-log2(B)
+// factor, then float32 or bf16 output. T wave tiles per wave as launched; a
+// smaller grid walks them with a stride of the grid.
 template <int LOGB, bool E5, bool BF16OUT, int T, bool REORD>
 __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_decode(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ kexp, const float* __restrict__ g_hdr,
@@ -634,18 +665,24 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
     // reordered input (block 128 only): the one-chunk-per-wave grid at every size
     if constexpr (LOGB == 7) {
       if (a.dbg) return hipErrorInvalidValue;
-      if (a.auto_prepass)
-        hipLaunchKernelGGL((k_fp8_had_amax<LOGB, true>), big_grid, block, order_lds_bytes(a.ro), s, x, a.nblocks, ws,
-                           a.ro);
-      // rows staged through LDS in units of whole rows, else gathered
+      // rows staged through LDS in units of whole rows (the abs-max pre-pass
+      // too), else gathered
       ReorderArgs ro = a.ro;
       ro.stage_rows = stage_rows_for(ro.cols, kTileElems);
       ro.staged = ro.stage_rows > 0;
       if (ro.staged) {
         const int64_t units = (elems / ro.cols + ro.stage_rows - 1) / ro.stage_rows;
         const size_t lds = (size_t)reorder_stage_offset(ro) * 2 + (size_t)ro.stage_rows * ro.cols * 2;
+        if (a.auto_prepass) {
+          auto* amax = k_fp8_had_amax<LOGB, true>;
+          hipLaunchKernelGGL(amax, resident_grid(reinterpret_cast<const void*>(amax), lds, units), block, lds, s, x,
+                             a.nblocks, ws, ro);
+        }
         launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, dim3(1), s, ro, lds, units);
       } else {
+        if (a.auto_prepass)
+          hipLaunchKernelGGL((k_fp8_had_amax<LOGB, true>), big_grid, block, order_lds_bytes(a.ro), s, x, a.nblocks,
+                             ws, ro);
         launch_compress_t<LOGB, kChunkTiles, E5, false, false, true>(a, big_grid, s, ro, order_lds_bytes(a.ro));
       }
       return hipGetLastError();
