@@ -96,6 +96,42 @@ def test_compress_and_decode_reordered(oc, shape):
         "decode bf16"
 
 
+def _random_shapes(seed, count):
+    """Seeded (rows, cols): cols a multiple of 512 up to 20480 (staged units of
+    1 to 16 rows, and a few gathered widths), rows 1 to 40 (partial last
+    units of every size)."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 41)), 512 * int(rng.integers(1, 41))) for _ in range(count)]
+
+
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(128, True), cd.Codec.int8_sym(), cd.Codec.int4_asym(),
+                                cd.Codec.int8_asym()], ids=cid)
+def test_reordered_random_shapes(oc):
+    """Compress and both decodes, reordered, on seeded random shapes against
+    the oracle, bit for bit (the FP8 codec with its data-driven tensor scale,
+    so the abs-max pre-pass runs too)."""
+    fp8 = oc.format in cd.FP8_FORMATS
+    c = ccodec(oc)
+    for rows, cols in _random_shapes(1000 + oc.format, 10):
+        print(f"[reorder random] {cid(oc)} {rows}x{cols}", flush=True)
+        x = outlier_bits((rows, cols), seed=rows * cols + oc.format)
+        order = gpu_order(outlier_bits((rows, cols), seed=rows * cols + 1))
+        o = order.cpu().numpy().astype(np.int64)
+        buf = T.empty_compressed(c, rows, cols)
+        T.taco_compress_reordered(c, upload_bits(x), rows, cols, T.TACO_SCALE_AUTO if fp8 else 1.0, buf, order,
+                                  workspace=new_workspace() if fp8 else None)
+        d32 = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+        d16 = torch.empty(rows * cols, dtype=torch.int16, device=DEV)
+        T.taco_decompress_reordered(c, buf, rows, cols, d32, order, 0)
+        T.taco_decompress_reordered(c, buf, rows, cols, d16, order, 1)
+        torch.cuda.synchronize()
+        ref = oracle.compress_reordered(oc, x, o)
+        assert_same(parse(buf, oc, rows, cols), ref, f"reordered compress {rows}x{cols}")
+        assert same_f32_bits(d32.cpu().numpy(), oracle.decode_reordered(ref, o)).all(), f"decode f32 {rows}x{cols}"
+        assert (d16.cpu().numpy().view(np.uint16) == oracle.decode_reordered(ref, o, "bf16").reshape(-1)).all(), \
+            f"decode bf16 {rows}x{cols}"
+
+
 @pytest.mark.parametrize("oc", [cd.Codec.fp8(128, True), cd.Codec.int8_sym(), cd.Codec.int4_asym()], ids=cid)
 def test_reordered_shards_through_the_reduce(oc):
     # every rank compresses its shard in the shared order; the reduce and the
