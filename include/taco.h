@@ -248,7 +248,8 @@ int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stre
  * block holds channels of similar magnitude. `order` is a device int32 array
  * of cols / 8 entries, reordered group j being original group order[j] of the
  * same row; it must be a permutation of [0, cols / 8) (other values are
- * clamped into range: no fault, unspecified codes). Shapes: cols a multiple
+ * clamped into range: no fault and no access outside the row or the output,
+ * but unspecified codes and decoded values). Shapes: cols a multiple
  * of 512 and at most 131072, FP8 block 128 (TACO_ERR_SHAPE otherwise).
  * Compressed buffers, decompress-reduce, requantize and the ring hop work on
  * the reordered tensor unchanged; taco_decompress_reordered restores the

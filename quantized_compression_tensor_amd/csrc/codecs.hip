@@ -761,53 +761,88 @@ __global__ __launch_bounds__(kBlockThreads) void k_dequantize(DequantK a) {
   constexpr int NW = BF16OUT ? 1 : 2;
   if constexpr (REORD) {
     if (a.ro.staged) {
-      // rows through LDS in units of stage_rows rows (whole 1024-element
-      // tiles, at most kStageMaxElems elements): the waves take the unit's
-      // tiles in turn, four at a time with their loads in flight together,
-      // and each lane writes its decoded group j to group order[j] of its
-      // span's row in LDS; then the unit is stored contiguously. (Holding the
-      // next unit's loads in registers as well, on a grid of resident
-      // workgroups, measured 5 % slower on the INT8 decode and 6 % faster on
-      // the INT4 one: the registers cost workgroups per CU.)
+      // rows in units of stage_rows rows (at most kStageMaxElems elements):
+      // a unit's codes are copied into LDS contiguously; the lane that writes
+      // output group g of a 512-element span reads the codes of reordered
+      // group inv[g] of the same row from LDS (inv, the inverse of the order,
+      // is built in LDS) and its block's scale (and zero point) from global
+      // memory, and the wave stores the span's decoded values contiguously.
+      // A wave issues all of its spans' loads of a unit before decoding any,
+      // and the next unit's codes are loaded into registers while this one is
+      // decoded.
       constexpr int WG = kBlockThreads / kWave;
-      uint8_t* rows_lds = reinterpret_cast<uint8_t*>(lds_order) + 2 * reorder_stage_offset(a.ro);
-      const int cols = a.ro.cols;
+      constexpr int CW = kStageMaxElems / CB / 16 / kBlockThreads;   // 16-byte code words per thread and unit
+      constexpr int TB = 4;                                          // spans per batch
+      int16_t* inv = lds_order + reorder_stage_offset(a.ro);
+      uint4* codes_lds = reinterpret_cast<uint4*>(inv + reorder_stage_offset(a.ro));
+      const int cols = a.ro.cols, ng = a.ro.ngroups;
+      // identity first, so that an order that is not a permutation leaves no
+      // entry unset (its output is unspecified, its accesses stay in the row)
+      for (int i = (int)threadIdx.x; i < ng; i += kBlockThreads) inv[i] = (int16_t)i;
+      __syncthreads();
+      for (int i = (int)threadIdx.x; i < ng; i += kBlockThreads) inv[lds_order[i]] = (int16_t)i;
       const StageUnits su(a.n, cols, a.ro.stage_rows);
+      uint4 next[CW];
+      auto issue = [&](int64_t u) {   // past the last unit: an empty resource, zeros
+        const rsrc_t r = make_rsrc32(a.codes + (u < su.count ? su.base(u) / CB : 0), su.elems(u) / CB);
+#pragma unroll
+        for (int j = 0; j < CW; ++j) next[j] = bload128<kNT>(r, 16 * ((int)threadIdx.x + j * kBlockThreads), 0);
+      };
+      issue(blockIdx.x);
       for (int64_t u = blockIdx.x; u < su.count; u += gridDim.x) {
-        const int64_t pbase = su.base(u);
-        const int pelems = su.elems(u);
-        for (int lt0 = wave_in_group(); lt0 * kWaveElems < pelems; lt0 += 4 * WG) {
-          LaneIn<FMT, B> in[4][2];
+        const int64_t ubase = su.base(u);
+        const int uelems = su.elems(u);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {   // tiles past the unit's end load nothing
-            const int lt = lt0 + j * WG;
-            const int64_t base = pbase + (int64_t)lt * kWaveElems;
-            const int rt = lt * kWaveElems >= pelems ? 0 : (a.n - base < kWaveElems ? (int)(a.n - base) : kWaveElems);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) in[j][h] = load_in(base, rt, h);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              float d[V];
-              dequant_lane<FMT, B, V>(in[j][h], d);
-              const int e0 = (lt0 + j * WG) * kWaveElems + h * HALF;   // span start inside the unit
-              if (e0 < pelems) {
-                const int lrow = e0 / cols, col0 = e0 - lrow * cols;   // row inside the unit
-                const int dst = lds_order[(col0 >> 3) + lane];
-                uint4 w[NW];
-                out_words(d, w);
-                uint4* p = reinterpret_cast<uint4*>(rows_lds + ((int64_t)lrow * cols + dst * kGroupElems) * OB);
-#pragma unroll
-                for (int q = 0; q < NW; ++q) p[q] = w[q];
-              }
-            }
+        for (int j = 0; j < CW; ++j) {
+          const int w = (int)threadIdx.x + j * kBlockThreads;
+          if (w < uelems / CB / 16) codes_lds[w] = next[j];
         }
         __syncthreads();
-        stage_drain(reinterpret_cast<const uint4*>(rows_lds),
-                    make_rsrc32(static_cast<uint8_t*>(a.out) + pbase * OB, pelems * OB), pelems * OB / 16);
-        __syncthreads();   // the unit's LDS rows are stored before the next unit's decode
+        issue(u + gridDim.x);
+        const rsrc_t rs = make_rsrc32(static_cast<const uint8_t*>(a.scale) + (ubase / B) * MB, (uelems / B) * MB);
+        const rsrc_t rz = make_rsrc32(ASYM ? a.zero + ubase / B : a.codes, ASYM ? uelems / B : 0);
+        const rsrc_t rout = make_rsrc32(static_cast<uint8_t*>(a.out) + ubase * OB, uelems * OB);
+        const uint8_t* cb = reinterpret_cast<const uint8_t*>(codes_lds);
+        // batches of four consecutive spans, batch b to wave b % 4, the
+        // batch's loads first; a span past the unit's end reads the last span
+        // again and its stores fall outside the output resource (dropped): no
+        // branch, so the compiler keeps every load ahead of the arithmetic
+        for (int bt = wave_in_group(); bt * TB * HALF < uelems; bt += WG) {
+          LaneIn<FMT, B> in[TB];
+#pragma unroll
+          for (int i = 0; i < TB; ++i) {
+            const int e0 = min((bt * TB + i) * HALF, uelems - HALF);   // span start inside the unit
+            const int lrow = e0 / cols, col0 = e0 - lrow * cols;       // row inside the unit
+            const int er = lrow * cols + 8 * inv[(col0 >> 3) + lane];  // the source group's first element
+            in[i].q = make_uint4(0, 0, 0, 0);
+            if constexpr (FMT == kINT4A) in[i].q.x = *reinterpret_cast<const uint32_t*>(cb + er / 2);
+            else {
+              const uint2 c = *reinterpret_cast<const uint2*>(cb + er);
+              in[i].q.x = c.x;
+              in[i].q.y = c.y;
+            }
+            in[i].z = 0;
+            in[i].sh = 0;
+            if constexpr (is_fp8(FMT)) {
+              in[i].z = bload8(rs, er / B, 0);
+            } else {
+              in[i].s = __uint_as_float(bload32(rs, 4 * (er / B), 0));
+              if constexpr (ASYM) in[i].z = bload8(rz, er / B, 0);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < TB; ++i) {
+            if constexpr (is_fp8(FMT)) in[i].s = g * pow2f(-(int)(int8_t)(uint8_t)in[i].z);
+            float d[V];
+            dequant_lane<FMT, B, V>(in[i], d);
+            uint4 w[NW];
+            out_words(d, w);
+            const int e0 = (bt * TB + i) * HALF;
+#pragma unroll
+            for (int q = 0; q < NW; ++q) bstore128<0>(w[q], rout, (e0 + lane * V) * OB + 16 * q, 0);
+          }
+        }
+        __syncthreads();   // the unit's codes are read before the next unit's are written
       }
       return;
     }
@@ -1257,12 +1292,15 @@ static void launch_dq(const DequantArgs& a, hipStream_t s) {
   dim3 grid = grid_for(a.n), block(kBlockThreads);
   if constexpr (!is_fp8(FMT) || B == 128) {
     if (a.ro.order != nullptr) {
-      k.ro.stage_rows = stage_rows_for(a.ro.cols, kWaveElems);
+      // staged: the order, its inverse and one unit's codes in LDS
+      k.ro.stage_rows = stage_rows_for(a.ro.cols, kSpanElems);
       k.ro.staged = k.ro.stage_rows > 0;
-      const size_t lds = k.ro.staged ? staged_lds_bytes(k.ro, a.bf16_out ? 2 : 4) : order_lds_bytes(a.ro);
-      if (k.ro.staged) grid = capped_grid(staged_units(a.n, k.ro));   // one workgroup per unit
-      if (a.bf16_out) hipLaunchKernelGGL((k_dequantize<FMT, B, true, true>), grid, block, lds, s, k);
-      else hipLaunchKernelGGL((k_dequantize<FMT, B, false, true>), grid, block, lds, s, k);
+      const size_t lds = k.ro.staged ? (size_t)reorder_stage_offset(k.ro) * 4 +
+                                           (size_t)k.ro.stage_rows * a.ro.cols / (FMT == kINT4A ? 2 : 1)
+                                     : order_lds_bytes(a.ro);
+      auto* kern = a.bf16_out ? k_dequantize<FMT, B, true, true> : k_dequantize<FMT, B, false, true>;
+      if (k.ro.staged) grid = resident_grid(reinterpret_cast<const void*>(kern), lds, staged_units(a.n, k.ro));
+      hipLaunchKernelGGL(kern, grid, block, lds, s, k);
       return;
     }
   }

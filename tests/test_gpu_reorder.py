@@ -199,6 +199,19 @@ def test_order_entries_out_of_range_are_clamped_into_the_row():
     clamped = np.clip(bad, 0, cols // 8 - 1).astype(np.int64)
     cmap = (clamped[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
     assert_same(parse(b, oc, rows, cols), oracle.compress(oc, x[:, cmap]), "clamped order")
+    # the decode of such an order writes unspecified values but stays inside
+    # its row and its output (INT: gathered through the order's inverse; FP8
+    # with the transform: scattered through the order)
+    for dc in (oc, cd.Codec.fp8(128, True)):
+        cc = ccodec(dc)
+        bb = T.empty_compressed(cc, rows, cols)
+        T.taco_compress(cc, upload_bits(x), rows, cols, 0.01 if dc.format in cd.FP8_FORMATS else 1.0, bb)
+        guard = torch.full((3 * rows * cols,), 7.0, dtype=torch.float32, device=DEV)
+        out = guard[rows * cols:2 * rows * cols]
+        T.taco_decompress_reordered(cc, bb, rows, cols, out, order, 0)
+        torch.cuda.synchronize()
+        g = guard.cpu().numpy()
+        assert (g[:rows * cols] == 7.0).all() and (g[2 * rows * cols:] == 7.0).all(), cid(dc)
 
 
 def test_full_size_reordered_compress_sampled_rows():
