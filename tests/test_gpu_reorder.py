@@ -216,8 +216,9 @@ def test_order_entries_out_of_range_are_clamped_into_the_row():
 
 def test_full_size_reordered_compress_sampled_rows():
     # qwen-tp shape: the order from another shard, the whole tensor through the
-    # GPU (compress, then the bf16 decode; each workgroup walks several staged
-    # units), sampled row chunks through the oracle with the same order
+    # GPU (compress, then the bf16 and float32 decodes: at this size each
+    # workgroup walks many staged units, with the next one's loads in flight),
+    # sampled row chunks through the oracle with the same order
     w = W.WORKLOADS["qwen-tp"]
     oc = cd.Codec.fp8(128, True)
     c = ccodec(oc)
@@ -243,6 +244,12 @@ def test_full_size_reordered_compress_sampled_rows():
     torch.cuda.synchronize()
     got_d = dec.view(w.rows, w.cols)[it].cpu().numpy().view(np.uint16).reshape(-1)
     assert (got_d == oracle.decode_reordered(ref, o, "bf16").reshape(-1)).all(), "decode"
+    del dec
+    d32 = torch.empty(w.rows * w.cols, dtype=torch.float32, device=DEV)
+    T.taco_decompress_reordered(c, buf, w.rows, w.cols, d32, order, 0)
+    torch.cuda.synchronize()
+    got_f = d32.view(w.rows, w.cols)[it].cpu().numpy().reshape(-1)
+    assert same_f32_bits(got_f, oracle.decode_reordered(ref, o).reshape(-1)).all(), "decode f32"
 
 
 @pytest.mark.parametrize("name", ["equarx", "flashcomm"])
