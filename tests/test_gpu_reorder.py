@@ -284,3 +284,55 @@ def test_full_size_staged_reorder_sampled_rows(name):
         assert (aux.view(w.rows, w.cols // oc.block)[it].cpu().numpy().reshape(-1) == ref.zero).all(), "zero points"
     got_d = dec.view(w.rows, w.cols)[it].cpu().numpy().view(np.uint16).reshape(-1)
     assert (got_d == oracle.decode_reordered(ref, o, "bf16").reshape(-1)).all(), "decode"
+
+
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(128, True), cd.Codec.int8_sym()], ids=cid)
+def test_reordered_graph_replays_match_eager(oc):
+    """The reordered compress (FP8: with the delayed tensor scale, so the
+    workspace protocol runs in the graph) and both decodes, captured once in a
+    HIP graph and replayed on three inputs copied in eagerly between the
+    replays, write exactly what the same calls write eagerly."""
+    rows, cols = 300, 5120
+    fp8 = oc.format in cd.FP8_FORMATS
+    c = ccodec(oc)
+    order = gpu_order(outlier_bits((rows, cols), seed=901))
+    xs = [upload_bits(outlier_bits((rows, cols), seed=910 + i)) for i in range(3)]
+    scale = T.TACO_SCALE_DELAYED if fp8 else 1.0
+
+    def calls(x, ws, buf, d32, d16, stream=None):
+        sh = None if stream is None else stream.cuda_stream
+        T.taco_compress_reordered(c, x, rows, cols, scale, buf, order, workspace=ws, stream=sh)
+        T.taco_decompress_reordered(c, buf, rows, cols, d32, order, 0, stream=sh)
+        T.taco_decompress_reordered(c, buf, rows, cols, d16, order, 1, stream=sh)
+
+    def alloc():
+        return (new_workspace() if fp8 else None, T.empty_compressed(c, rows, cols),
+                torch.empty(rows * cols, dtype=torch.float32, device=DEV),
+                torch.empty(rows * cols, dtype=torch.int16, device=DEV))
+
+    eager = []
+    ws, buf, d32, d16 = alloc()
+    for x in xs:
+        calls(x, ws, buf, d32, d16)
+        torch.cuda.synchronize()
+        eager.append((buf.clone(), d32.clone(), d16.clone()))
+    ws, buf, d32, d16 = alloc()
+    x_in = torch.empty_like(xs[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=st):
+        calls(x_in, ws, buf, d32, d16, stream=st)
+    for i, x in enumerate(xs):
+        x_in.copy_(x)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eb, e32, e16 = eager[i]
+        got, want = T.regions(buf, c, rows, cols), T.regions(eb, c, rows, cols)
+        for k in range(3):   # codes, scales, zero points
+            assert torch.equal(got[k], want[k]), f"replay {i}: region {k}"
+        assert torch.equal(got[3][:1], want[3][:1]), f"replay {i}: tensor scale"
+        assert torch.equal(d32.view(torch.int32), e32.view(torch.int32)), f"replay {i}: float32 decode"
+        assert torch.equal(d16, e16), f"replay {i}: bf16 decode"
