@@ -409,6 +409,45 @@ def test_reduce_int4_handmade_shards(nshards):
 
 # ------------------------------------------------------------- decode ----
 
+@pytest.mark.parametrize("pair", PAIRS, ids=pid)
+def test_step_on_random_shapes(pair):
+    """The whole path on seeded random shapes and shard counts: every shard's
+    compress, the decompress-reduce with its float32 sum and re-quantized
+    output, and both decodes of that output, each against the oracle bit for
+    bit (rows 1-40, cols any multiple of the blocks up to 20480 columns, so
+    the tensors end anywhere inside a wave tile; 1-16 shards)."""
+    cin, cout = pair
+    step = max(cin.block, cout.block)
+    body = "t3" if cin.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    rng = np.random.default_rng(4000 + 10 * cin.format + cin.block)
+    for case in range(6):
+        rows, cols = int(rng.integers(1, 41)), step * int(rng.integers(1, 20480 // step + 1))
+        n = int(rng.integers(1, 17))
+        print(f"[random step] {pid(pair)} case {case}: {rows}x{cols}, {n} shards", flush=True)
+        refs, bufs = [], []
+        for r in range(n):
+            bits = bits_for((rows, cols), seed=int(rng.integers(1 << 30)), body=body, sigma=0.01 * (1 + r % 4))
+            g = np.float32(0.003 * (1 + r % 5))
+            refs.append(oracle.compress(cin, bits, tensor_scale=g))
+            buf, _ = gpu_compress(cin, bits, scale=float(g))
+            assert_same(parse(buf, cin, rows, cols), refs[-1], f"case {case} shard {r}")
+            bufs.append(buf)
+        acc, rq = oracle.decompress_reduce(refs, cout)
+        sm = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+        out = T.empty_compressed(ccodec(cout), rows, cols)
+        T.taco_decompress_reduce(ccodec(cin), bufs, rows, cols, sm, ccodec(cout), out)
+        d32 = torch.empty(rows * cols, dtype=torch.float32, device=DEV)
+        d16 = torch.empty(rows * cols, dtype=torch.int16, device=DEV)
+        T.taco_decompress(ccodec(cout), out, rows, cols, d32, 0)
+        T.taco_decompress(ccodec(cout), out, rows, cols, d16, 1)
+        torch.cuda.synchronize()
+        assert same_f32_bits(sm.cpu().numpy(), acc).all(), f"case {case}: sum"
+        assert_same(parse(out, cout, rows, cols), rq, f"case {case}: requantized")
+        assert same_f32_bits(d32.cpu().numpy(), oracle.decode(rq, "f32")).all(), f"case {case}: decode f32"
+        assert (d16.cpu().numpy().view(np.uint16) == oracle.decode(rq, "bf16").reshape(-1)).all(), \
+            f"case {case}: decode bf16"
+
+
 @pytest.mark.parametrize("out_dtype", [0, 1], ids=["f32", "bf16"])
 @pytest.mark.parametrize("oc", ALL, ids=cid)
 def test_decompress(oc, out_dtype):
