@@ -98,6 +98,9 @@ def parse():
     ap.add_argument("--summarize-issue", metavar="DIR",
                     help="turn a rocprofv3 --pmc run of instruction and busy counters (with --kernel-trace) into "
                          "profiles/issue_<kernel>_<workload>.txt and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "NAME"),
+                    help="write profiles/kernels_NAME_trace.txt: kernel-trace statistics of every kernel of this "
+                         "library in one profiled run (with --command)")
     ap.add_argument("--summarize-consumer", nargs=2, metavar=("TRACE_DIR", "MFMA_DIR"),
                     help="write profiles/consumer_gemm.txt from a kernel trace of the default bench command and "
                          "an MFMA counter pass (then exit)")
@@ -1194,6 +1197,25 @@ def _short(name):
     return name[:140]
 
 
+def summarize_trace(trace_dir, name, command):
+    """Kernel-trace statistics of every kernel of this library in one profiled
+    run (e.g. `--reorder`, whose reordered and plain kernels run side by side),
+    written to profiles/kernels_<name>_trace.txt."""
+    lines = [f"# rocprofv3 kernel-trace statistics of this library's kernels: {name}",
+             f"# command: {command}",
+             f"source_hash: {kernel_source_hash()}",
+             " calls    avg_us    min_us    max_us  kernel"]
+    stats = _trace_stats(trace_dir, concurrent_with=("Cijk",))
+    for n, r in sorted(stats.items(), key=lambda kv: -float(kv[1]["AverageNs"])):
+        if "taco::" in n:
+            lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                         f"{float(r['MaxNs']) / 1e3:9.2f}  {_short(n)}")
+    path = os.path.join(ROOT, "profiles", f"kernels_{name}_trace.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def summarize_consumer(trace_dir, mfma_dir, command):
     """Kernel-trace statistics of the consumer kernels (the fused decode-GEMM,
     the library GEMM, the bf16 decode) and the fused kernel's MFMA counters:
@@ -1235,6 +1257,9 @@ def main():
     args = parse()
     if args.summarize_consumer:
         summarize_consumer(*args.summarize_consumer, args.command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
         return
     if args.summarize_issue:
         names = [args.workload] + [x for x in args.extra.split(",") if x and x != "none"]

@@ -67,3 +67,26 @@ def test_trace_stats_leave_out_launches_beside_a_gemm(tmp_path):
     split = bench._trace_stats(str(tmp_path), concurrent_with=(), by_grid=("Cijk",))
     assert split["Cijk_gemm [grid 65536]"]["Calls"] == 1 and split["Cijk_gemm [grid 4096]"]["Calls"] == 1
     assert split["taco::k_reduce"]["Calls"] == 5
+
+
+def test_summarize_trace_lists_this_librarys_kernels(tmp_path, monkeypatch):
+    """The generic trace summary keeps this library's kernels only (slowest
+    first), leaves out launches beside a library GEMM and records the command
+    and the kernel-source hash."""
+    import bench
+    rows = [("Cijk_gemm", 100, 200), ("taco::k_quantize<2>", 0, 30), ("taco::k_quantize<2>", 150, 160),
+            ("taco::k_dequantize<2>", 300, 360), ("other_kernel", 400, 500)]
+    trace = tmp_path / "trace"
+    trace.mkdir()
+    lines = ['"Kernel_Name","Start_Timestamp","End_Timestamp"'] + [f'"{n}",{a},{b}' for n, a, b in rows]
+    (trace / "run_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc123")
+    bench.summarize_trace(str(trace), "demo", "the command")
+    text = (tmp_path / "profiles" / "kernels_demo_trace.txt").read_text().splitlines()
+    assert text[1] == "# command: the command" and text[2] == "source_hash: abc123"
+    body = text[4:]
+    assert len(body) == 2 and "k_dequantize" in body[0] and "k_quantize" in body[1]
+    assert body[1].split()[0] == "1"      # the launch beside the GEMM is left out
+    assert float(body[0].split()[1]) == 0.06
