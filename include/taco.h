@@ -257,7 +257,7 @@ int taco_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stre
 
 /* The order of the groups of a statistics tensor (device bf16 [rows, cols];
  * rows may be 0: identity order) into `order` (device int32 [cols / 8]).
- * Three launches on `stream`; `order` is their only memory. */
+ * Four launches on `stream`; `order` is their only memory. */
 int taco_chunk_order(const void* stats_bf16, int64_t rows, int64_t cols, int32_t* order, hipStream_t stream);
 
 /* taco_compress of the reordered tensor: column 8 j + i of the tensor the

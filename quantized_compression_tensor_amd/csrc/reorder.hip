@@ -9,15 +9,17 @@
 // magnitudes by group index, so that the blocks of the reordered tensor hold
 // channels of similar magnitude.
 //
-// Three launches on the caller's stream, with the output array as the only
+// Four launches on the caller's stream, with the output array as the only
 // memory: it first holds each group's abs-max (float bits, as unsigned
-// integers they order like the non-negative floats they are), then the order.
+// integers they order like the non-negative floats they are; the abs-max of
+// bf16 values has zero low 16 bits), then the abs-max with each group's rank in
+// the low 16 bits, then the order.
 #include "device_common.h"
 #include "taco_internal.h"
 
 namespace taco {
 
-constexpr int kRankThreads = 1024;
+constexpr int kRankThreads = 1024;   // the scatter's workgroup
 constexpr int kStatRows = 64;   // rows per workgroup of the statistics pass
 
 __global__ __launch_bounds__(kBlockThreads) void k_zero_u32(uint32_t* p, int n) {
@@ -58,22 +60,36 @@ __global__ __launch_bounds__(kBlockThreads) void k_group_absmax(const uint16_t* 
   }
 }
 
-// One workgroup: read every group's abs-max into LDS, then give group j the
-// rank #{i : a_i > a_j} + #{i < j : a_i = a_j} and write order[rank] = j into
-// the same array (every read happens before the barrier).
-__global__ __launch_bounds__(kRankThreads) void k_rank_groups(uint32_t* __restrict__ buf, int ngroups) {
-  extern __shared__ uint32_t a[];
-  for (int i = (int)threadIdx.x; i < ngroups; i += kRankThreads) a[i] = buf[i];
+// Group j's rank is #{i : a_i > a_j} + #{i < j : a_i = a_j}. Workgroup
+// (bj, bi) counts, for each group j of tile bj, the groups i of tile bi that
+// precede it and adds the count into the low 16 bits of j's entry (ranks are
+// below 2^14). Every read masks those bits off, so tiles running at the same
+// time see the same abs-maxima.
+constexpr int kRankTile = 256;
+constexpr uint32_t kValueBits = 0xFFFF0000u;
+__global__ __launch_bounds__(kRankTile) void k_rank_tiles(uint32_t* __restrict__ buf, int ngroups) {
+  __shared__ uint32_t ai[kRankTile];
+  const int i0 = (int)blockIdx.y * kRankTile, j = (int)blockIdx.x * kRankTile + (int)threadIdx.x;
+  const int ni = ngroups - i0 < kRankTile ? ngroups - i0 : kRankTile;
+  if ((int)threadIdx.x < ni) ai[threadIdx.x] = buf[i0 + threadIdx.x] & kValueBits;
   __syncthreads();
-  for (int j = (int)threadIdx.x; j < ngroups; j += kRankThreads) {
-    const uint32_t aj = a[j];
-    int rank = 0;
-    for (int i = 0; i < ngroups; ++i) {
-      const uint32_t ai = a[i];
-      rank += (ai > aj) || (ai == aj && i < j);
-    }
-    buf[rank] = (uint32_t)j;
+  if (j >= ngroups) return;
+  const uint32_t aj = buf[j] & kValueBits;
+  uint32_t cnt = 0;
+  for (int t = 0; t < ni; ++t) {
+    const uint32_t a = ai[t];
+    cnt += (a > aj) || (a == aj && i0 + t < j);
   }
+  if (cnt != 0) __hip_atomic_fetch_add(&buf[j], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup: read every group's rank into LDS, then write order[rank] = j
+// into the same array (every read happens before the barrier).
+__global__ __launch_bounds__(kRankThreads) void k_scatter_order(uint32_t* __restrict__ buf, int ngroups) {
+  extern __shared__ uint32_t rank[];
+  for (int i = (int)threadIdx.x; i < ngroups; i += kRankThreads) rank[i] = buf[i] & ~kValueBits;
+  __syncthreads();
+  for (int j = (int)threadIdx.x; j < ngroups; j += kRankThreads) buf[rank[j]] = (uint32_t)j;
 }
 
 hipError_t launch_chunk_order(const void* stats, int64_t rows, int64_t cols, int32_t* order, hipStream_t s) {
@@ -87,7 +103,9 @@ hipError_t launch_chunk_order(const void* stats, int64_t rows, int64_t cols, int
     hipLaunchKernelGGL(k_group_absmax, grid, dim3(kBlockThreads), 0, s, static_cast<const uint16_t*>(stats), rows,
                        (int)cols, buf);
   }
-  hipLaunchKernelGGL(k_rank_groups, dim3(1), dim3(kRankThreads), (size_t)ngroups * 4, s, buf, ngroups);
+  const unsigned tiles = (unsigned)((ngroups + kRankTile - 1) / kRankTile);
+  hipLaunchKernelGGL(k_rank_tiles, dim3(tiles, tiles), dim3(kRankTile), 0, s, buf, ngroups);
+  hipLaunchKernelGGL(k_scatter_order, dim3(1), dim3(kRankThreads), (size_t)ngroups * 4, s, buf, ngroups);
   return hipGetLastError();
 }
 

@@ -50,7 +50,8 @@ def outlier_bits(shape, seed):
     return f32_to_bf16_bits(x)
 
 
-@pytest.mark.parametrize("shape", SHAPES + [(0, 1024), (2000, 512)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", SHAPES + [(0, 1024), (2000, 512), (3, 131072), (0, 131072)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
 def test_chunk_order_matches_oracle(shape):
     bits = outlier_bits(shape, seed=shape[0] + shape[1]) if shape[0] else np.zeros(shape, np.uint16)
     got = gpu_order(bits).cpu().numpy()
