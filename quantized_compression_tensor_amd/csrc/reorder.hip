@@ -68,17 +68,24 @@ __global__ __launch_bounds__(kBlockThreads) void k_group_absmax(const uint16_t* 
 constexpr int kRankTile = 256;
 constexpr uint32_t kValueBits = 0xFFFF0000u;
 __global__ __launch_bounds__(kRankTile) void k_rank_tiles(uint32_t* __restrict__ buf, int ngroups) {
-  __shared__ uint32_t ai[kRankTile];
+  __shared__ __attribute__((aligned(16))) uint32_t ai[kRankTile];
   const int i0 = (int)blockIdx.y * kRankTile, j = (int)blockIdx.x * kRankTile + (int)threadIdx.x;
   const int ni = ngroups - i0 < kRankTile ? ngroups - i0 : kRankTile;
   if ((int)threadIdx.x < ni) ai[threadIdx.x] = buf[i0 + threadIdx.x] & kValueBits;
   __syncthreads();
   if (j >= ngroups) return;
   const uint32_t aj = buf[j] & kValueBits;
+  // ni is a multiple of 64 (cols is a multiple of 512): four entries per LDS
+  // read, several reads in flight
   uint32_t cnt = 0;
-  for (int t = 0; t < ni; ++t) {
-    const uint32_t a = ai[t];
-    cnt += (a > aj) || (a == aj && i0 + t < j);
+#pragma unroll 4
+  for (int t = 0; t < ni; t += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(&ai[t]);
+    const int i = i0 + t;
+    cnt += (q.x > aj) || (q.x == aj && i < j);
+    cnt += (q.y > aj) || (q.y == aj && i + 1 < j);
+    cnt += (q.z > aj) || (q.z == aj && i + 2 < j);
+    cnt += (q.w > aj) || (q.w == aj && i + 3 < j);
   }
   if (cnt != 0) __hip_atomic_fetch_add(&buf[j], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
