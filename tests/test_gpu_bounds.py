@@ -142,3 +142,39 @@ def test_decompress_gemm_stays_inside_buffers(oc, shape, out_dtype):
     a.assert_guards("decode-GEMM activation")
     w.assert_guards("decode-GEMM weight")
     assert torch.equal(a.buf(), a_before) and torch.equal(w.buf(), w_before), "an input was written"
+
+
+@pytest.mark.parametrize("shape", [(1, 512), (3, 1536), (7, 9728), (2, 16896)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("oc", [cd.Codec.fp8(128, True), cd.Codec.fp8(128, False), cd.Codec.int8_sym(),
+                                cd.Codec.int4_asym(), cd.Codec.int8_asym()],
+                         ids=lambda oc: f"f{oc.format}-b{oc.block}" + ("-h" if oc.hadamard else ""))
+def test_reordered_entry_points_stay_inside_buffers(oc, shape):
+    """The group order, the reordered compress (FP8: with the data-driven scale,
+    so its abs-max pre-pass runs too) and both reordered decodes, at widths that
+    are staged through LDS in partial units (512, 1536, 9728) and gathered
+    (16896)."""
+    rows, cols = shape
+    n = rows * cols
+    c = ccodec(oc)
+    fp8 = oc.format in cd.FP8_FORMATS
+    print(f"bounds (reordered): codec {oc} shape {shape}", flush=True)
+    stats = Arena(2 * n).fill(W.random_bits(shape, seed=70, sigma=0.05))
+    order = Arena(4 * (cols // 8))
+    T.taco_chunk_order(stats.buf(), rows, cols, order.buf(torch.int32))
+    order.assert_guards("chunk_order")
+    stats.assert_guards("chunk_order statistics")
+    body = "t3" if oc.format in (cd.INT4_ASYM, cd.INT8_ASYM) else "normal"
+    x = Arena(2 * n).fill(W.random_bits(shape, seed=71, sigma=0.05, body=body))
+    ws = Arena(T.TACO_WORKSPACE_BYTES).fill(np.zeros(T.TACO_WORKSPACE_BYTES, np.uint8)) if fp8 else None
+    out = Arena(T.taco_compressed_bytes(c, rows, cols))
+    T.taco_compress_reordered(c, x.buf(), rows, cols, T.TACO_SCALE_AUTO if fp8 else 1.0, out.buf(),
+                              order.buf(torch.int32), workspace=ws.buf() if ws else None)
+    out.assert_guards("compress_reordered")
+    x.assert_guards("compress_reordered input")
+    if ws:
+        ws.assert_guards("compress_reordered workspace")
+    for dt, es in ((0, 4), (1, 2)):
+        o = Arena(es * n)
+        T.taco_decompress_reordered(c, out.buf(), rows, cols, o.buf(), order.buf(torch.int32), dt)
+        o.assert_guards(f"decompress_reordered out_dtype={dt}")
+    order.assert_guards("order after use")
