@@ -277,8 +277,9 @@ int taco_decompress_reordered(taco_codec c, const void* in, int64_t rows, int64_
  * is that computation for a linear layer, with the decode in its prologue:
  *   out[M, N] = decode(A)[M, K] * W^T,
  * where decode(A) is the bf16 tensor taco_decompress(c, a, M, K, ., 1, .)
- * writes (each value the nearest-even bf16 of the exact decoded value; for a
- * NaN the sign and payload may differ), W is bf16 [N, K] row-major (the
+ * writes (each value the nearest-even bf16 of its float32 decoded value,
+ * which is the single rounding of the exact one; for a NaN the sign and
+ * payload may differ), W is bf16 [N, K] row-major (the
  * weight layout of a linear layer), and the products are summed in float32
  * on the matrix cores. The decoded activation is never written to memory.
  *   c          a compressed format without the Hadamard transform: INT8_SYM,

@@ -10,7 +10,8 @@
 // group 128, INT8 symmetric block 64, dual-scale FP8 with block 32, 64 or
 // 128); each value is decoded in registers, between the global load and the
 // LDS store of the A tile, to the bf16 number taco_decompress writes for it
-// (the single rounding of the exact decoded value, nearest-even). W is a bf16
+// (the nearest-even bf16 of the float32 decoded value, itself the single
+// rounding of the exact value). W is a bf16
 // weight in the layout of a linear layer, [N, K] row-major, so both operands
 // are contiguous along K.
 //
