@@ -92,7 +92,7 @@ int scale_mode(const taco_codec& c, float ts, void* ws, size_t ws_bytes, bool in
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
 
-// A launch is judged by hipGetLastError afterwards, so drop any error an
+// A launch's status is read with hipGetLastError afterwards, so drop any error an
 // earlier, unrelated runtime call on this thread left behind.
 void clear_stale_error() { (void)hipGetLastError(); }
 
