@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_fp8_had_compress(
     float* __restrict__ dbg, ReorderArgs ro) {
   using Gm = HadGeom<LOGB>;
   using CH = HadChunk<LOGB, T>;
-  static_assert(!(REORD && PERSIST), "the reordering compress runs the one-chunk-per-wave grid");
+  static_assert(!(REORD && PERSIST), "the reordering compress does not run the persistent grid");
   __shared__ uint32_t lds_e;
   __shared__ float lds_g;
   __shared__ float lds_m[kBlockThreads / kWave];
@@ -662,7 +662,7 @@ static hipError_t launch_compress_fmt(const FP8HadArgs& a, hipStream_t s) {
   auto* ws = static_cast<Workspace*>(a.ws);
   const dim3 big_grid = capped_grid(had_groups(LOGB, a.nblocks, kChunkTiles));
   if (a.ro.order != nullptr) {
-    // reordered input (block 128 only): the one-chunk-per-wave grid at every size
+    // reordered input (block 128 only): never the persistent small-tensor grid
     if constexpr (LOGB == 7) {
       if (a.dbg) return hipErrorInvalidValue;
       // rows staged through LDS in units of whole rows (the abs-max pre-pass
